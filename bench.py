@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV GQA attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: kv_append of the
+step's new tokens into their cache slots, then paged_attn_forward (work
+planner, attention kernel(s), LSE merge).  Inputs are resident in HBM before
+the timed region.
+
+Default workload (the headline): single-session incremental prefill, one
+layer, 32 q / 8 KV heads, head_dim 128, block 16, bf16: 45,700 cached tokens,
+2,700 new (a 45.7K -> 48.4K agent turn).  `value` is its attention TFLOP/s
+(4 * d * Hq flops per unmasked (query, key) pair) over the whole step.  Also
+measured in the same run and reported as sub-objects: batched decode (64
+sessions, lognormal contexts with median 142K) in KV GB/s, and incremental
+prefill at 128K history.  The oracle's CPU rate on a bounded sample of the
+headline workload is reported as `cpu_baseline`.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+METRIC = "incremental-prefill attn TFLOP/s + decode KV GB/s, % of MI355X roofline"
+
+
+def prefill_flops(hist, incr, hq, d):
+    """4 * d * Hq flops per unmasked (query, key) pair."""
+    pairs = sum(int(n) * int(h) + int(n) * (int(n) + 1) // 2 for h, n in zip(hist, incr))
+    return 4 * d * hq * pairs
+
+
+def kv_bytes_per_token(spec):
+    elem = 1 if spec.kv_dtype == "e4m3" else 2
+    return 2 * spec.num_kv_heads * spec.head_dim * elem
+
+
+def decode_bytes(spec):
+    """Algorithmic HBM bytes of one decode step: every context token's K and V
+    once, plus q, out, the step's appended K/V and the block-table entries read."""
+    ctx = sum(int(h) + int(n) for h, n in zip(spec.hist, spec.incr))
+    q = spec.total_q * spec.num_q_heads * spec.head_dim * 2
+    nb = sum(-(-(int(h) + int(n)) // spec.block_size) for h, n in zip(spec.hist, spec.incr))
+    return ctx * kv_bytes_per_token(spec) + 2 * q + nb * 4
+
+
+def prefill_bytes(spec):
+    ctx = sum(int(h) + int(n) for h, n in zip(spec.hist, spec.incr))
+    q = spec.total_q * spec.num_q_heads * spec.head_dim * 2
+    return ctx * kv_bytes_per_token(spec) + 2 * q
+
+
+class Runner:
+    """Holds one workload's device inputs and runs steps through the C ABI."""
+
+    def __init__(self, pa, torch, spec, dev):
+        import workloads as W
+        self.pa, self.torch, self.spec = pa, torch, spec
+        b = W.make_batch(spec, dev)
+        self.b = b
+        self.cache = pa.make_cache(b.k_pool, b.v_pool)
+        self.bt = torch.from_numpy(b.block_tables).to(dev)
+        self.slots = b.slot_mapping.to(dev)
+        ws = pa.pa_workspace_size(b.hist, b.incr, spec.num_q_heads, self.cache)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((spec.total_q, spec.num_q_heads, spec.head_dim),
+                               dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        b, pa = self.b, self.pa
+        pa.kv_append(self.cache, b.k_new, b.v_new, self.slots, stream=self.stream)
+        pa.paged_attn_forward(b.q, self.cache, self.bt, b.hist, b.incr, self.spec.scale, self.out,
+                              self.ws, stream=self.stream)
+
+    def timed(self, steps, warmup):
+        torch, pa = self.torch, self.pa
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        for k in range(4):
+            pa.pa_timing_read(k)  # drop anything recorded before
+        pa.pa_timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        pa.pa_timing_enable(False)
+        ms = e0.elapsed_time(e1) / steps
+        kern = {}
+        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge")):
+            tot, cnt = pa.pa_timing_read(kind)
+            if cnt:
+                kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step
+        return ms, kern
+
+
+def run_cpu_baseline(spec, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload's query rows
+    (all heads), on this host's cores.  Rate in the metric's unit."""
+    import oracle
+    import torch
+    import workloads as W
+    b = W.make_batch(spec, "cpu")
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    kc, vc = bits(b.k_pool).copy(), bits(b.v_pool).copy()
+    oracle.kv_append(kc, vc, None, None, oracle.KV_BF16, bits(b.k_new), bits(b.v_new),
+                     b.slot_mapping.numpy())
+    q = bits(b.q)
+    rng = np.random.default_rng(0)
+    n_incr = int(b.incr[0])
+    # calibrate with a few rows, then size the sample to the budget
+    rows = [n_incr - 1]
+    t0 = time.time()
+    oracle.attention(q, kc, vc, None, None, oracle.KV_BF16, b.block_tables, b.hist, b.incr,
+                     spec.num_q_heads, spec.scale, rows=rows)
+    t1 = max(time.time() - t0, 1e-3)
+    n = int(max(1, min(n_incr, budget_s / t1)))
+    rows = np.sort(rng.choice(n_incr, size=n, replace=False)).astype(np.int64)
+    t0 = time.time()
+    oracle.attention(q, kc, vc, None, None, oracle.KV_BF16, b.block_tables, b.hist, b.incr,
+                     spec.num_q_heads, spec.scale, rows=rows)
+    dt = time.time() - t0
+    pairs = sum(int(b.hist[0]) + int(r) + 1 for r in rows)
+    flops = 4 * spec.head_dim * spec.num_q_heads * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {n_incr} query rows (all {spec.num_q_heads} heads) of the headline "
+                      f"workload, fp64, {dt:.1f} s, host {os.cpu_count()} CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the path is built and measured on one "
+              "MI355X only (multi-GPU sharding is not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_gqa_amd as pa
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+
+    spec = W.incremental()
+    r = Runner(pa, torch, spec, dev)
+    ms, kern = r.timed(args.steps, args.warmup)
+    flops = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
+    value = flops / (ms * 1e-3) / 1e12
+    k_ms = kern["prefill"][0]
+    k_launch_per_step = kern["prefill"][1]
+    achieved = flops / (k_ms * k_launch_per_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "incremental_prefill: 1 session, 45,700 cached + 2,700 new tokens, "
+                               "32 q / 8 KV heads, head_dim 128, block 16, bf16 KV, one layer",
+                   "hist": spec.hist[0], "incr": spec.incr[0], "num_q_heads": 32,
+                   "num_kv_heads": 8, "head_dim": 128, "block_size": 16},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_kernel<128,16,false>",
+                     "kernel_ms": round(k_ms, 4)},
+        "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
+    }
+    del r
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        # batched decode, 64 sessions, median context 142K
+        dspec = W.decode_batch()
+        r = Runner(pa, torch, dspec, dev)
+        dms, dk = r.timed(args.steps, args.warmup)
+        byts = decode_bytes(dspec)
+        dk_ms = dk["decode"][0]
+        line["decode"] = {
+            "workload": "decode_batch: 64 sessions x 1 token, lognormal context (median 142K, "
+                        "sigma 0.5, clipped [10K, 256K]), 32 q / 8 KV heads, d 128, block 16, bf16",
+            "sum_ctx": int(sum(dspec.hist) + 64),
+            "ms_per_step": round(dms, 4),
+            "GB/s": round(byts / (dms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(64 / (dms * 1e-3), 1),
+            "kernels_ms": {k: round(v[0], 4) for k, v in dk.items()},
+            "roofline": {"bound": "hbm", "achieved": round(byts / (dk_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None, "algorithmic_bytes": int(byts)},
+        }
+        del r
+        torch.cuda.empty_cache()
+        # incremental prefill at 128K history
+        pspec = W.incremental(131_072, 2_700, "incremental_128k")
+        r = Runner(pa, torch, pspec, dev)
+        pms, pk = r.timed(max(3, args.steps // 2), args.warmup)
+        pfl = prefill_flops(pspec.hist, pspec.incr, 32, 128)
+        pk_ms = pk["prefill"][0] * pk["prefill"][1]
+        line["prefill_128k"] = {
+            "workload": "incremental_prefill: 131,072 cached + 2,700 new tokens, 32 q / 8 KV, d 128",
+            "ms_per_step": round(pms, 4), "TFLOP/s": round(pfl / (pms * 1e-3) / 1e12, 2),
+            "kernels_ms": {k: round(v[0], 4) for k, v in pk.items()},
+            "roofline": {"bound": "mfma", "achieved": round(pfl / (pk_ms * 1e-3) / 1e12, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        }
+        del r
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = run_cpu_baseline(spec, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged-KV GQA attention library.
+ *
+ * One scheduler step of one attention layer is two calls, in this order:
+ *   1. kv_append           scatter the step's new K/V tokens into their cache
+ *                          slots;
+ *   2. paged_attn_forward  every new query token attends to its sequence's
+ *                          cached history plus, causally, the new tokens.
+ *
+ * Pages cited (title, then section):
+ *   [Agentic] "vLLM Agentic 推理｜面向 Agent 负载的推理优化"
+ *   [AMPD]    "ICML'26 | AMPD：PD 分离遇上多轮推理，incremental prefill 到底该在哪跑"
+ *   [V1Sched] "vLLM/V1 推理调度器"
+ *   [V41]     "vLLM 优化 DeepSeek-V4.1-Flash：智能体吞吐提升 5 倍"
+ *
+ * The pages state the problem, not the formula or the layout; the readings
+ * taken here are: scaled dot-product softmax attention, causal mask with an
+ * inclusive boundary (a query at absolute position p sees keys 0..p), query
+ * head h reads KV head h / (num_q_heads / num_kv_heads), cache layout
+ * [num_blocks][num_kv_heads][block_size][head_dim], OCP E4M3 ("e4m3fn") for
+ * 8-bit KV with one fp32 scale per (physical block, KV head).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked HOST.  All tensors are dense
+ *     row-major.  The caller owns and allocates every buffer; the library
+ *     keeps only a small pinned host staging ring for work lists.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous and ordered on `stream`; host arrays may be
+ *     reused as soon as a call returns.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     A non-OK status means nothing was enqueued and nothing was written;
+ *     pa_last_error() describes why.  PA_ERR_HIP reports a failed HIP call
+ *     (outputs are then undefined).
+ *   - Device *contents* are trusted: block ids outside [0, num_blocks),
+ *     duplicate slots, or tables shorter than cdiv(ctx, block_size) are
+ *     caller bugs with undefined results.
+ *   - The library never aborts the process.
+ *
+ * Supported domain: head_dim in {64, 128}; block_size in {16, 64};
+ * num_q_heads % num_kv_heads == 0 with group size in {1, 2, 4, 8, 16};
+ * q and out bf16; KV bf16 or E4M3.  Element offsets are 64-bit throughout.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_ARG = 1,
+  PA_ERR_BAD_SHAPE = 2,
+  PA_ERR_UNSUPPORTED = 3,
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_HIP = 5
+} pa_status;
+
+typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+
+/* The paged KV cache: a pool of physical blocks, each holding block_size
+ * consecutive token positions of one sequence for every KV head
+ * ([V1Sched] 源码片段 "KVCacheManager.allocate_slots — 块容量": a request
+ * needs cdiv(tokens, block_size) blocks; "Scheduler.schedule — 记账与状态":
+ * each request holds a list of block ids; blocks may be shared).
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim],
+ *                     bf16 (2 bytes) or E4M3 codes (1 byte) per element.
+ *   k_scale, v_scale  fp32 [num_blocks][num_kv_heads]; stored value =
+ *                     decode(code) * scale.  NULL iff dtype == PA_KV_BF16.
+ * ([V41] "SWA 有界重放" and the kernels section keep KV in FP8 to cut its
+ * footprint.) */
+typedef struct {
+  void *k_cache;
+  void *v_cache;
+  float *k_scale;
+  float *v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  pa_kv_dtype dtype;
+} pa_kv_cache;
+
+/*
+ * kv_append -- write the step's new K/V tokens into their cache slots.
+ *
+ * [Agentic] §5.2: within a decode layer the KV write happens before the
+ * attention reads the cache.  [AMPD] §7: the increment's KV is concatenated
+ * onto the history already held locally; only the increment moves.
+ *
+ *   k_new, v_new   bf16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping   int64 [num_tokens]; slot = physical_block * block_size +
+ *                  offset; a negative slot skips the token.
+ * For token t with slot >= 0 and every KV head h:
+ *   bf16:  cache[slot / bs][h][slot % bs][:] = new[t][h][:]   (bit copy)
+ *   E4M3:  cache[...][e] = E4M3(new[t][h][e] / scale[slot / bs][h]) where the
+ *          division is the correctly rounded fp32 quotient and E4M3() rounds
+ *          to nearest-even, saturating to +-448 (NaN -> NaN).
+ * Only the named slots are written; scales are inputs and never modified.
+ * num_tokens == 0 is a no-op.
+ */
+PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                    const int64_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/*
+ * paged_attn_forward -- attention of the step's query tokens over the paged
+ * cache: incremental prefill, initial prefill and decode in one call.
+ *
+ * [AMPD] §1 and §3: incremental prefill processes l_incr new tokens that must
+ * read the l_hist tokens already cached; initial prefill is l_hist = 0; decode
+ * produces one token at a time over the whole, growing cache.  [V1Sched]
+ * "实际实现" / "Scheduler.schedule": per request the scheduler knows the
+ * computed-token count (hist) and the tokens scheduled this step (incr).
+ *
+ *   q             bf16 [total_q][num_q_heads][head_dim], total_q = sum(incr);
+ *                 the rows of sequence s are rows rowstart[s] .. +incr[s]-1
+ *                 with rowstart the exclusive prefix sum of incr.
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries beyond
+ *                 cdiv(hist + incr, block_size) are never read.
+ *   hist_lens     HOST int32 [num_seqs]: tokens cached before this step.
+ *   incr_lens     HOST int32 [num_seqs]: new tokens this step (1 = decode,
+ *                 0 = sequence idle).  Their K/V must already be appended.
+ *   scale         softmax scale applied to q.k (1/sqrt(head_dim) usually).
+ *   out           bf16 [total_q][num_q_heads][head_dim].
+ *   lse_out       optional fp32 [total_q][num_q_heads]: ln(sum_j exp(scale *
+ *                 q.k_j)) over the keys the row sees; NULL to skip.
+ *   workspace     device scratch of at least pa_workspace_size(...) bytes,
+ *                 256-byte aligned; contents need no initialisation.
+ * Row i of sequence s is at position p = hist[s] + i, and
+ *   out[row][h] = sum_{j<=p} softmax_j(scale * q[row][h] . K[j][h/G]) V[j][h/G].
+ * Neither q nor the caches are written.
+ */
+PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *hist_lens, const int32_t *incr_lens,
+                             int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
+                             float *lse_out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Bytes of workspace paged_attn_forward needs for these HOST lengths.
+ * Returns 0 and sets pa_last_error() if the arguments are invalid. */
+PA_API size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int32_t num_seqs,
+                         int32_t num_q_heads, const pa_kv_cache *cache);
+
+/* Text of the calling thread's most recent non-OK status ("" if none). */
+PA_API const char *pa_last_error(void);
+
+/* Test hook for block-table addressing: gathers one sequence's cached
+ * tokens in logical order, raw (bf16 or E4M3 bytes, no scaling):
+ *   k_out[p][h][:] = k_cache[block_table_row[p / bs]][h][p % bs][:]
+ * for p < ctx; same for v_out.  block_table_row is a device pointer;
+ * k_out, v_out are [ctx][num_kv_heads][head_dim] elements of the cache type. */
+PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_row, int32_t ctx,
+                          void *k_out, void *v_out, void *stream);
+
+/* Per-kernel timing for measurement.  When enabled (nonzero), each launch
+ * records HIP events on the call's stream around the kernel; the durations
+ * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
+ * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention,
+ * 3 = LSE merge, the summed milliseconds and launch count since the last
+ * reset (it synchronises on the recorded events), then resets that kind. */
+PA_API pa_status pa_timing_enable(int enable);
+PA_API pa_status pa_timing_read(int kind, double *ms, int64_t *count);
+
+/* Test hook for the work planner: the work list paged_attn_forward would
+ * build for these HOST lengths, written to HOST memory.  items_out receives
+ * up to items_cap records of 8 int32 each, prefill items first, then decode
+ * items: {seq, kv_head, first_row, first_pos, tokens, key_lo, key_hi,
+ * partial_slot (-1 = final)}.  counts_out[0..3] = prefill items, decode items,
+ * merge tasks, partial slots.  Returns PA_ERR_WORKSPACE_TOO_SMALL (with the
+ * counts filled) if items_cap is too small. */
+PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens,
+                               int32_t num_seqs, int32_t num_q_heads, const pa_kv_cache *cache,
+                               int32_t *items_out, int32_t items_cap, int32_t *counts_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_H */

@@ -128,12 +128,21 @@ typedef struct {
   int32_t num_blocks, hkv, bs, d, dtype;
 } cache_view;
 
+/* Value of every E4M3 code, filled once from orc_e4m3_to_double (a memo of
+ * the definition above, so the per-element work is a lookup). */
+static double e4m3_value[256];
+static int e4m3_value_ready = 0;
+static void e4m3_table_init(void) {
+  if (e4m3_value_ready) return;
+  for (int i = 0; i < 256; i++) e4m3_value[i] = orc_e4m3_to_double((uint8_t)i);
+  e4m3_value_ready = 1;
+}
+
 static double cache_elem(const cache_view *c, const void *base, const float *scale,
                          int64_t phys, int32_t kvh, int32_t off, int32_t dd) {
   int64_t idx = ((phys * c->hkv + kvh) * (int64_t)c->bs + off) * (int64_t)c->d + dd;
   if (c->dtype == ORC_KV_BF16) return orc_bf16_to_double(((const uint16_t *)base)[idx]);
-  return orc_e4m3_to_double(((const uint8_t *)base)[idx]) *
-         (double)scale[phys * c->hkv + kvh];
+  return e4m3_value[((const uint8_t *)base)[idx]] * (double)scale[phys * c->hkv + kvh];
 }
 
 /* ------------------------------------------------------------------ */
@@ -277,6 +286,7 @@ int orc_attention(const uint16_t *q, const void *k_cache, const void *v_cache,
                   const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hq,
                   float scale, const int64_t *rows, int64_t nrows, double *out, double *lse) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return ORC_ERR_RANGE;
+  e4m3_table_init();
   cache_view c = {k_cache, v_cache, k_scale, v_scale, num_blocks, hkv, bs, d, dtype};
   int64_t *rowstart = (int64_t *)malloc(sizeof(int64_t) * (num_seqs + 1));
   rowstart[0] = 0;
@@ -336,6 +346,7 @@ int orc_attention_partial(const uint16_t *qrow, const void *k_cache, const void 
                           int32_t num_blocks, int32_t hkv, int32_t bs, int32_t d,
                           const int32_t *bt_row, int32_t kvh, int64_t pos, int64_t k_lo,
                           int64_t k_hi, float scale, double *o, double *lse, double *probs) {
+  e4m3_table_init();
   cache_view c = {k_cache, v_cache, k_scale, v_scale, num_blocks, hkv, bs, d, dtype};
   int64_t n = (k_hi < pos + 1 ? k_hi : pos + 1) - k_lo;
   double *logits = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));

@@ -1,0 +1,156 @@
+"""Python binding of libpagedattn.so (include/pagedattn.h): argument
+marshalling only.  Every step of the attention path runs in the HIP kernels;
+torch tensors are used for device memory and streams.
+
+The library must have been built (``paged_kv_cache_gqa_amd.build.build()``);
+importing this module without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK, PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
+PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = 4, 5
+PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
+TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
+
+# Every symbol the header declares.
+EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
+           "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan")
+
+
+class pa_kv_cache(C.Structure):
+    _fields_ = [("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("k_scale", C.c_void_p), ("v_scale", C.c_void_p),
+                ("num_blocks", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("block_size", C.c_int32), ("head_dim", C.c_int32),
+                ("dtype", C.c_int)]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"pagedattn status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with paged_kv_cache_gqa_amd.build.build()")
+    L = C.CDLL(LIB_PATH)
+    P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    pc = C.POINTER(pa_kv_cache)
+    L.kv_append.argtypes = [pc, P, P, P, i32, P]
+    L.paged_attn_forward.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P, sz, P]
+    L.pa_workspace_size.argtypes = [P, P, i32, i32, pc]
+    L.pa_workspace_size.restype = sz
+    L.pa_last_error.argtypes = []
+    L.pa_last_error.restype = C.c_char_p
+    L.pa_debug_gather.argtypes = [pc, P, i32, P, P, P]
+    L.pa_timing_enable.argtypes = [C.c_int]
+    L.pa_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
+    L.pa_debug_plan.argtypes = [P, P, i32, i32, pc, P, i32, P]
+    for f in ("kv_append", "paged_attn_forward", "pa_debug_gather", "pa_timing_enable",
+              "pa_timing_read", "pa_debug_plan"):
+        getattr(L, f).restype = C.c_int
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _check(status):
+    if status != PA_OK:
+        raise PagedAttnError(status, lib.pa_last_error().decode())
+
+
+def make_cache(k_cache, v_cache, k_scale=None, v_scale=None) -> pa_kv_cache:
+    """Describe caches [num_blocks, num_kv_heads, block_size, head_dim]
+    (bf16, or uint8 E4M3 codes with fp32 [num_blocks, num_kv_heads] scales)."""
+    nb, hkv, bs, d = k_cache.shape
+    fp8 = k_cache.element_size() == 1
+    return pa_kv_cache(k_cache.data_ptr(), v_cache.data_ptr(),
+                       None if k_scale is None else k_scale.data_ptr(),
+                       None if v_scale is None else v_scale.data_ptr(),
+                       nb, hkv, bs, d, PA_KV_FP8_E4M3 if fp8 else PA_KV_BF16)
+
+
+def _host_i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def kv_append(cache: pa_kv_cache, k_new, v_new, slot_mapping, stream=None):
+    """Scatter new K/V rows [T, Hkv, d] (bf16) into the slots slot_mapping [T] (int64)."""
+    _check(lib.kv_append(C.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                         int(slot_mapping.shape[0]), _stream_ptr(stream)))
+
+
+def pa_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache) -> int:
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    r = lib.pa_workspace_size(h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p),
+                              len(h), num_q_heads, C.byref(cache))
+    if r == 0:
+        raise PagedAttnError(PA_ERR_BAD_SHAPE, lib.pa_last_error().decode())
+    return int(r)
+
+
+def paged_attn_forward(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale, out,
+                       workspace, lse_out=None, stream=None):
+    """Attention of q [total_q, Hq, d] over the paged cache; writes out (and lse_out)."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    _check(lib.paged_attn_forward(
+        _ptr(q), C.byref(cache), _ptr(block_tables), int(block_tables.shape[1]),
+        h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), int(q.shape[1]),
+        float(scale), _ptr(out), _ptr(lse_out), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _stream_ptr(stream)))
+
+
+def pa_debug_gather(cache: pa_kv_cache, block_table_row, ctx, k_out, v_out, stream=None):
+    _check(lib.pa_debug_gather(C.byref(cache), _ptr(block_table_row), int(ctx), _ptr(k_out),
+                               _ptr(v_out), _stream_ptr(stream)))
+
+
+def pa_last_error() -> str:
+    return lib.pa_last_error().decode()
+
+
+def pa_timing_enable(on: bool):
+    _check(lib.pa_timing_enable(1 if on else 0))
+
+
+def pa_timing_read(kind: int):
+    ms, cnt = C.c_double(), C.c_int64()
+    _check(lib.pa_timing_read(kind, C.byref(ms), C.byref(cnt)))
+    return ms.value, cnt.value
+
+
+def pa_debug_plan(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache):
+    """The planner's work list for these lengths: (items int32 [n, 8], counts[4])."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    counts = np.zeros(4, dtype=np.int32)
+    args = [h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), num_q_heads,
+            C.byref(cache)]
+    st = lib.pa_debug_plan(*args, None, 0, counts.ctypes.data_as(C.c_void_p))
+    if st not in (PA_OK, PA_ERR_WORKSPACE_TOO_SMALL):
+        _check(st)
+    cap = int(counts[0] + counts[1])
+    items = np.zeros((max(cap, 1), 8), dtype=np.int32)
+    _check(lib.pa_debug_plan(*args, items.ctypes.data_as(C.c_void_p), cap,
+                             counts.ctypes.data_as(C.c_void_p)))
+    return items[:cap], counts

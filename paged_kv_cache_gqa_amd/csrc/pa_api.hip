@@ -1,0 +1,560 @@
+// pa_api.hip -- the C ABI (include/pagedattn.h): host-side validation, the
+// work planner, workspace layout, pinned staging of the work list, launches
+// and per-kernel timing.
+//
+// Pages cited (title, then section):
+//   [Agentic] "vLLM Agentic 推理｜面向 Agent 负载的推理优化"
+//   [AMPD]    "ICML'26 | AMPD：PD 分离遇上多轮推理，incremental prefill 到底该在哪跑"
+//   [V1Sched] "vLLM/V1 推理调度器"
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.h"
+
+using namespace pa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_fail(hipError_t e, const char *what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int log2_exact(int v) {
+  int k = 0;
+  while ((1 << k) < v) k++;
+  return (1 << k) == v ? k : -1;
+}
+
+pa_status check_cache(const pa_kv_cache *c) {
+  if (!c) return fail(PA_ERR_NULL_ARG, "cache is NULL");
+  if (!c->k_cache || !c->v_cache) return fail(PA_ERR_NULL_ARG, "k_cache/v_cache is NULL");
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+    return fail(PA_ERR_BAD_SHAPE, "num_blocks (%d) and num_kv_heads (%d) must be positive",
+                c->num_blocks, c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->block_size != 16 && c->block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (16 or 64)", c->block_size);
+  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "unknown KV dtype %d", (int)c->dtype);
+  const bool fp8 = c->dtype == PA_KV_FP8_E4M3;
+  if (fp8 && (!c->k_scale || !c->v_scale))
+    return fail(PA_ERR_NULL_ARG, "E4M3 cache needs k_scale and v_scale");
+  if (!fp8 && (c->k_scale || c->v_scale))
+    return fail(PA_ERR_BAD_SHAPE, "bf16 cache must not carry scales");
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Work planner.  Inputs are the scheduler's host-side lengths ([V1Sched]
+// "实际实现": per request, the computed-token count and the tokens scheduled
+// this step).  A sequence whose increment times the group size fits 16 rows
+// is a decode-class tile (one tile per KV head); otherwise its increment is
+// cut into 128-row prefill tiles.  Key ranges are split so that there are
+// enough similar-sized items to fill every compute unit; split items write
+// partials merged by LSE ([Agentic] §4.3.3).
+constexpr int kNumCUs = 256;
+constexpr int kDecodeTargetItems = 32 * kNumCUs;
+constexpr int kDecodeMinChunk = 2048;
+constexpr int kPrefillTargetItems = 8 * kNumCUs;
+constexpr int kPrefillMinChunk = 4096;
+
+struct Plan {
+  std::vector<Item> prefill, decode;
+  std::vector<Merge> merges;
+  int64_t n_part_prefill = 0, n_part_decode = 0;
+  size_t off_prefill = 0, off_decode = 0, off_merges = 0, plan_bytes = 0;
+  size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Tile {
+  int32_t seq, row0, pos0, nq, keys;  // keys = last row's position + 1
+  bool decode;
+};
+
+// Balanced cut of [0, keys) into n ranges whose inner boundaries are
+// multiples of the 64-key tile.
+void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out) {
+  out.clear();
+  const int32_t ntile = (int32_t)cdiv64(keys, kKeyTile);
+  n = std::max(1, std::min(n, ntile));
+  for (int32_t i = 0; i < n; i++) {
+    const int32_t lo = (int32_t)((int64_t)ntile * i / n) * kKeyTile;
+    const int32_t hi = i + 1 == n ? keys : (int32_t)((int64_t)ntile * (i + 1) / n) * kKeyTile;
+    if (hi > lo) out.push_back({lo, hi});
+  }
+}
+
+void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
+               int32_t group, int32_t d, Plan &P) {
+  const int32_t dec_tokens = kDecodeRows / group;  // >= 1 for group <= 16
+  const int32_t pre_tokens = kPrefillRows / group;
+  std::vector<Tile> tiles;
+  int64_t row = 0;
+  for (int32_t s = 0; s < num_seqs; s++) {
+    const int32_t h = hist[s], n = incr[s];
+    if (n > 0) {
+      if (n <= dec_tokens) {
+        tiles.push_back({s, (int32_t)row, h, n, h + n, true});
+      } else {
+        for (int32_t i = 0; i < n; i += pre_tokens) {
+          const int32_t nq = std::min(pre_tokens, n - i);
+          tiles.push_back({s, (int32_t)(row + i), h + i, nq, h + i + nq, false});
+        }
+      }
+    }
+    row += n;
+  }
+  int64_t wd = 0, wp = 0, np0 = 0;
+  for (const Tile &t : tiles) {
+    if (t.decode)
+      wd += (int64_t)t.keys * hkv;
+    else {
+      wp += (int64_t)t.keys * hkv;
+      np0 += hkv;
+    }
+  }
+  const int64_t dchunk =
+      std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), kDecodeTargetItems));
+  int64_t pchunk = INT32_MAX;
+  if (np0 > 0 && np0 < kPrefillTargetItems)
+    pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, kPrefillTargetItems));
+
+  std::vector<std::vector<Item>> pre_by_head(hkv);
+  std::vector<std::pair<int32_t, int32_t>> ranges;
+  for (const Tile &t : tiles) {
+    const int64_t chunk = t.decode ? dchunk : pchunk;
+    const int32_t nsplit = (int32_t)std::min<int64_t>(cdiv64(t.keys, chunk), INT32_MAX);
+    cut(t.keys, nsplit, ranges);
+    for (int32_t kvh = 0; kvh < hkv; kvh++) {
+      int32_t part0 = -1;
+      if (ranges.size() > 1) {
+        int64_t &np = t.decode ? P.n_part_decode : P.n_part_prefill;
+        part0 = (int32_t)np;
+        np += (int64_t)ranges.size();
+        P.merges.push_back({t.row0, t.nq, kvh, part0, (int32_t)ranges.size(),
+                            t.decode ? kDecodeRows : kPrefillRows, t.decode ? 1 : 0, 0});
+      }
+      for (size_t i = 0; i < ranges.size(); i++) {
+        Item it{t.seq, kvh, t.row0, t.pos0, t.nq, ranges[i].first, ranges[i].second,
+                part0 < 0 ? -1 : part0 + (int32_t)i};
+        if (t.decode)
+          P.decode.push_back(it);
+        else
+          pre_by_head[kvh].push_back(it);
+      }
+    }
+  }
+  // Longest items first; prefill items of one KV head are interleaved with
+  // stride hkv so that consecutive work-group ids (dispatched round-robin
+  // over the XCDs) keep one KV head's tiles on one XCD's L2 when hkv == 8.
+  auto cost = [](const Item &x) { return (int64_t)(x.kv_hi - x.kv_lo) * (x.nq > 0 ? 1 : 0); };
+  auto longer = [&](const Item &x, const Item &y) { return cost(x) > cost(y); };
+  for (auto &v : pre_by_head) std::stable_sort(v.begin(), v.end(), longer);
+  size_t maxlen = 0;
+  for (auto &v : pre_by_head) maxlen = std::max(maxlen, v.size());
+  for (size_t i = 0; i < maxlen; i++)
+    for (int32_t k = 0; k < hkv; k++)
+      if (i < pre_by_head[k].size()) P.prefill.push_back(pre_by_head[k][i]);
+  std::stable_sort(P.decode.begin(), P.decode.end(), longer);
+
+  size_t off = 0;
+  P.off_prefill = off;
+  off = align256(off + P.prefill.size() * sizeof(Item));
+  P.off_decode = off;
+  off = align256(off + P.decode.size() * sizeof(Item));
+  P.off_merges = off;
+  off = align256(off + P.merges.size() * sizeof(Merge));
+  P.plan_bytes = off;
+  P.off_po_pre = off;
+  off = align256(off + (size_t)P.n_part_prefill * kPrefillRows * d * sizeof(float));
+  P.off_pl_pre = off;
+  off = align256(off + (size_t)P.n_part_prefill * kPrefillRows * sizeof(float));
+  P.off_po_dec = off;
+  off = align256(off + (size_t)P.n_part_decode * kDecodeRows * d * sizeof(float));
+  P.off_pl_dec = off;
+  off = align256(off + (size_t)P.n_part_decode * kDecodeRows * sizeof(float));
+  P.total = off;
+}
+
+pa_status check_lengths(const int32_t *hist, const int32_t *incr, int32_t num_seqs,
+                        int32_t num_q_heads, const pa_kv_cache *c, int32_t max_blocks,
+                        bool check_table, int64_t *total_q_out) {
+  if (num_seqs < 0) return fail(PA_ERR_BAD_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 0 && (!hist || !incr)) return fail(PA_ERR_NULL_ARG, "hist_lens/incr_lens is NULL");
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_BAD_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, c->num_kv_heads);
+  const int group = num_q_heads / c->num_kv_heads;
+  if (log2_exact(group) < 0 || group > 16)
+    return fail(PA_ERR_UNSUPPORTED, "GQA group size %d not supported (1, 2, 4, 8, 16)", group);
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; s++) {
+    if (hist[s] < 0 || incr[s] < 0)
+      return fail(PA_ERR_BAD_SHAPE, "sequence %d: negative length (hist %d, incr %d)", s, hist[s],
+                  incr[s]);
+    const int64_t ctx = (int64_t)hist[s] + incr[s];
+    if (ctx > INT32_MAX - kKeyTile) return fail(PA_ERR_BAD_SHAPE, "sequence %d: context too long", s);
+    if (check_table && incr[s] > 0 && ctx > (int64_t)max_blocks * c->block_size)
+      return fail(PA_ERR_BAD_SHAPE,
+                  "sequence %d: context %lld exceeds its block table (%d blocks of %d)", s,
+                  (long long)ctx, max_blocks, c->block_size);
+    total += incr[s];
+  }
+  if (total >= INT32_MAX) return fail(PA_ERR_BAD_SHAPE, "total query rows %lld too large", (long long)total);
+  *total_q_out = total;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Pinned staging ring for work lists (one per device).  A slot is reused only
+// after the copy that last read it has completed.
+struct StageSlot {
+  void *host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+struct DeviceStage {
+  int device = -1;
+  std::vector<StageSlot> slots;
+  size_t next = 0;
+};
+std::mutex g_stage_mu;
+std::vector<DeviceStage> g_stages;
+
+pa_status stage_copy(const void *src, size_t bytes, void *dst_dev, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  DeviceStage *ds = nullptr;
+  for (auto &x : g_stages)
+    if (x.device == dev) ds = &x;
+  if (!ds) {
+    g_stages.push_back(DeviceStage{});
+    ds = &g_stages.back();
+    ds->device = dev;
+    ds->slots.resize(8);
+  }
+  StageSlot &sl = ds->slots[ds->next];
+  ds->next = (ds->next + 1) % ds->slots.size();
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    sl.pending = false;
+  }
+  if (!sl.done) {
+    e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate(staging)");
+  }
+  if (sl.cap < bytes) {
+    if (sl.host) (void)hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 1 << 20);
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    sl.cap = cap;
+  }
+  memcpy(sl.host, src, bytes);
+  e = hipMemcpyAsync(dst_dev, sl.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  e = hipEventRecord(sl.done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
+  sl.pending = true;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing with HIP events on the launch stream.
+constexpr int kKinds = 4;
+std::mutex g_time_mu;
+bool g_timing = false;
+struct TimedLaunch {
+  hipEvent_t a, b;
+};
+std::vector<TimedLaunch> g_pending[kKinds];
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t get_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F &&launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    on = g_timing;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    a = get_event();
+    b = get_event();
+  }
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  g_pending[kind].push_back({a, b});
+  return hipSuccess;
+}
+
+}  // namespace
+
+// =============================================================================
+extern "C" {
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  g_timing = enable != 0;
+  return PA_OK;
+}
+
+pa_status pa_timing_read(int kind, double *ms, int64_t *count) {
+  if (kind < 0 || kind >= kKinds) return fail(PA_ERR_BAD_SHAPE, "timing kind %d", kind);
+  if (!ms || !count) return fail(PA_ERR_NULL_ARG, "ms/count is NULL");
+  std::vector<TimedLaunch> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    pend.swap(g_pending[kind]);
+  }
+  double sum = 0;
+  for (auto &p : pend) {
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+    float t = 0;
+    e = hipEventElapsedTime(&t, p.a, p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    sum += t;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    for (auto &p : pend) {
+      g_event_pool.push_back(p.a);
+      g_event_pool.push_back(p.b);
+    }
+  }
+  *ms = sum;
+  *count = (int64_t)pend.size();
+  return PA_OK;
+}
+
+pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                    const int64_t *slot_mapping, int32_t num_tokens, void *stream) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens < 0) return fail(PA_ERR_BAD_SHAPE, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_NULL_ARG, "k_new/v_new/slot_mapping is NULL");
+  AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.ks = cache->k_scale;
+  a.vs = cache->v_scale;
+  a.hkv = cache->num_kv_heads;
+  a.bs = cache->block_size;
+  a.d = cache->head_dim;
+  a.total_chunks = (int64_t)num_tokens * a.hkv * (a.d / 8);
+  const bool fp8 = cache->dtype == PA_KV_FP8_E4M3;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(0, s, [&] { return launch_append(a, fp8, s); });
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return PA_OK;
+}
+
+size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int32_t num_seqs,
+                         int32_t num_q_heads, const pa_kv_cache *cache) {
+  if (check_cache(cache)) return 0;
+  int64_t total_q = 0;
+  if (check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, 0, false, &total_q))
+    return 0;
+  Plan P;
+  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
+            num_q_heads / cache->num_kv_heads, cache->head_dim, P);
+  return std::max<size_t>(P.total, 256);
+}
+
+pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *hist_lens, const int32_t *incr_lens,
+                             int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
+                             float *lse_out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  if (max_blocks_per_seq < 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq < 0");
+  int64_t total_q = 0;
+  st = check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, max_blocks_per_seq, true,
+                     &total_q);
+  if (st) return st;
+  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
+  if (total_q == 0) return PA_OK;
+  if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
+  const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
+  Plan P;
+  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, P);
+  if (!workspace) return fail(PA_ERR_NULL_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(PA_ERR_BAD_SHAPE, "workspace not 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                P.total);
+
+  std::vector<unsigned char> host(P.plan_bytes, 0);
+  if (!P.prefill.empty()) memcpy(host.data() + P.off_prefill, P.prefill.data(), P.prefill.size() * sizeof(Item));
+  if (!P.decode.empty()) memcpy(host.data() + P.off_decode, P.decode.data(), P.decode.size() * sizeof(Item));
+  if (!P.merges.empty()) memcpy(host.data() + P.off_merges, P.merges.data(), P.merges.size() * sizeof(Merge));
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char *ws = (unsigned char *)workspace;
+  st = stage_copy(host.data(), P.plan_bytes, ws, s);
+  if (st) return st;
+
+  AttnArgs a{};
+  a.q = q;
+  a.c.k = cache->k_cache;
+  a.c.v = cache->v_cache;
+  a.c.ks = cache->k_scale;
+  a.c.vs = cache->v_scale;
+  a.c.num_blocks = cache->num_blocks;
+  a.c.hkv = hkv;
+  a.bt = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.hq = num_q_heads;
+  a.group = group;
+  a.lg = log2_exact(group);
+  a.scale_log2 = scale * 1.44269504088896341f;
+  a.out = out;
+  a.lse_out = lse_out;
+  const bool fp8 = cache->dtype == PA_KV_FP8_E4M3;
+  const int bs = cache->block_size;
+  hipError_t e;
+  if (!P.prefill.empty()) {
+    a.items = (const Item *)(ws + P.off_prefill);
+    a.part_o = (float *)(ws + P.off_po_pre);
+    a.part_lse = (float *)(ws + P.off_pl_pre);
+    const int n = (int)P.prefill.size();
+    e = timed(1, s, [&] { return launch_prefill(a, n, d, bs, fp8, s); });
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  if (!P.decode.empty()) {
+    a.items = (const Item *)(ws + P.off_decode);
+    a.part_o = (float *)(ws + P.off_po_dec);
+    a.part_lse = (float *)(ws + P.off_pl_dec);
+    const int n = (int)P.decode.size();
+    e = timed(2, s, [&] { return launch_decode(a, n, d, bs, fp8, s); });
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  }
+  if (!P.merges.empty()) {
+    MergeArgs m{};
+    m.merges = (const Merge *)(ws + P.off_merges);
+    m.part_o_prefill = (const float *)(ws + P.off_po_pre);
+    m.part_lse_prefill = (const float *)(ws + P.off_pl_pre);
+    m.part_o_decode = (const float *)(ws + P.off_po_dec);
+    m.part_lse_decode = (const float *)(ws + P.off_pl_dec);
+    m.out = out;
+    m.lse_out = lse_out;
+    m.hq = num_q_heads;
+    m.group = group;
+    m.lg = a.lg;
+    m.d = d;
+    const int n = (int)P.merges.size();
+    e = timed(3, s, [&] { return launch_merge(m, n, s); });
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return PA_OK;
+}
+
+pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_row, int32_t ctx,
+                          void *k_out, void *v_out, void *stream) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  if (ctx < 0) return fail(PA_ERR_BAD_SHAPE, "ctx %d < 0", ctx);
+  if (ctx == 0) return PA_OK;
+  if (!block_table_row || !k_out || !v_out)
+    return fail(PA_ERR_NULL_ARG, "block_table_row/k_out/v_out is NULL");
+  GatherArgs g{};
+  g.k = cache->k_cache;
+  g.v = cache->v_cache;
+  g.bt_row = block_table_row;
+  g.k_out = k_out;
+  g.v_out = v_out;
+  g.hkv = cache->num_kv_heads;
+  g.bs = cache->block_size;
+  g.row_bytes = cache->head_dim * (cache->dtype == PA_KV_FP8_E4M3 ? 1 : 2);
+  g.total_chunks = (int64_t)ctx * g.hkv * (g.row_bytes / 16);
+  hipError_t e = launch_gather(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return PA_OK;
+}
+
+pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens, int32_t num_seqs,
+                        int32_t num_q_heads, const pa_kv_cache *cache, int32_t *items_out,
+                        int32_t items_cap, int32_t *counts_out) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  int64_t total_q = 0;
+  st = check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, 0, false, &total_q);
+  if (st) return st;
+  if (!counts_out || (items_cap > 0 && !items_out)) return fail(PA_ERR_NULL_ARG, "output is NULL");
+  Plan P;
+  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
+            num_q_heads / cache->num_kv_heads, cache->head_dim, P);
+  counts_out[0] = (int32_t)P.prefill.size();
+  counts_out[1] = (int32_t)P.decode.size();
+  counts_out[2] = (int32_t)P.merges.size();
+  counts_out[3] = (int32_t)(P.n_part_prefill + P.n_part_decode);
+  const size_t n = P.prefill.size() + P.decode.size();
+  if (n > (size_t)std::max(items_cap, 0))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "items_cap %d, need %zu", items_cap, n);
+  if (!P.prefill.empty()) memcpy(items_out, P.prefill.data(), P.prefill.size() * sizeof(Item));
+  if (!P.decode.empty())
+    memcpy(items_out + 8 * P.prefill.size(), P.decode.data(), P.decode.size() * sizeof(Item));
+  return PA_OK;
+}
+
+}  // extern "C"

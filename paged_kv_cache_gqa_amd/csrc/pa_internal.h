@@ -1,0 +1,116 @@
+// pa_internal.h -- work-list records and kernel arguments shared by the host
+// planner (pa_api.hip) and the gfx950 kernels (pa_*.hip).  Library-internal.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pa {
+
+// One attention work item: a tile of query rows of one (sequence, KV head)
+// against the key range [kv_lo, kv_hi) of that sequence.  The tile's rows are
+// the query tokens [row0, row0 + nq) times the G query heads of the group,
+// ordered row = token * G + head_in_group.  part < 0: the item covers every
+// key its rows see and writes the final output; otherwise it writes partial
+// results into partial slot `part`, merged later.
+struct Item {
+  int32_t seq;
+  int32_t kvh;
+  int32_t row0;   // global q row of the tile's first token
+  int32_t pos0;   // absolute position of that token (hist + index in increment)
+  int32_t nq;     // query tokens in the tile
+  int32_t kv_lo;  // first key (multiple of the 64-key tile)
+  int32_t kv_hi;  // one past the last key
+  int32_t part;   // partial slot or -1
+};
+static_assert(sizeof(Item) == 32, "Item layout");
+
+// One merge task: rows of one split tile, partial slots [part0, part0+nparts).
+struct Merge {
+  int32_t row0;
+  int32_t nq;
+  int32_t kvh;
+  int32_t part0;
+  int32_t nparts;
+  int32_t rows_per_part;  // slot height: 128 (prefill tiles) or 16 (decode tiles)
+  int32_t is_decode;      // which partial array the slots live in
+  int32_t pad;
+};
+static_assert(sizeof(Merge) == 32, "Merge layout");
+
+struct CacheArgs {
+  const void *k;
+  const void *v;
+  const float *ks;
+  const float *vs;
+  int32_t num_blocks;
+  int32_t hkv;
+};
+
+struct AttnArgs {
+  const void *q;          // bf16 [total_q][hq][d]
+  CacheArgs c;
+  const int32_t *bt;      // [num_seqs][max_blocks]
+  int32_t max_blocks;
+  int32_t hq;
+  int32_t group;          // G = hq / hkv (power of two)
+  int32_t lg;             // log2(G)
+  float scale_log2;       // softmax scale * log2(e)
+  void *out;              // bf16 [total_q][hq][d]
+  float *lse_out;         // optional fp32 [total_q][hq] (natural log)
+  const Item *items;
+  float *part_o;          // [slots][rows_per_slot][d] fp32, normalised partial outputs
+  float *part_lse;        // [slots][rows_per_slot], log2 units
+};
+
+struct MergeArgs {
+  const Merge *merges;
+  const float *part_o_prefill;
+  const float *part_lse_prefill;
+  const float *part_o_decode;
+  const float *part_lse_decode;
+  void *out;
+  float *lse_out;
+  int32_t hq;
+  int32_t group;
+  int32_t lg;
+  int32_t d;
+};
+
+struct AppendArgs {
+  const void *k_new;
+  const void *v_new;
+  const int64_t *slots;
+  void *k_cache;
+  void *v_cache;
+  const float *ks;
+  const float *vs;
+  int64_t total_chunks;   // tokens * hkv * (d / 8)
+  int32_t hkv;
+  int32_t bs;
+  int32_t d;
+};
+
+struct GatherArgs {
+  const void *k;
+  const void *v;
+  const int32_t *bt_row;
+  void *k_out;
+  void *v_out;
+  int64_t total_chunks;   // ctx * hkv * (row bytes / 16)
+  int32_t hkv;
+  int32_t bs;
+  int32_t row_bytes;      // d * element bytes
+};
+
+constexpr int kPrefillRows = 128;  // query rows (tokens x heads) per prefill tile
+constexpr int kDecodeRows = 16;    // query rows per decode tile
+constexpr int kKeyTile = 64;       // keys per inner-loop tile
+
+// Launchers (defined next to their kernels).
+hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
+hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, int n_merges, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+
+}  // namespace pa

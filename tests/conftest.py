@@ -18,3 +18,23 @@ def _oracle_built():
     import oracle
     oracle.build(force=False)
     yield
+
+
+def _lib_stale():
+    pkg = os.path.join(ROOT, "paged_kv_cache_gqa_amd")
+    lib = os.path.join(pkg, "libpagedattn.so")
+    if not os.path.exists(lib):
+        return True
+    srcs = [os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))]
+    srcs.append(os.path.join(ROOT, "include", "pagedattn.h"))
+    return max(os.path.getmtime(s) for s in srcs) > os.path.getmtime(lib)
+
+
+@pytest.fixture(scope="session")
+def palib():
+    """The product library's Python binding (built first if missing or stale)."""
+    if _lib_stale():
+        from paged_kv_cache_gqa_amd import build as B
+        B.build()
+    import paged_kv_cache_gqa_amd as pa
+    return pa
