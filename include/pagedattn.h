@@ -129,7 +129,8 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  *   hist_lens     HOST int32 [num_seqs]: tokens cached before this step.
  *   incr_lens     HOST int32 [num_seqs]: new tokens this step (1 = decode,
  *                 0 = sequence idle).  Their K/V must already be appended.
- *   scale         softmax scale applied to q.k (1/sqrt(head_dim) usually).
+ *   scale         softmax scale applied to q.k (1/sqrt(head_dim) usually);
+ *                 must be finite and > 0.
  *   out           bf16 [total_q][num_q_heads][head_dim].
  *   lse_out       optional fp32 [total_q][num_q_heads]: ln(sum_j exp(scale *
  *                 q.k_j)) over the keys the row sees; NULL to skip.

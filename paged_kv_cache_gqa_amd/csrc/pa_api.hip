@@ -433,7 +433,8 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   st = check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, max_blocks_per_seq, true,
                      &total_q);
   if (st) return st;
-  if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_BAD_SHAPE, "scale must be finite and > 0 (got %g)", (double)scale);
   if (total_q == 0) return PA_OK;
   if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;

@@ -26,15 +26,43 @@
 
 namespace pa {
 
-// XOR swizzle of 16-byte chunks within an LDS row (D/8 chunks per row).
-// Rows r..r+7 map one logical chunk to eight different chunks, and four
-// consecutive rows map a 32-byte column slice to four disjoint bank groups,
-// so neither the 16-byte A-operand reads nor the transpose reads conflict.
+// LDS row layout of a K or V tile: rows of D bf16 (D/8 16-byte chunks).  Rows
+// are padded by kLdsPad bytes so that consecutive rows start in different
+// banks: the 16-byte A-operand reads of eight rows and the transpose reads of
+// four rows x 32 bytes then touch disjoint banks, while every address a lane
+// uses stays a per-lane base plus a compile-time offset.  kLdsPad == 0 selects
+// an XOR swizzle of the chunk index instead (no padding).
+#ifndef PA_LDS_PAD
+#define PA_LDS_PAD 32
+#endif
+constexpr int kLdsPad = PA_LDS_PAD;
+
 template <int D>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  constexpr int MASK = D / 16 - 1;
-  return chunk ^ ((row & MASK) << 1);
-}
+struct LdsRow {
+  static constexpr int bytes = D * 2 + kLdsPad;  // row stride
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    if constexpr (kLdsPad == 0) {
+      constexpr int MASK = D / 16 - 1;
+      return row * bytes + ((chunk ^ ((row & MASK) << 1)) * 16);
+    } else {
+      return row * bytes + chunk * 16;
+    }
+  }
+};
+
+// =============================================================================
+// Softmax bookkeeping shared by both kernels.  Scores are kept raw (q.k); the
+// running maximum m is kept in log2 units (raw * sl, sl = scale * log2 e > 0),
+// so a probability is one fused multiply-add and one exp2.  The maximum is
+// updated lazily: only when some lane's tile maximum exceeds its m by more than
+// kRescaleSlack does the wave move m up and rescale its sums; otherwise the
+// stale m is kept and the probabilities may reach 2^kRescaleSlack, which bf16
+// and fp32 hold exactly as well as values below 1.  The final O / l is the
+// same quantity either way.
+constexpr float kRescaleSlack = 8.0f;
+
+using MaskedTile = std::true_type;
+using FullTile = std::false_type;
 
 // =============================================================================
 // Prefill: one work-group (4 waves) per item; 128 query rows (tokens x heads),
@@ -42,20 +70,21 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 template <int D, int BS, bool FP8>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   constexpr int CPR = D / 8;             // 16-byte bf16 chunks per LDS row
-  constexpr int ROWB = D * 2;            // LDS row bytes
-  constexpr int TILEB = kKeyTile * ROWB; // one K or V tile in LDS
+  typedef LdsRow<D> L;
+  constexpr int TILEB = kKeyTile * L::bytes;  // one K or V tile in LDS
   constexpr int NCH = kKeyTile * CPR / 256;
   constexpr int NC = D / 16;             // k-steps of the score product
   constexpr int ND = D / 32;             // 32-wide d blocks of the output
-  constexpr int EB = FP8 ? 1 : 2;        // cache element bytes
-  constexpr int NSC = FP8 ? (BS == 16 ? 4 : 1) : 1;  // scales per tile
+  constexpr int NSC = FP8 ? (BS == 16 ? 4 : 1) : 1;  // K/V scales per tile
+  constexpr int RPI = 64 / CPR;          // key rows one wave covers per load instruction
 
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * TILEB];
   lds_u8 *smem = (lds_u8 *)smem_raw;
 
   const Item it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int row = wave * 32 + col;
   const int tok = row >> a.lg, g = row & (a.group - 1);
@@ -86,29 +115,37 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   const unsigned char *vc = (const unsigned char *)a.c.v;
   const int t_begin = it.kv_lo / kKeyTile;
   const int t_end = (it.kv_hi + kKeyTile - 1) / kKeyTile;
+  // tiles below t_full need no mask: every key is < kv_hi and <= every row's position
+  const int t_full = max(t_begin, min(t_end, min(it.pos0 + 1, it.kv_hi) / kKeyTile));
+  const int last_blk = (it.kv_hi - 1) / BS;
+  const int lim = min(pos, it.kv_hi - 1);  // last key this lane's row may see
 
-  // Staging registers for the next tile's K and V chunks.
+  // Staging registers for the next tile's K and V chunks.  Load instruction i
+  // of this wave covers key rows rb .. rb + RPI - 1 of the tile, all in one
+  // cache block, so the block id is a wave-uniform (scalar) load.
   typedef typename std::conditional<FP8, uint2, uint4>::type chunk_t;
   chunk_t kr[NCH], vr[NCH];
   float ksc_n[NSC], vsc_n[NSC], ksc[NSC], vsc[NSC];
+  const int lrow = lane / CPR, lch = lane % CPR;
 
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](auto partial, int t) {
+    constexpr bool PART = decltype(partial)::value;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CPR, ch = ci % CPR;
-      const int p = t * kKeyTile + r;
-      if (p < it.kv_hi) {
-        const int64_t blk = bt[p / BS];
-        const int64_t e = ((blk * hkv + it.kvh) * BS + (p % BS)) * D + ch * 8;
-        if constexpr (FP8) {
-          kr[i] = gload8(kc + e);
-          vr[i] = gload8(vc + e);
-        } else {
-          kr[i] = gload16(kc + e * 2);
-          vr[i] = gload16(vc + e * 2);
-        }
+      const int rb = (256 * i + 64 * wave) / CPR;
+      int bidx = (t * kKeyTile + rb) / BS;
+      if (PART) bidx = min(bidx, last_blk);
+      const int64_t blk = bt[bidx];
+      const int p = t * kKeyTile + rb + lrow;
+      const int64_t e = ((blk * hkv + it.kvh) * BS + (p % BS)) * D + lch * 8;
+      if constexpr (FP8) {
+        kr[i] = gload8(kc + e);
+        vr[i] = gload8(vc + e);
       } else {
+        kr[i] = gload16(kc + e * 2);
+        vr[i] = gload16(vc + e * 2);
+      }
+      if (PART && p >= it.kv_hi) {
         kr[i] = chunk_t{};
         vr[i] = chunk_t{};
       }
@@ -116,15 +153,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     if constexpr (FP8) {
 #pragma unroll
       for (int j = 0; j < NSC; j++) {
-        const int p = t * kKeyTile + j * BS;
-        if (p < it.kv_hi) {
-          const int64_t blk = bt[p / BS];
-          ksc_n[j] = a.c.ks[blk * hkv + it.kvh];
-          vsc_n[j] = a.c.vs[blk * hkv + it.kvh];
-        } else {
-          ksc_n[j] = 0.f;
-          vsc_n[j] = 0.f;
-        }
+        const int bidx = min((t * kKeyTile + j * BS) / BS, last_blk);
+        const int64_t blk = bt[bidx];
+        ksc_n[j] = a.c.ks[blk * hkv + it.kvh];
+        vsc_n[j] = a.c.vs[blk * hkv + it.kvh];
       }
     }
   };
@@ -133,9 +165,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     lds_u8 *vb = kb + TILEB;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CPR, ch = ci % CPR;
-      const int off = r * ROWB + swz<D>(r, ch) * 16;
+      const int r = (256 * i + 64 * wave) / CPR + lrow;
+      const int off = L::off(r, lch);
       if constexpr (FP8) {
         lds_store16(kb + off, e4m3x8_to_bf16x8(kr[i]));
         lds_store16(vb + off, e4m3x8_to_bf16x8(vr[i]));
@@ -152,79 +183,78 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       }
     }
   };
+  auto load_next = [&](int t) {
+    if ((t + 1) * kKeyTile <= it.kv_hi)
+      load_tile(FullTile{}, t);
+    else
+      load_tile(MaskedTile{}, t);
+  };
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
+  const int g16 = lane >> 4, j16 = lane & 15;
 
-  for (int t = t_begin; t < t_end; t++) {
-    const int buf = (t - t_begin) & 1;
-    const lds_u8 *Kb = smem + buf * 2 * TILEB;
-    const lds_u8 *Vb = Kb + TILEB;
-    if (t + 1 < t_end) load_tile(t + 1);
-
+  auto compute = [&](auto masked, int t, const lds_u8 *Kb, const lds_u8 *Vb) {
+    constexpr bool MASK = decltype(masked)::value;
     // ---- S^T = K * Q^T : two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      s[kb] = f32x16{};
       const int krow = kb * 32 + col;
+      s[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + L::off(krow, hh))), qf[0], f32x16{});
 #pragma unroll
-      for (int c = 0; c < NC; c++) {
-        bf16x8 af = as_bf16x8(lds_load16(Kb + krow * ROWB + swz<D>(krow, 2 * c + hh) * 16));
+      for (int c = 1; c < NC; c++) {
+        bf16x8 af = as_bf16x8(lds_load16(Kb + L::off(krow, 2 * c + hh)));
         s[kb] = mfma32x32x16(af, qf[c], s[kb]);
       }
     }
-
-    // ---- scale, mask, online softmax (this lane: one query row, 32 keys)
+    // ---- mask, tile maximum (raw scores; element 4i+r of block kb is key
+    //      kb*32 + 8i + 4hh + r)
+    float sl[NSC];
+#pragma unroll
+    for (int j = 0; j < NSC; j++) sl[j] = FP8 ? a.scale_log2 * ksc[j] : a.scale_log2;
     const int kbase = t * kKeyTile;
-    const bool need_mask = (kbase + kKeyTile - 1 > it.pos0) || (kbase + kKeyTile > it.kv_hi);
-    float x[2][16];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
-        const int i = e >> 2, r = e & 3;
-        float sl = a.scale_log2;
-        if constexpr (FP8) sl *= ksc[(NSC == 1) ? 0 : (kb * 2 + (i >> 1))];
-        float v = s[kb][e] * sl;
-        if (need_mask) {
-          const int key = kbase + kb * 32 + 8 * i + 4 * hh + r;
-          if (!(key <= pos && key < it.kv_hi)) v = -INFINITY;
+        if (MASK) {
+          const int key = kbase + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          s[kb][e] = key <= lim ? s[kb][e] : -INFINITY;
         }
-        x[kb][e] = v;
-        mx = fmaxf(mx, v);
+        if constexpr (NSC > 1) s[kb][e] *= sl[kb * 2 + (e >> 3)];
+        mx = fmaxf(mx, s[kb][e]);
       }
-    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+    const float mxs = NSC > 1 ? mx : mx * sl[0];
+    if (__any(mxs > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+    const float slp = NSC > 1 ? 1.0f : sl[0];
+    const float nm = -m;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
-        const float p = fast_exp2(x[kb][e] - m_new);
-        x[kb][e] = p;
+        const float p = fast_exp2(__builtin_fmaf(s[kb][e], slp, nm));
+        s[kb][e] = p;
         psum += p;
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < ND; db++) o[db] *= alpha;
+    l += psum;
 
     // ---- O^T += V^T * P^T : four 16-key steps
-    const int g16 = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       const int kb = ks >> 1, i0 = (ks & 1) * 2;
       bf16x8 pb;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        float p0 = x[kb][4 * i0 + r], p1 = x[kb][4 * (i0 + 1) + r];
+        float p0 = s[kb][4 * i0 + r], p1 = s[kb][4 * (i0 + 1) + r];
         if constexpr (FP8) {
           const float v0 = vsc[(NSC == 1) ? 0 : (kb * 2 + (i0 >> 1))];
           p0 *= v0;
@@ -235,21 +265,39 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < ND; db++) {
-        const int d0 = db * 32 + (g16 & 1) * 16 + 4 * (j & 3);
-        bf16x4 h0, h1;
-        {
-          const int vrow = ks * 16 + 4 * hh + (j >> 2);
-          h0 = lds_read_tr(Vb + vrow * ROWB + swz<D>(vrow, d0 >> 3) * 16 + (d0 & 7) * 2);
-        }
-        {
-          const int vrow = ks * 16 + 8 + 4 * hh + (j >> 2);
-          h1 = lds_read_tr(Vb + vrow * ROWB + swz<D>(vrow, d0 >> 3) * 16 + (d0 & 7) * 2);
-        }
+        const int d0 = db * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
+        const int vr0 = ks * 16 + 4 * hh + (j16 >> 2);
+        const int vr1 = vr0 + 8;
+        const bf16x4 h0 = lds_read_tr(Vb + L::off(vr0, d0 >> 3) + (d0 & 7) * 2);
+        const bf16x4 h1 = lds_read_tr(Vb + L::off(vr1, d0 >> 3) + (d0 & 7) * 2);
         bf16x8 af = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = mfma32x32x16(af, pb, o[db]);
       }
     }
+  };
 
+  if (t_begin < t_end) {
+    load_next(t_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  // unmasked tiles, then the tiles that cross the causal diagonal or the
+  // range's end (separate loops keep each body branch-free)
+  int t = t_begin;
+  for (; t < t_full; t++) {
+    const int buf = (t - t_begin) & 1;
+    const lds_u8 *Kb = smem + buf * 2 * TILEB;
+    if (t + 1 < t_end) load_next(t + 1);
+    compute(FullTile{}, t, Kb, Kb + TILEB);
+    if (t + 1 < t_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  for (; t < t_end; t++) {
+    const int buf = (t - t_begin) & 1;
+    const lds_u8 *Kb = smem + buf * 2 * TILEB;
+    if (t + 1 < t_end) load_tile(MaskedTile{}, t + 1);
+    compute(MaskedTile{}, t, Kb, Kb + TILEB);
     if (t + 1 < t_end) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -293,7 +341,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 // its own softmax state, and are combined through LDS at the end.  K goes
 // straight from HBM into MFMA A-operand registers; V passes through a
 // per-wave LDS tile for the transposed read.  The next tile's K and V are in
-// flight while the current one is computed.
+// flight while the current one is computed; block ids are wave-uniform scalar
+// loads, so waiting for them never waits for the K/V stream.
 template <int D, bool FP8>
 struct DecodeRegs {
   static constexpr int NCK = D / 32;  // 16-byte (bf16) or 8-byte (E4M3) loads per row slice
@@ -306,11 +355,9 @@ struct DecodeRegs {
 template <int D, int BS, bool FP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
   constexpr int NCK = D / 32;   // score MFMAs per 16-key block (k = 32 each)
-  constexpr int DQ = D / 4;     // d elements per lane group
   constexpr int ND = D / 16;    // 16-wide d blocks of the output
-  constexpr int ROWB = D * 2;
-  constexpr int WAVEB = kKeyTile * ROWB;
-  constexpr int EB = FP8 ? 1 : 2;
+  typedef LdsRow<D> L;
+  constexpr int WAVEB = kKeyTile * L::bytes;
   typedef DecodeRegs<D, FP8> Regs;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * WAVEB];
@@ -318,7 +365,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 
   const Item it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, q4 = lane >> 4;
   const int tok = n >> a.lg, g = n & (a.group - 1);
   const bool active = tok < it.nq;
@@ -327,14 +375,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
   const int hkv = a.c.hkv;
   lds_u8 *Vw = smem + wave * WAVEB;
 
-  // Q as the B operand of K * Q^T (16x16x32): lane holds q[n][q4*DQ + 8c .. +7].
+  // Q as the B operand of K * Q^T (16x16x32): for product c the lane holds
+  // q[n][32c + 8*q4 .. +7], matching the K slice its A operand holds.
   bf16x8 qf[NCK];
   {
     const unsigned char *qrow =
         (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
 #pragma unroll
     for (int c = 0; c < NCK; c++) {
-      uint4 v = active ? gload16(qrow + (q4 * DQ + 8 * c) * 2) : make_uint4(0, 0, 0, 0);
+      uint4 v = active ? gload16(qrow + (32 * c + 8 * q4) * 2) : make_uint4(0, 0, 0, 0);
       qf[c] = as_bf16x8(v);
     }
   }
@@ -349,23 +398,29 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
   const unsigned char *vc = (const unsigned char *)a.c.v;
   const int t_first = it.kv_lo / kKeyTile;
   const int ntiles = (it.kv_hi - it.kv_lo + kKeyTile - 1) / kKeyTile;
+  const int last_blk = (it.kv_hi - 1) / BS;
+  const int lim = min(pos, it.kv_hi - 1);
+  // tiles below t_full need no mask
+  const int t_full = min(it.pos0 + 1, it.kv_hi) / kKeyTile;
 
-  // Issue the loads of tile t (this lane: key row kb*16 + n, d slice q4).
+  // Issue the loads of tile t.  This lane: key row kb*16 + n, elements
+  // 32c + 8*q4 .. +7 for c = 0..NCK-1, so that each load instruction reads a
+  // contiguous 64-byte (bf16) slice of every key row of the block.
   auto load = [&](Regs &R, int t) {
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-      const int p = t * kKeyTile + kb * 16 + n;
-      const int pc = p < it.kv_hi ? p : it.kv_hi - 1;  // clamp: tail rows masked/zeroed later
-      const int64_t blk = bt[pc / BS];
-      const int64_t e = ((blk * hkv + it.kvh) * BS + (pc % BS)) * D + q4 * DQ;
+      const int bidx = min((t * kKeyTile + kb * 16) / BS, last_blk);  // wave-uniform
+      const int64_t blk = bt[bidx];
+      const int off = (BS == 16) ? n : kb * 16 + n;
+      const int64_t e = ((blk * hkv + it.kvh) * BS + off) * D + 8 * q4;
 #pragma unroll
       for (int c = 0; c < NCK; c++) {
         if constexpr (FP8) {
-          R.k[kb][c] = gload8_nt(kc + e + 8 * c);
-          R.v[kb][c] = gload8_nt(vc + e + 8 * c);
+          R.k[kb][c] = gload8(kc + e + 32 * c);
+          R.v[kb][c] = gload8(vc + e + 32 * c);
         } else {
-          R.k[kb][c] = gload16_nt(kc + (e + 8 * c) * 2);
-          R.v[kb][c] = gload16_nt(vc + (e + 8 * c) * 2);
+          R.k[kb][c] = gload16(kc + (e + 32 * c) * 2);
+          R.v[kb][c] = gload16(vc + (e + 32 * c) * 2);
         }
       }
       if constexpr (FP8) {
@@ -375,13 +430,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
     }
   };
 
-  auto compute = [&](Regs &R, int t) {
+  auto compute = [&](auto masked, Regs &R, int t) {
+    constexpr bool MASK = decltype(masked)::value;
     const int kbase = t * kKeyTile;
     // V tile -> this wave's LDS (rows beyond the range zeroed)
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
       const int r = kb * 16 + n;
-      const bool ok = kbase + r < it.kv_hi;
 #pragma unroll
       for (int c = 0; c < NCK; c++) {
         uint4 v;
@@ -389,15 +444,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
           v = e4m3x8_to_bf16x8(R.v[kb][c]);
         else
           v = R.v[kb][c];
-        if (!ok) v = make_uint4(0, 0, 0, 0);
-        lds_store16(Vw + r * ROWB + swz<D>(r, (q4 * DQ) / 8 + c) * 16, v);
+        if (MASK && kbase + r >= it.kv_hi) v = make_uint4(0, 0, 0, 0);
+        lds_store16(Vw + L::off(r, 4 * c + q4), v);
       }
     }
-    // S^T = K * Q^T per 16-key block
+    // S^T = K * Q^T per 16-key block; element r of block kb is key kb*16 + 4*q4 + r
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-      s[kb] = f32x4{};
 #pragma unroll
       for (int c = 0; c < NCK; c++) {
         bf16x8 kf;
@@ -405,58 +459,58 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
           kf = as_bf16x8(e4m3x8_to_bf16x8(R.k[kb][c]));
         else
           kf = as_bf16x8(R.k[kb][c]);
-        s[kb] = mfma16x16x32(kf, qf[c], s[kb]);
+        s[kb] = c == 0 ? mfma16x16x32(kf, qf[0], f32x4{}) : mfma16x16x32(kf, qf[c], s[kb]);
       }
     }
-    const bool need_mask = (kbase + kKeyTile - 1 > it.pos0) || (kbase + kKeyTile > it.kv_hi);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        float sl = a.scale_log2;
-        if constexpr (FP8) sl *= R.ksc[kb];
-        float v = s[kb][r] * sl;
-        if (need_mask) {
+        if (MASK) {
           const int key = kbase + kb * 16 + 4 * q4 + r;
-          if (!(key <= pos && key < it.kv_hi)) v = -INFINITY;
+          s[kb][r] = key <= lim ? s[kb][r] : -INFINITY;
         }
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
+        if constexpr (FP8) s[kb][r] *= R.ksc[kb];
+        mx = fmaxf(mx, s[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+    const float mxs = mx * a.scale_log2;
+    if (__any(mxs > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+    const float nm = -m;
     float psum = 0.f;
     bf16x4 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const float p = fast_exp2(s[kb][r] - m_new);
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, nm));
         psum += p;
         float pv = p;
         if constexpr (FP8) pv *= R.vsc[kb];
         pb[kb][r] = (__bf16)pv;
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < ND; db++) o[db] *= alpha;
+    l += psum;
 
     // the wave's own LDS writes above must land before its transpose reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int j = lane & 15;
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-      const int vrow = kb * 16 + 4 * q4 + (j >> 2);
+      const int vrow = kb * 16 + 4 * q4 + (n >> 2);
 #pragma unroll
       for (int db = 0; db < ND; db++) {
-        const int d0 = db * 16 + 4 * (j & 3);
-        bf16x4 af = lds_read_tr(Vw + vrow * ROWB + swz<D>(vrow, d0 >> 3) * 16 + (d0 & 7) * 2);
+        const int d0 = db * 16 + 4 * (n & 3);
+        bf16x4 af = lds_read_tr(Vw + L::off(vrow, d0 >> 3) + (d0 & 7) * 2);
         o[db] = mfma16x16x16(af, pb[kb], o[db]);
       }
     }
@@ -464,17 +518,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  auto step = [&](Regs &R, int t) {
+    if (t < t_full)
+      compute(FullTile{}, R, t);
+    else
+      compute(MaskedTile{}, R, t);
+  };
 
   Regs A, B;
   int tw = wave;
   if (tw < ntiles) load(A, t_first + tw);
   while (tw < ntiles) {
     if (tw + 4 < ntiles) load(B, t_first + tw + 4);
-    compute(A, t_first + tw);
+    step(A, t_first + tw);
     tw += 4;
     if (tw >= ntiles) break;
     if (tw + 4 < ntiles) load(A, t_first + tw + 4);
-    compute(B, t_first + tw);
+    step(B, t_first + tw);
     tw += 4;
   }
 
@@ -523,21 +583,32 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 
 // =============================================================================
 // LSE merge of split items ([Agentic] §4.3.3): for each row,
-// out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), lse = M + log2(sum),
-// M = max_i lse_i, parts without keys (lse = -inf) contribute nothing.
+// out = sum_i w_i o_i / sum_i w_i with w_i = 2^(lse_i - M), M = max_i lse_i,
+// lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing.
+// The weights of a task are computed once into LDS; each thread then reduces
+// four consecutive d of one row over the parts with 16-byte loads.
+constexpr int kMergeWeights = 8192;
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const Merge mt = a.merges[blockIdx.x];
   const float *po = mt.is_decode ? a.part_o_decode : a.part_o_prefill;
   const float *pl = mt.is_decode ? a.part_lse_decode : a.part_lse_prefill;
   const int rows = mt.nq << a.lg;
   const int rpp = mt.rows_per_part;
+  const int np = mt.nparts;
+  const bool cached = rows * np <= kMergeWeights;
+  __shared__ float sm_w[kMergeWeights];
   __shared__ float sm_max[kPrefillRows], sm_inv[kPrefillRows];
   for (int r = threadIdx.x; r < rows; r += blockDim.x) {
     float M = -INFINITY;
-    for (int i = 0; i < mt.nparts; i++) M = fmaxf(M, pl[(int64_t)(mt.part0 + i) * rpp + r]);
+    for (int i = 0; i < np; i++) M = fmaxf(M, pl[(int64_t)(mt.part0 + i) * rpp + r]);
     float S = 0.f;
-    if (M > -INFINITY)
-      for (int i = 0; i < mt.nparts; i++) S += fast_exp2(pl[(int64_t)(mt.part0 + i) * rpp + r] - M);
+    for (int i = 0; i < np; i++) {
+      const float li = pl[(int64_t)(mt.part0 + i) * rpp + r];
+      const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
+      S += w;
+      if (cached) sm_w[r * np + i] = w;
+    }
     sm_max[r] = M;
     sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
     if (a.lse_out) {
@@ -546,19 +617,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
   }
   __syncthreads();
-  const int d = a.d;
-  for (int idx = threadIdx.x; idx < rows * d; idx += blockDim.x) {
-    const int r = idx / d, e = idx % d;
+  const int d = a.d, d4 = d / 4;
+  for (int idx = threadIdx.x; idx < rows * d4; idx += blockDim.x) {
+    const int r = idx / d4, e = (idx % d4) * 4;
     const float M = sm_max[r];
-    float O = 0.f;
-    if (M > -INFINITY)
-      for (int i = 0; i < mt.nparts; i++) {
-        const int64_t slot = (int64_t)(mt.part0 + i) * rpp + r;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < np; i++) {
+      const int64_t slot = (int64_t)(mt.part0 + i) * rpp + r;
+      float w;
+      if (cached) {
+        w = sm_w[r * np + i];
+      } else {
         const float li = pl[slot];
-        if (li > -INFINITY) O += fast_exp2(li - M) * po[slot * d + e];
+        w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
       }
+      if (w != 0.f) O += w * *(const f32x4 *)(po + slot * d + e);
+    }
+    const float inv = sm_inv[r];
     const int64_t orow = (int64_t)(mt.row0 + (r >> a.lg)) * a.hq + mt.kvh * a.group + (r & (a.group - 1));
-    ((__bf16 *)a.out)[orow * d + e] = (__bf16)(O * sm_inv[r]);
+    bf16x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = (__bf16)(O[k] * inv);
+    *(bf16x4 *)((__bf16 *)a.out + orow * d + e) = v;
   }
 }
 

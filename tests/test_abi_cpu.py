@@ -83,6 +83,8 @@ def test_forward_rejects_bad_arguments(palib):
         (lambda: fwd(pa, cache(pa), hist=(60,), incr=(5,), max_blocks=4), E.PA_ERR_BAD_SHAPE),
         (lambda: fwd(pa, cache(pa), scale=float("nan")), E.PA_ERR_BAD_SHAPE),
         (lambda: fwd(pa, cache(pa), scale=float("inf")), E.PA_ERR_BAD_SHAPE),
+        (lambda: fwd(pa, cache(pa), scale=0.0), E.PA_ERR_BAD_SHAPE),
+        (lambda: fwd(pa, cache(pa), scale=-0.1), E.PA_ERR_BAD_SHAPE),
         (lambda: fwd(pa, cache(pa), q=None), E.PA_ERR_NULL_ARG),
         (lambda: fwd(pa, cache(pa), out=None), E.PA_ERR_NULL_ARG),
         (lambda: fwd(pa, cache(pa), bt=None), E.PA_ERR_NULL_ARG),
