@@ -141,15 +141,126 @@ def run_cpu_baseline(spec, budget_s):
                       f"workload, fp64, {dt:.1f} s, host {os.cpu_count()} CPUs"}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries.  The commands below are run from /tmp with
+# TMPDIR=/tmp and OUT an absolute output directory; --summarize-profiles OUT
+# then writes the text summaries committed under profiles/.
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_CMDS = {
+    "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o kt -- "
+              "python3 REPO/bench.py --steps 10 --warmup 2 --no-cpu",
+    "pmc": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/{w}_{counter} -o p -- "
+           "python3 REPO/bench.py --only {w} --steps 2 --warmup 1",
+    "copy": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/copy_{counter} -o p -- "
+            "python3 REPO/bench.py --copy-calibration 1024 --steps 2",
+}
+KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
+                  "paged_kv_cache_gqa_amd/csrc/pa_device.h",
+                  "paged_kv_cache_gqa_amd/csrc/pa_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+PREFILL_KERNEL = "void pa::prefill_kernel<128, 16, false>(pa::AttnArgs)"
+DECODE_KERNEL = "void pa::decode_kernel<128, 16, false>(pa::AttnArgs)"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(path):
+    import csv
+    import glob
+    f = glob.glob(os.path.join(path, "*counter_collection.csv"))[0]
+    acc = {}
+    for r in csv.DictReader(open(f)):
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_profiles(out):
+    import csv
+    import glob
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(out, "ktrace", "*kernel_stats.csv"))[0])))
+    by_name = {r["Name"]: r for r in stats}
+    copy_f = _counter_means(os.path.join(out, "pmc", "copy_FETCH_SIZE"))["__amd_rocclr_copyBuffer"][0]
+    copy_w = _counter_means(os.path.join(out, "pmc", "copy_WRITE_SIZE"))["__amd_rocclr_copyBuffer"][0]
+    gib = float(1 << 30)
+    f_scale, w_scale = gib / (copy_f * 1024), gib / (copy_w * 1024)
+    src = kernel_source_hash()
+    traffic = {}
+    for w, kname, unit_desc in (("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k"),
+                                ("decode", DECODE_KERNEL, "decode_batch_64x142k")):
+        fetch, nf = _counter_means(os.path.join(out, "pmc", f"{w}_FETCH_SIZE"))[kname]
+        write, nw = _counter_means(os.path.join(out, "pmc", f"{w}_WRITE_SIZE"))[kname]
+        tb = fetch * 1024 * f_scale + write * 1024 * w_scale
+        traffic[w] = tb
+        st = by_name[kname]
+        kshort = kname.split("pa::")[1].split("(")[0].replace("<", "_").replace(">", "").replace(", ", "_")
+        fn = os.path.join(ROOT, "profiles", f"{kshort}__{unit_desc}.txt")
+        with open(fn, "w") as fh:
+            fh.write(f"Kernel: {kname}\nWorkload: {unit_desc}\n\n")
+            fh.write("Commands (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root):\n")
+            fh.write("  " + PROFILE_CMDS["ktrace"] + "\n")
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                fh.write("  " + PROFILE_CMDS["pmc"].format(counter=c, w=w) + "\n")
+                fh.write("  " + PROFILE_CMDS["copy"].format(counter=c) + "\n")
+            fh.write(f"  python3 REPO/bench.py --summarize-profiles OUT\n\n")
+            fh.write("rocprofv3 --kernel-trace --stats (kernel_stats.csv rows of this run):\n")
+            fh.write("  Name | Calls | AverageNs | MinNs | MaxNs\n")
+            for r in stats:
+                if r["Name"].startswith(("void pa::", "pa::")):
+                    fh.write(f"  {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                             f"{r['MinNs']} | {r['MaxNs']}\n")
+            fh.write(f"\nThis kernel: average {float(st['AverageNs']) / 1e6:.4f} ms over {st['Calls']} calls\n\n")
+            fh.write("HBM counters per dispatch (mean over dispatches of this kernel):\n")
+            fh.write(f"  FETCH_SIZE {fetch:.1f} KiB ({nf} dispatches), WRITE_SIZE {write:.1f} KiB ({nw})\n")
+            fh.write(f"  copy calibration (1 GiB device copy): FETCH_SIZE {copy_f:.1f} KiB, WRITE_SIZE {copy_w:.1f} KiB\n")
+            fh.write(f"  scale factors: read x{f_scale:.4f}, write x{w_scale:.4f}\n")
+            fh.write(f"  HBM traffic per launch = {tb / 1e9:.4f} GB\n")
+            fh.write(f"\nKernel sources sha256[:16] = {src}\n")
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE, scaled by a 1 GiB copy\n")
+        fh.write(f"source_hash={src}\n")
+        fh.write(f"prefill_incremental_bytes={traffic['incremental']:.0f}\n")
+        fh.write(f"decode_batch_bytes={traffic['decode']:.0f}\n")
+    print(f"wrote profiles for source {src}")
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    return float(kv[key]) if key in kv else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--with-128k", action="store_true",
+                    help="also time the 128K-history incremental prefill (same kernel as the headline)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/*.txt from rocprofv3 outputs under DIR and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k"],
+                    help="run one workload (for profiling); prints its JSON object")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the path is built and measured on one "
               "MI355X only (multi-GPU sharding is not part of this build).", file=sys.stderr)
@@ -162,6 +273,25 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": max(1, args.steps)}))
+        return
+    if args.only:
+        spec = {"incremental": W.incremental(), "decode": W.decode_batch(),
+                "incremental_128k": W.incremental(131_072, 2_700, "incremental_128k")}[args.only]
+        r = Runner(pa, torch, spec, dev)
+        ms, kern = r.timed(args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, "ms_per_step": round(ms, 4),
+                          "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()}}))
+        return
 
     spec = W.incremental()
     r = Runner(pa, torch, spec, dev)
@@ -190,7 +320,8 @@ def main():
                    "num_kv_heads": 8, "head_dim": 128, "block_size": 16},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_kernel<128,16,false>",
+                     "traffic": measured_traffic("prefill_incremental_bytes"),
+                     "kernel": "prefill_kernel<128,16,false>",
                      "kernel_ms": round(k_ms, 4)},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
     }
@@ -215,10 +346,12 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(byts / (dk_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None, "algorithmic_bytes": int(byts)},
+                         "traffic": measured_traffic("decode_batch_bytes"),
+                         "algorithmic_bytes": int(byts)},
         }
         del r
         torch.cuda.empty_cache()
+    if args.with_128k:
         # incremental prefill at 128K history
         pspec = W.incremental(131_072, 2_700, "incremental_128k")
         r = Runner(pa, torch, pspec, dev)
