@@ -110,10 +110,16 @@ void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out)
   }
 }
 
+// Query rows per prefill tile: the LDS-DMA kernel (bf16 KV, head_dim 128)
+// takes 256, the register-staged kernel 128.
+int32_t prefill_tile_rows(const pa_kv_cache *c) {
+  return (c->dtype == PA_KV_BF16 && c->head_dim == 128) ? kDmaTileRows : kRegTileRows;
+}
+
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
-               int32_t group, int32_t d, Plan &P) {
+               int32_t group, int32_t d, int32_t tile_rows, Plan &P) {
   const int32_t dec_tokens = kDecodeRows / group;  // >= 1 for group <= 16
-  const int32_t pre_tokens = kPrefillRows / group;
+  const int32_t pre_tokens = tile_rows / group;
   std::vector<Tile> tiles;
   int64_t row = 0;
   for (int32_t s = 0; s < num_seqs; s++) {
@@ -144,6 +150,7 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   int64_t pchunk = INT32_MAX;
   if (np0 > 0 && np0 < kPrefillTargetItems)
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, kPrefillTargetItems));
+  if (tile_rows == kDmaTileRows) pchunk = std::min<int64_t>(pchunk, kMaxDmaItemKeys);
 
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
@@ -158,7 +165,7 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
         part0 = (int32_t)np;
         np += (int64_t)ranges.size();
         P.merges.push_back({t.row0, t.nq, kvh, part0, (int32_t)ranges.size(),
-                            t.decode ? kDecodeRows : kPrefillRows, t.decode ? 1 : 0, 0});
+                            t.decode ? kDecodeRows : tile_rows, t.decode ? 1 : 0, 0});
       }
       for (size_t i = 0; i < ranges.size(); i++) {
         Item it{t.seq, kvh, t.row0, t.pos0, t.nq, ranges[i].first, ranges[i].second,
@@ -192,9 +199,9 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + P.merges.size() * sizeof(Merge));
   P.plan_bytes = off;
   P.off_po_pre = off;
-  off = align256(off + (size_t)P.n_part_prefill * kPrefillRows * d * sizeof(float));
+  off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
   P.off_pl_pre = off;
-  off = align256(off + (size_t)P.n_part_prefill * kPrefillRows * sizeof(float));
+  off = align256(off + (size_t)P.n_part_prefill * tile_rows * sizeof(float));
   P.off_po_dec = off;
   off = align256(off + (size_t)P.n_part_decode * kDecodeRows * d * sizeof(float));
   P.off_pl_dec = off;
@@ -416,7 +423,7 @@ size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int
     return 0;
   Plan P;
   make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, P);
+            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
   return std::max<size_t>(P.total, 256);
 }
 
@@ -439,7 +446,8 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
-  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, P);
+  const int32_t tile_rows = prefill_tile_rows(cache);
+  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, tile_rows, P);
   if (!workspace) return fail(PA_ERR_NULL_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(PA_ERR_BAD_SHAPE, "workspace not 256-byte aligned");
   if (workspace_bytes < P.total)
@@ -467,6 +475,7 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   a.max_blocks = max_blocks_per_seq;
   a.hq = num_q_heads;
   a.group = group;
+  a.tile_rows = tile_rows;
   a.lg = log2_exact(group);
   a.scale_log2 = scale * 1.44269504088896341f;
   a.out = out;
@@ -544,7 +553,7 @@ pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens, int3
   if (!counts_out || (items_cap > 0 && !items_out)) return fail(PA_ERR_NULL_ARG, "output is NULL");
   Plan P;
   make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, P);
+            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
   counts_out[0] = (int32_t)P.prefill.size();
   counts_out[1] = (int32_t)P.decode.size();
   counts_out[2] = (int32_t)P.merges.size();

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       }
     if (a.lse_out && hh == 0) a.lse_out[(int64_t)(it.row0 + tok) * a.hq + qh] = lse2 * kLn2;
   } else {
-    float *prow = a.part_o + ((int64_t)it.part * kPrefillRows + row) * D;
+    float *prow = a.part_o + ((int64_t)it.part * kRegTileRows + row) * D;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -331,7 +331,352 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         for (int r = 0; r < 4; r++) v[r] = o[db][4 * i + r] * inv;
         *(f32x4 *)(prow + db * 32 + 8 * i + 4 * hh) = v;
       }
-    if (hh == 0) a.part_lse[(int64_t)it.part * kPrefillRows + row] = lse2;
+    if (hh == 0) a.part_lse[(int64_t)it.part * kRegTileRows + row] = lse2;
+  }
+}
+
+// =============================================================================
+// Prefill for bf16 KV with head_dim 128 ("ping-pong"): one work-group of 8
+// waves per CU, 256 query rows; waves 0-3 (group 0) own rows 0-127, waves 4-7
+// (group 1) rows 128-255, each wave 32 rows.  Every tile step has two phases
+// separated by work-group barriers; in each phase one group issues the tile's
+// matrix-core work (S(t+1) = K(t+1) Q^T and O += V(t)^T P(t)^T) while the
+// other turns scores into probabilities on the vector ALUs, so each SIMD
+// always has one wave feeding its matrix core and one wave doing softmax.
+//
+// K/V tiles (64 keys) live in a four-stage LDS ring filled directly from HBM
+// by buffer loads that write LDS (no register staging); tile t+3 is requested
+// right after the barrier that opens step t.  Each load covers four key rows
+// of one cache block; its buffer resource starts at those rows and ends at
+// the range's last key, so rows past the end read as zeros without touching
+// memory.  The loads are issued as inline assembly with explicit vmcnt waits:
+// the compiler neither reorders them nor inserts waits of its own for them.
+// LDS tile rows are 256 bytes with the 16-byte chunk index XOR-swizzled by
+// the row (conflict-free for both the 16-byte and the transposing reads).
+// The item's block ids are staged in LDS once (items span at most
+// kMaxDmaItemKeys keys).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ void dma_load16(i32x4_t rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 16)
+#define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
+
+// Work-group barrier without a memory fence: LDS hazards around it are
+// handled by explicit waits; the compiler-only fences keep memory operations
+// and the scheduling barriers keep all instructions on their side of it.
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int BS>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int NC = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int TILEB = kKeyTile * D * 2;  // 16 KB
+  constexpr int STAGEB = 2 * TILEB;        // K + V of one tile
+  constexpr int NST = 4;
+  constexpr int MAXB = kMaxDmaItemKeys / BS + 2;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NST * STAGEB];
+  __shared__ int bt_lds[MAXB];
+  lds_u8 *smem = (lds_u8 *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const Item it = a.items[blockIdx.x];
+  const float scale_log2 = a.scale_log2;
+  const int kv_hi = it.kv_hi, kvh = it.kvh, hkv = a.c.hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int col = lane & 31, hh = lane >> 5;
+  const int row = wave * 32 + col;
+  const int tok = row >> a.lg, g = row & (a.group - 1);
+  const bool active = tok < it.nq;
+  const int pos = it.pos0 + tok;
+  const int qh = kvh * a.group + g;
+
+  bf16x8 qf[NC];
+  {
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+      uint4 v = active ? gload16(qrow + (c * 16 + hh * 8) * 2) : make_uint4(0, 0, 0, 0);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+
+  const int t_begin = it.kv_lo / kKeyTile;
+  const int t_end = (kv_hi + kKeyTile - 1) / kKeyTile;
+  const int t_full = max(t_begin, min(t_end, min(it.pos0 + 1, kv_hi) / kKeyTile));
+  const int blk0 = it.kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+  const int lim = min(pos, kv_hi - 1);
+
+  {  // stage the item's block ids
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
+  }
+
+  // per-lane LDS offsets (XOR swizzle folded): K A-operand reads and V transposing reads
+  int kofs[NC], vofs[ND];
+  {
+    const int y = col & 7;
+#pragma unroll
+    for (int c = 0; c < NC; c++) kofs[c] = col * 256 + hh * 16 + ((c ^ y) << 5);
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int r0 = 4 * hh + (j16 >> 2);  // row within a 16-key step
+    const int y2 = r0 & 7;
+    const int c0 = (g16 & 1) * 2 + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+      vofs[db] = r0 * 256 + ((db ^ (y2 >> 1)) << 6) + ((c0 ^ ((2 * y2) & 3)) << 4) + (j16 & 1) * 8;
+  }
+  // this wave's DMA lanes: instructions jj = 0, 1 cover tile rows 8*wave + 4*jj .. +3
+  int voff[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; jj++) {
+    const int lr = lane >> 4, pc = lane & 15;
+    voff[jj] = lr * 256 + ((pc ^ (((4 * jj + lr) & 7) << 1)) << 4);
+  }
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+
+  __syncthreads();  // block ids visible
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int tt = min(t, t_end - 1);
+    const uint32_t st = smem_addr + ((t - t_begin) & (NST - 1)) * STAGEB;
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+      const int j = 2 * wave + jj;
+      const int rpos = tt * kKeyTile + 4 * j;
+      const int64_t blk = __builtin_amdgcn_readfirstlane(bt_lds[min(rpos / BS, last_blk) - blk0]);
+      const int nrec = __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos, 0), 4) * (D * 2) : 0);
+      const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
+      const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
+                          __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
+                          __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16(rk, voff[jj], st + j * 1024);
+      dma_load16(rv, voff[jj], st + TILEB + j * 1024);
+    }
+  };
+  auto stage = [&](int t) __attribute__((always_inline)) {
+    return (const lds_u8 *)(smem + ((t - t_begin) & (NST - 1)) * STAGEB);
+  };
+
+  float m = kNegBig, l = 0.f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; i++) o[i] = f32x16{};
+  f32x16 S[2];
+  bf16x8 pb[4];
+
+  // Matrix-core phase: O += V(t)^T P(t)^T (16 MFMAs, 32 transposing reads),
+  // then S(t+1) = K(t+1) Q^T (16 MFMAs, 16 reads).  The scheduling-group
+  // pattern keeps the LDS reads a few MFMAs ahead of their use, so read
+  // latency hides behind the matrix core and only a handful of fragments
+  // occupy registers at any time.  The score product alternates its two
+  // accumulators so consecutive MFMAs are independent.
+  auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
+    constexpr bool with_qk = decltype(with_qk_tag)::value;
+    bf16x8 vf[16];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+      for (int db = 0; db < ND; db++) {
+        const bf16x4 h0 = lds_read_tr(Vb + ks * 4096 + vofs[db]);
+        const bf16x4 h1 = lds_read_tr(Vb + ks * 4096 + 2048 + vofs[db]);
+        vf[ks * ND + db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] = mfma32x32x16(vf[ks * ND + db], pb[ks], o[db]);
+    if constexpr (with_qk) {
+      bf16x8 kf[16];
+#pragma unroll
+      for (int c = 0; c < NC; c++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) kf[2 * c + kb] = as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c]));
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[kb], qf[0], f32x16{});
+#pragma unroll
+      for (int c = 1; c < NC; c++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[2 * c + kb], qf[c], S[kb]);
+      // order: 4 reads; (MFMA, 2 reads) x 14; then the score reads interleaved
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 14; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 12; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 14; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+  auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[0])), qf[0], f32x16{});
+#pragma unroll
+      for (int c = 1; c < NC; c++)
+        S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c])), qf[c], S[kb]);
+    }
+  };
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    if (t >= t_full) {
+      const int kbase = t * kKeyTile;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int key = kbase + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          S[kb][e] = key <= lim ? S[kb][e] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) mx = fmaxf(mx, S[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * scale_log2;
+    if (__any(mxs > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+    const float nm = -m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const float p = fast_exp2(__builtin_fmaf(S[kb][e], scale_log2, nm));
+        S[kb][e] = p;
+        psum += p;
+      }
+    l += psum;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int kb = ks >> 1, i0 = (ks & 1) * 2;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        pb[ks][r] = (__bf16)S[kb][4 * i0 + r];
+        pb[ks][4 + r] = (__bf16)S[kb][4 * (i0 + 1) + r];
+      }
+    }
+  };
+
+  // prologue: three tiles requested; S(t0) for both groups, P(t0) for group 0
+  issue(t_begin);
+  issue(t_begin + 1);
+  issue(t_begin + 2);
+  PA_WAIT_VMCNT(8);
+  wg_barrier();
+  qk_only(stage(t_begin));
+  // Each group runs its own loop (same number of barriers); step t opens
+  // once this wave's share of tile t+1 has landed (its tile t+2 loads may
+  // still be in flight), then requests tile t+3 into the stage tile t-1 left.
+  if (grp == 0) {
+    wg_barrier();
+    softmax(t_begin);
+    int t = t_begin;
+    for (; t + 1 < t_end; t++) {
+      PA_WAIT_VMCNT(4);
+      wg_barrier();
+      issue(t + 3);
+      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
+      wg_barrier();
+      softmax(t + 1);                                          // phase B: vector ALUs
+    }
+    PA_WAIT_VMCNT(4);
+    wg_barrier();
+    issue(t + 3);
+    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
+    wg_barrier();
+  } else {
+    wg_barrier();
+    int t = t_begin;
+    for (; t + 1 < t_end; t++) {
+      PA_WAIT_VMCNT(4);
+      wg_barrier();
+      issue(t + 3);
+      softmax(t);                                              // phase A: vector ALUs
+      wg_barrier();
+      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
+    }
+    PA_WAIT_VMCNT(4);
+    wg_barrier();
+    issue(t + 3);
+    softmax(t);
+    wg_barrier();
+    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
+  }
+  PA_WAIT_VMCNT(0);  // the trailing (empty) tile requests complete before exit
+
+  const float lt = l + __shfl_xor(l, 32);
+  if (!active) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+  if (it.part < 0) {
+    unsigned char *orow =
+        (unsigned char *)a.out + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; r++) v[r] = (__bf16)(o[db][4 * i + r] * inv);
+        *(bf16x4 *)(orow + (db * 32 + 8 * i + 4 * hh) * 2) = v;
+      }
+    if (a.lse_out && hh == 0) a.lse_out[(int64_t)(it.row0 + tok) * a.hq + qh] = lse2 * kLn2;
+  } else {
+    float *prow = a.part_o + ((int64_t)it.part * kDmaTileRows + row) * D;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; r++) v[r] = o[db][4 * i + r] * inv;
+        *(f32x4 *)(prow + db * 32 + 8 * i + 4 * hh) = v;
+      }
+    if (hh == 0) a.part_lse[(int64_t)it.part * kDmaTileRows + row] = lse2;
   }
 }
 
@@ -598,7 +943,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int np = mt.nparts;
   const bool cached = rows * np <= kMergeWeights;
   __shared__ float sm_w[kMergeWeights];
-  __shared__ float sm_max[kPrefillRows], sm_inv[kPrefillRows];
+  __shared__ float sm_max[kPrefillRowsMax], sm_inv[kPrefillRowsMax];
   for (int r = threadIdx.x; r < rows; r += blockDim.x) {
     float M = -INFINITY;
     for (int i = 0; i < np; i++) M = fmaxf(M, pl[(int64_t)(mt.part0 + i) * rpp + r]);
@@ -645,6 +990,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 // =============================================================================
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
+  if constexpr (!FP8 && D == 128) {
+    if (a.tile_rows == kDmaTileRows) {
+      hipLaunchKernelGGL((prefill_pp_kernel<BS>), dim3(n), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((prefill_kernel<D, BS, FP8>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }

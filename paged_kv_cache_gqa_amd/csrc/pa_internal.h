@@ -53,6 +53,7 @@ struct AttnArgs {
   int32_t max_blocks;
   int32_t hq;
   int32_t group;          // G = hq / hkv (power of two)
+  int32_t tile_rows;      // query rows per prefill tile (128 or 256)
   int32_t lg;             // log2(G)
   float scale_log2;       // softmax scale * log2(e)
   void *out;              // bf16 [total_q][hq][d]
@@ -102,7 +103,10 @@ struct GatherArgs {
   int32_t row_bytes;      // d * element bytes
 };
 
-constexpr int kPrefillRows = 128;  // query rows (tokens x heads) per prefill tile
+constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
+constexpr int kDmaTileRows = 256;  // query rows per tile of prefill_dma_kernel
+constexpr int kPrefillRowsMax = 256;
+constexpr int kMaxDmaItemKeys = 65536;  // keys per item of prefill_pp_kernel (block ids staged in LDS)
 constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
 

@@ -142,7 +142,9 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
     parts = {}
     for it in items:
         seq, kvh, row0, pos0, nq, lo, hi, part = (int(x) for x in it)
-        assert 0 <= kvh < hkv and nq >= 1 and nq * G <= 128
+        assert 0 <= kvh < hkv and nq >= 1 and nq * G <= (256 if d == 128 else 128)
+        if d == 128 and nq * G > 16:  # LDS-staged block ids bound the item's span
+            assert hi - lo <= 65536
         assert lo % 64 == 0 and hi > lo
         assert rowstart[seq] <= row0 and row0 + nq <= rowstart[seq] + incr[seq]
         assert pos0 == hist[seq] + (row0 - rowstart[seq])
