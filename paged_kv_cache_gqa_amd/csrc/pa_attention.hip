@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         if constexpr (NSC > 1) s[kb][e] *= sl[kb * 2 + (e >> 3)];
         mx = fmaxf(mx, s[kb][e]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     const float mxs = NSC > 1 ? mx : mx * sl[0];
     if (__any(mxs > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mxs);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: combine the two key halves' sums, normalise, store
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = xor32_sum(l);
   if (!active) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 //
 // K/V tiles (64 keys) live in a four-stage LDS ring filled directly from HBM
 // by buffer loads that write LDS (no register staging); tile t+3 is requested
-// right after the barrier that opens step t.  Each load covers four key rows
+// in step t by each wave during its softmax phase.  Each load covers four key rows
 // of one cache block; its buffer resource starts at those rows and ends at
 // the range's last key, so rows past the end read as zeros without touching
 // memory.  The loads are issued as inline assembly with explicit vmcnt waits:
@@ -354,12 +354,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 // LDS tile rows are 256 bytes with the 16-byte chunk index XOR-swizzled by
 // the row (conflict-free for both the 16-byte and the transposing reads).
 // The item's block ids are staged in LDS once (items span at most
-// kMaxDmaItemKeys keys).
+// kMaxDmaItemKeys keys) and read one tile ahead of their use.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+// The compiler does not see inside the asm, so it cannot pad the hazards of
+// its operands: the resource words come from v_readfirstlane (a VALU write
+// of an SGPR needs 5 wait states before a vector-memory instruction reads
+// it) and M0 was just written by a scalar move (1 wait state before a load
+// that writes LDS).  The leading s_nop 4 provides both.
 __device__ __forceinline__ void dma_load16(i32x4_t rsrc, int voff, uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
 // s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 16)
@@ -376,6 +381,9 @@ __device__ __forceinline__ void wg_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+#ifndef PA_LOOKAHEAD
+#define PA_LOOKAHEAD 12
+#endif
 template <int BS>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -454,23 +462,32 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
 
   __syncthreads();  // block ids visible
 
+  // Rows 8*wave .. 8*wave+7 of a tile lie in one cache block (BS is a
+  // multiple of 8), so each wave needs one block id per tile; it is read
+  // from LDS one tile ahead so the read's latency is never waited on.
+  auto block_of = [&](int t) __attribute__((always_inline)) {
+    const int tt = min(t, t_end - 1);
+    return bt_lds[min((tt * kKeyTile + 8 * wave) / BS, last_blk) - blk0];
+  };
+  int blk_next = block_of(t_begin);
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int tt = min(t, t_end - 1);
+    const int64_t blk = __builtin_amdgcn_readfirstlane(blk_next);
+    blk_next = block_of(t + 1);
     const uint32_t st = smem_addr + ((t - t_begin) & (NST - 1)) * STAGEB;
+    const int rpos = tt * kKeyTile + 8 * wave;
+    const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
 #pragma unroll
     for (int jj = 0; jj < 2; jj++) {
-      const int j = 2 * wave + jj;
-      const int rpos = tt * kKeyTile + 4 * j;
-      const int64_t blk = __builtin_amdgcn_readfirstlane(bt_lds[min(rpos / BS, last_blk) - blk0]);
-      const int nrec = __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos, 0), 4) * (D * 2) : 0);
-      const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
-      const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+      const int nrec =
+          __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos - 4 * jj, 0), 4) * (D * 2) : 0);
+      const uint64_t ka = (uint64_t)(kc + base + jj * 4 * D * 2), va = (uint64_t)(vc + base + jj * 4 * D * 2);
       const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
                           __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
       const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
                           __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-      dma_load16(rk, voff[jj], st + j * 1024);
-      dma_load16(rv, voff[jj], st + TILEB + j * 1024);
+      dma_load16(rk, voff[jj], st + (2 * wave + jj) * 1024);
+      dma_load16(rv, voff[jj], st + TILEB + (2 * wave + jj) * 1024);
     }
   };
   auto stage = [&](int t) __attribute__((always_inline)) {
@@ -517,31 +534,28 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
       for (int c = 1; c < NC; c++)
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[2 * c + kb], qf[c], S[kb]);
-      // order: 4 reads; (MFMA, 2 reads) x 14; then the score reads interleaved
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      // order: 12 reads ahead; (MFMA, 2 reads) x 16 over the value product;
+      // then the last score reads between the first score MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, PA_LOOKAHEAD, 0);
 #pragma unroll
-      for (int i = 0; i < 14; i++) {
+      for (int i = 0; i < 16; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int i = 0; i < 12; i++) {
+      for (int i = 0; i < PA_LOOKAHEAD - 8; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - (PA_LOOKAHEAD - 8), 0);
     } else {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, PA_LOOKAHEAD, 0);
 #pragma unroll
-      for (int i = 0; i < 14; i++) {
+      for (int i = 0; i < (32 - PA_LOOKAHEAD) / 2; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - (32 - PA_LOOKAHEAD) / 2, 0);
     }
   };
   auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) mx = fmaxf(mx, S[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     const float mxs = mx * scale_log2;
     if (__any(mxs > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mxs);
@@ -610,7 +624,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
   qk_only(stage(t_begin));
   // Each group runs its own loop (same number of barriers); step t opens
   // once this wave's share of tile t+1 has landed (its tile t+2 loads may
-  // still be in flight), then requests tile t+3 into the stage tile t-1 left.
+  // still be in flight).  Tile t+3 is requested into the stage tile t-1 left
+  // during the wave's softmax phase of step t, keeping the load issue off
+  // the matrix-core phase.
   if (grp == 0) {
     wg_barrier();
     softmax(t_begin);
@@ -618,16 +634,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
     for (; t + 1 < t_end; t++) {
       PA_WAIT_VMCNT(4);
       wg_barrier();
-      issue(t + 3);
       gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
       wg_barrier();
-      softmax(t + 1);                                          // phase B: vector ALUs
+      issue(t + 3);                                            // phase B: loads, vector ALUs
+      softmax(t + 1);
     }
     PA_WAIT_VMCNT(4);
     wg_barrier();
-    issue(t + 3);
     gemm(std::false_type{}, stage(t) + TILEB, nullptr);
     wg_barrier();
+    issue(t + 3);
   } else {
     wg_barrier();
     int t = t_begin;
@@ -648,7 +664,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
   }
   PA_WAIT_VMCNT(0);  // the trailing (empty) tile requests complete before exit
 
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = xor32_sum(l);
   if (!active) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
@@ -819,8 +835,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
         if constexpr (FP8) s[kb][r] *= R.ksc[kb];
         mx = fmaxf(mx, s[kb][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
     const float mxs = mx * a.scale_log2;
     if (__any(mxs > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mxs);
@@ -884,8 +900,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
   }
 
   // ---- combine the four waves' states through LDS
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = xor16_sum(l);
+  l = xor32_sum(l);
   __syncthreads();
   float *red_o = (float *)smem_raw;                  // [4][16][D]
   float *red_m = red_o + 4 * 16 * D;                 // [4][16]

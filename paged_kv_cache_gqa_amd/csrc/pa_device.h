@@ -48,6 +48,29 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_u8 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
 }
 
+// Cross-lane reductions between lane l and lane l ^ 32 (or l ^ 16) without
+// an LDS round trip.  v_permlane32_swap exchanges lanes 32-63 of its first
+// operand with lanes 0-31 of its second; fed the same value twice, the two
+// results hold {v[l], v[l ^ 32]} in some order, so any symmetric operation
+// of the pair is the same on every lane.  v_permlane16_swap does the same
+// between odd and even 16-lane rows (lane l and lane l ^ 16).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
