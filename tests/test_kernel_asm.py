@@ -1,0 +1,90 @@
+"""Static checks on the gfx950 assembly of the attention kernels (CPU only).
+
+The LDS-filling buffer loads are inline assembly, so the compiler cannot pad
+the hazards of their operands.  The ISA requires 5 wait states between a
+VALU write of an SGPR (v_readfirstlane) and a vector-memory instruction that
+reads it, and 1 wait state between a scalar write of M0 and a buffer load
+that writes LDS.  This test compiles the kernels to assembly and checks every
+such load.  It also checks that no kernel spills to scratch and that no
+packed fp32 VALU instruction was generated.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_gqa_amd import build as pabuild
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pabuild.HIPCC), reason="hipcc not installed")
+
+
+@pytest.fixture(scope="module")
+def attention_asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "pa_attention.s"
+    flags = [f for f in pabuild.FLAGS if f not in ("-fPIC",)]
+    cmd = [pabuild.HIPCC, *flags, "--cuda-device-only", "-S",
+           os.path.join(pabuild.CSRC, "pa_attention.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out.read_text()
+
+
+def _functions(asm):
+    """{kernel symbol: [instruction lines]} for every kernel body."""
+    funcs = {}
+    for m in re.finditer(r"^(_Z\S+):\s*(?:;.*)?$", asm, re.M):
+        name = m.group(1)
+        end = asm.find(".Lfunc_end", m.end())
+        body = asm[m.end():end].split("\n")
+        funcs[name] = [l.strip() for l in body if l.strip() and not l.strip().startswith(";")]
+    return funcs
+
+
+def _sgprs(op):
+    m = re.match(r"s\[(\d+):(\d+)\]$", op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", op)
+    return {int(m.group(1))} if m else set()
+
+
+def _wait_states(line):
+    op = line.split()[0]
+    return int(line.split()[1], 0) + 1 if op == "s_nop" else 1
+
+
+def test_lds_dma_hazards_padded(attention_asm):
+    funcs = _functions(attention_asm)
+    checked = 0
+    for name, lines in funcs.items():
+        for k, line in enumerate(lines):
+            if not (line.startswith("buffer_load") and " lds" in line):
+                continue
+            checked += 1
+            rsrc = _sgprs(line.split(None, 1)[1].split(",")[1].strip())
+            assert rsrc, line
+            dist, m0_done, sgpr_done = 0, False, False
+            for prev in reversed(lines[max(0, k - 64):k]):
+                if prev.endswith(":"):
+                    break  # block boundary: only straight-line predecessors are checked
+                parts = prev.split(None, 1)
+                dst = parts[1].split(",")[0].strip() if len(parts) > 1 else ""
+                if not m0_done and dst == "m0":
+                    assert dist >= 1, f"{name}: M0 write too close to LDS load: {prev} -> {line}"
+                    m0_done = True
+                if not sgpr_done and parts[0].startswith("v_") and _sgprs(dst) & rsrc:
+                    assert dist >= 5, f"{name}: VALU SGPR write too close to LDS load: {prev} -> {line}"
+                    sgpr_done = True
+                if m0_done and sgpr_done:
+                    break
+                dist += _wait_states(prev)
+    assert checked > 0, "no LDS-filling buffer loads found"
+
+
+def test_no_scratch_and_no_packed_fp32(attention_asm):
+    for name, lines in _functions(attention_asm).items():
+        for line in lines:
+            op = line.split()[0]
+            assert not op.startswith("scratch_"), f"{name} spills: {line}"
+            assert op not in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"), f"{name}: {line}"
