@@ -183,6 +183,18 @@ PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_len
                                int32_t num_seqs, int32_t num_q_heads, const pa_kv_cache *cache,
                                int32_t *items_out, int32_t items_cap, int32_t *counts_out);
 
+/* Test hook for the persistent prefill launch: when the plan for these HOST
+ * lengths runs the 256-row kernel (bf16 KV, head_dim 128) with one
+ * work-group per balanced range of work, *num_groups_out receives the number
+ * of work-groups n and first_out[0..n] the offsets into the prefill items
+ * (as listed by pa_debug_plan) where each work-group's items begin, with
+ * first_out[n] = the number of prefill items.  n = 0 (nothing written) for
+ * plans without such a launch.  PA_ERR_WORKSPACE_TOO_SMALL if cap < n + 1. */
+PA_API pa_status pa_debug_plan_groups(const int32_t *hist_lens, const int32_t *incr_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      const pa_kv_cache *cache, int32_t *first_out, int32_t cap,
+                                      int32_t *num_groups_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,7 +2,7 @@
 marshalling only.  Every step of the attention path runs in the HIP kernels;
 torch tensors are used for device memory and streams.
 
-The library must have been built (``paged_kv_cache_gqa_amd.build.build()``);
+The library must have been built (``python paged_kv_cache_gqa_amd/build.py``);
 importing this module without it raises ImportError -- there is no fallback.
 """
 from __future__ import annotations
@@ -22,7 +22,8 @@ TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
 
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
-           "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan")
+           "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
+           "pa_debug_plan_groups")
 
 
 class pa_kv_cache(C.Structure):
@@ -41,7 +42,7 @@ class PagedAttnError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with paged_kv_cache_gqa_amd.build.build()")
+        raise ImportError(f"{LIB_PATH} is missing: build it with python paged_kv_cache_gqa_amd/build.py")
     L = C.CDLL(LIB_PATH)
     P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     pc = C.POINTER(pa_kv_cache)
@@ -55,8 +56,9 @@ def _load():
     L.pa_timing_enable.argtypes = [C.c_int]
     L.pa_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
     L.pa_debug_plan.argtypes = [P, P, i32, i32, pc, P, i32, P]
+    L.pa_debug_plan_groups.argtypes = [P, P, i32, i32, pc, P, i32, P]
     for f in ("kv_append", "paged_attn_forward", "pa_debug_gather", "pa_timing_enable",
-              "pa_timing_read", "pa_debug_plan"):
+              "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -154,3 +156,20 @@ def pa_debug_plan(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache):
     _check(lib.pa_debug_plan(*args, items.ctypes.data_as(C.c_void_p), cap,
                              counts.ctypes.data_as(C.c_void_p)))
     return items[:cap], counts
+
+
+def pa_debug_plan_groups(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache):
+    """Per-work-group item offsets of the persistent prefill launch (int32 [n + 1]);
+    empty when the plan has no such launch."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    ng = C.c_int32(0)
+    args = [h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), num_q_heads,
+            C.byref(cache)]
+    st = lib.pa_debug_plan_groups(*args, None, 0, C.byref(ng))
+    if st not in (PA_OK, PA_ERR_WORKSPACE_TOO_SMALL):
+        _check(st)
+    if ng.value == 0:
+        return np.zeros(0, dtype=np.int32)
+    first = np.zeros(ng.value + 1, dtype=np.int32)
+    _check(lib.pa_debug_plan_groups(*args, first.ctypes.data_as(C.c_void_p), len(first), C.byref(ng)))
+    return first

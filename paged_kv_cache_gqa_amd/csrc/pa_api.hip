@@ -81,12 +81,15 @@ constexpr int kDecodeTargetItems = 32 * kNumCUs;
 constexpr int kDecodeMinChunk = 2048;
 constexpr int kPrefillTargetItems = 8 * kNumCUs;
 constexpr int kPrefillMinChunk = 4096;
+constexpr int kMinGroupKeyTiles = 16;  // persistent launch: at least 1024 keys per work-group
 
 struct Plan {
   std::vector<Item> prefill, decode;
   std::vector<Merge> merges;
+  std::vector<int32_t> wg_first;  // persistent prefill launch: items of work-group w are
+                                  // prefill[wg_first[w] .. wg_first[w+1]); empty otherwise
   int64_t n_part_prefill = 0, n_part_decode = 0;
-  size_t off_prefill = 0, off_decode = 0, off_merges = 0, plan_bytes = 0;
+  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, plan_bytes = 0;
   size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
 };
 
@@ -114,6 +117,95 @@ void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out)
 // takes 256, the register-staged kernel 128.
 int32_t prefill_tile_rows(const pa_kv_cache *c) {
   return (c->dtype == PA_KV_BF16 && c->head_dim == 128) ? kDmaTileRows : kRegTileRows;
+}
+
+// Persistent split for the 256-row kernel.  The prefill work -- every tile
+// times every KV head, measured in 64-key steps -- is laid out KV-head-major,
+// then by key chunk, then by tile, and cut into nwg contiguous ranges of equal
+// length (to within one step), one per work-group: every compute unit gets
+// the same amount of work.  Key chunks are common to all tiles (chunk c is
+// keys [c*C, (c+1)*C)), so the work-groups that walk one chunk of different
+// tiles at the same time read the same K/V bytes and share them in L2.  A
+// (tile, head) whose keys are spread over several chunks or ranges writes
+// partials merged by LSE.  Range r goes to work-group w with r = (w % 8) *
+// (nwg / 8) + w / 8 when nwg is a multiple of 8: work-group ids are dispatched
+// round-robin over the eight XCDs, so each XCD (and its L2) holds one
+// contiguous stretch of the work, i.e. mostly one KV head.
+constexpr int kGroupPieces = 3;  // target pieces of work per work-group
+
+void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, Plan &P) {
+  std::vector<int32_t> pre;  // prefill tiles
+  int32_t max_steps = 0;
+  int64_t W = 0;
+  for (size_t i = 0; i < tiles.size(); i++) {
+    if (tiles[i].decode) continue;
+    pre.push_back((int32_t)i);
+    const int32_t steps = (int32_t)cdiv64(tiles[i].keys, kKeyTile);
+    max_steps = std::max(max_steps, steps);
+    W += (int64_t)steps * hkv;
+  }
+  if (W == 0) return;
+  const int32_t nwg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kNumCUs, W / kMinGroupKeyTiles));
+  // chunk length (in steps) so that a work-group's range spans about
+  // kGroupPieces (tile, chunk) pieces
+  const int64_t units = (int64_t)pre.size() * hkv;
+  const int64_t nchunk = std::max<int64_t>(1, cdiv64((int64_t)kGroupPieces * nwg, units));
+  const int32_t C = (int32_t)std::max<int64_t>(1, cdiv64(max_steps, nchunk));
+
+  struct Piece {
+    int32_t unit, lo, hi, range;  // unit = kvh * pre.size() + tile index; [lo, hi) in steps
+  };
+  std::vector<Piece> pieces;
+  auto bound = [&](int64_t r) { return W * r / nwg; };  // first step of range r
+  constexpr int32_t kMaxSegSteps = kMaxDmaItemKeys / kKeyTile;
+  int64_t pos = 0;
+  int32_t r = 0;
+  for (int32_t kvh = 0; kvh < hkv; kvh++)
+    for (int32_t c0 = 0; c0 < max_steps; c0 += C)
+      for (size_t k = 0; k < pre.size(); k++) {
+        const int32_t steps = (int32_t)cdiv64(tiles[pre[k]].keys, kKeyTile);
+        if (c0 >= steps) continue;
+        const int32_t c1 = std::min(steps, c0 + C);
+        for (int32_t lo = c0; lo < c1;) {
+          while (bound(r + 1) <= pos) r++;
+          const int32_t hi = (int32_t)std::min<int64_t>({(int64_t)c1, lo + bound(r + 1) - pos,
+                                                         (int64_t)lo + kMaxSegSteps});
+          pieces.push_back({kvh * (int32_t)pre.size() + (int32_t)k, lo, hi, r});
+          pos += hi - lo;
+          lo = hi;
+        }
+      }
+  // partial slots: consecutive per (tile, head) unit, in key order
+  std::vector<int32_t> count(units, 0), part0(units, -1), seen(units, 0);
+  for (const Piece &pc : pieces) count[pc.unit]++;
+  for (int64_t u = 0; u < units; u++) {
+    if (count[u] < 2) continue;
+    const Tile &t = tiles[pre[u % pre.size()]];
+    part0[u] = (int32_t)P.n_part_prefill;
+    P.n_part_prefill += count[u];
+    P.merges.push_back({t.row0, t.nq, (int32_t)(u / pre.size()), part0[u], count[u], tile_rows, 0, 0});
+  }
+  std::vector<std::vector<Item>> by_range(nwg);
+  for (const Piece &pc : pieces) {
+    const Tile &t = tiles[pre[pc.unit % pre.size()]];
+    const int32_t part = part0[pc.unit] < 0 ? -1 : part0[pc.unit] + seen[pc.unit]++;
+    by_range[pc.range].push_back({t.seq, pc.unit / (int32_t)pre.size(), t.row0, t.pos0, t.nq,
+                                  pc.lo * kKeyTile, std::min(t.keys, pc.hi * kKeyTile), part});
+  }
+  // Within a range, pieces that start at a chunk boundary run first: every
+  // work-group then starts its first piece at the start of a chunk at the
+  // same moment, and the work-groups on one chunk stay in step.
+  for (auto &v : by_range)
+    std::stable_sort(v.begin(), v.end(), [&](const Item &x, const Item &y) {
+      return (x.kv_lo % (C * kKeyTile) == 0) > (y.kv_lo % (C * kKeyTile) == 0);
+    });
+  P.wg_first.assign(nwg + 1, 0);
+  for (int32_t w = 0; w < nwg; w++) {
+    const int32_t rr = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;
+    P.wg_first[w] = (int32_t)P.prefill.size();
+    P.prefill.insert(P.prefill.end(), by_range[rr].begin(), by_range[rr].end());
+  }
+  P.wg_first[nwg] = (int32_t)P.prefill.size();
 }
 
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
@@ -150,11 +242,13 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   int64_t pchunk = INT32_MAX;
   if (np0 > 0 && np0 < kPrefillTargetItems)
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, kPrefillTargetItems));
-  if (tile_rows == kDmaTileRows) pchunk = std::min<int64_t>(pchunk, kMaxDmaItemKeys);
 
+  const bool persistent = tile_rows == kDmaTileRows;
+  if (persistent) plan_persistent(tiles, hkv, tile_rows, P);
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
   for (const Tile &t : tiles) {
+    if (persistent && !t.decode) continue;
     const int64_t chunk = t.decode ? dchunk : pchunk;
     const int32_t nsplit = (int32_t)std::min<int64_t>(cdiv64(t.keys, chunk), INT32_MAX);
     cut(t.keys, nsplit, ranges);
@@ -197,6 +291,8 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + P.decode.size() * sizeof(Item));
   P.off_merges = off;
   off = align256(off + P.merges.size() * sizeof(Merge));
+  P.off_wg = off;
+  off = align256(off + P.wg_first.size() * sizeof(int32_t));
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -458,6 +554,8 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   if (!P.prefill.empty()) memcpy(host.data() + P.off_prefill, P.prefill.data(), P.prefill.size() * sizeof(Item));
   if (!P.decode.empty()) memcpy(host.data() + P.off_decode, P.decode.data(), P.decode.size() * sizeof(Item));
   if (!P.merges.empty()) memcpy(host.data() + P.off_merges, P.merges.data(), P.merges.size() * sizeof(Merge));
+  if (!P.wg_first.empty())
+    memcpy(host.data() + P.off_wg, P.wg_first.data(), P.wg_first.size() * sizeof(int32_t));
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   st = stage_copy(host.data(), P.plan_bytes, ws, s);
@@ -487,12 +585,14 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
     a.items = (const Item *)(ws + P.off_prefill);
     a.part_o = (float *)(ws + P.off_po_pre);
     a.part_lse = (float *)(ws + P.off_pl_pre);
-    const int n = (int)P.prefill.size();
+    a.wg_first = P.wg_first.empty() ? nullptr : (const int32_t *)(ws + P.off_wg);
+    const int n = P.wg_first.empty() ? (int)P.prefill.size() : (int)P.wg_first.size() - 1;
     e = timed(1, s, [&] { return launch_prefill(a, n, d, bs, fp8, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
   if (!P.decode.empty()) {
     a.items = (const Item *)(ws + P.off_decode);
+    a.wg_first = nullptr;
     a.part_o = (float *)(ws + P.off_po_dec);
     a.part_lse = (float *)(ws + P.off_pl_dec);
     const int n = (int)P.decode.size();
@@ -564,6 +664,26 @@ pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens, int3
   if (!P.prefill.empty()) memcpy(items_out, P.prefill.data(), P.prefill.size() * sizeof(Item));
   if (!P.decode.empty())
     memcpy(items_out + 8 * P.prefill.size(), P.decode.data(), P.decode.size() * sizeof(Item));
+  return PA_OK;
+}
+
+pa_status pa_debug_plan_groups(const int32_t *hist_lens, const int32_t *incr_lens,
+                               int32_t num_seqs, int32_t num_q_heads, const pa_kv_cache *cache,
+                               int32_t *first_out, int32_t cap, int32_t *num_groups_out) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  int64_t total_q = 0;
+  st = check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, 0, false, &total_q);
+  if (st) return st;
+  if (!num_groups_out || (cap > 0 && !first_out)) return fail(PA_ERR_NULL_ARG, "output is NULL");
+  Plan P;
+  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
+            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
+  const int32_t n = P.wg_first.empty() ? 0 : (int32_t)P.wg_first.size() - 1;
+  *num_groups_out = n;
+  if (n == 0) return PA_OK;
+  if (n + 1 > cap) return fail(PA_ERR_WORKSPACE_TOO_SMALL, "cap %d, need %d", cap, n + 1);
+  memcpy(first_out, P.wg_first.data(), (size_t)(n + 1) * sizeof(int32_t));
   return PA_OK;
 }
 

@@ -384,22 +384,21 @@ __device__ __forceinline__ void wg_barrier() {
 #ifndef PA_LOOKAHEAD
 #define PA_LOOKAHEAD 12
 #endif
+constexpr int kPpTileBytes = kKeyTile * 128 * 2;  // one 64-key K (or V) tile, 16 KB
+constexpr int kPpStages = 4;                        // K+V stages in the LDS ring
+
+// One work item of the 256-row kernel; the caller separates consecutive
+// items by a work-group barrier.
 template <int BS>
-__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
+__device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
   constexpr int D = 128;
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  constexpr int TILEB = kKeyTile * D * 2;  // 16 KB
-  constexpr int STAGEB = 2 * TILEB;        // K + V of one tile
-  constexpr int NST = 4;
-  constexpr int MAXB = kMaxDmaItemKeys / BS + 2;
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NST * STAGEB];
-  __shared__ int bt_lds[MAXB];
-  lds_u8 *smem = (lds_u8 *)smem_raw;
+  constexpr int TILEB = kPpTileBytes;
+  constexpr int STAGEB = 2 * TILEB;  // K + V of one tile
+  constexpr int NST = kPpStages;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  const Item it = a.items[blockIdx.x];
   const float scale_log2 = a.scale_log2;
   const int kv_hi = it.kv_hi, kvh = it.kvh, hkv = a.c.hkv;
   const int tid = threadIdx.x;
@@ -436,26 +435,35 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
     for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
   }
 
-  // per-lane LDS offsets (XOR swizzle folded): K A-operand reads and V transposing reads
-  int kofs[NC], vofs[ND];
+  // LDS tile layout: row r (a key) is 256 bytes; its logical 16-byte chunk q
+  // (elements 8q .. 8q+7) sits at chunk position q ^ swz(r).  The swizzle
+  // spreads the 16 rows a K read touches at one chunk (lanes 0-15, or
+  // 32-47) over 16 distinct positions, and keeps the transposing V reads,
+  // whose 16-lane groups span 4 rows x 2 chunks x 2 halves, conflict-free.
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  // per-lane LDS offsets: K A-operand reads (row col, chunk 2c + hh) and V
+  // transposing reads (rows r0 and 8 + r0 of each 16-key step, chunk 4db + c0)
+  int kofs[NC], vofs0[ND], vofs1[ND];
   {
-    const int y = col & 7;
 #pragma unroll
-    for (int c = 0; c < NC; c++) kofs[c] = col * 256 + hh * 16 + ((c ^ y) << 5);
+    for (int c = 0; c < NC; c++) kofs[c] = col * 256 + (((2 * c + hh) ^ swz(col)) << 4);
     const int g16 = lane >> 4, j16 = lane & 15;
-    const int r0 = 4 * hh + (j16 >> 2);  // row within a 16-key step
-    const int y2 = r0 & 7;
+    const int r0 = 4 * hh + (j16 >> 2);
     const int c0 = (g16 & 1) * 2 + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int db = 0; db < ND; db++)
-      vofs[db] = r0 * 256 + ((db ^ (y2 >> 1)) << 6) + ((c0 ^ ((2 * y2) & 3)) << 4) + (j16 & 1) * 8;
+    for (int db = 0; db < ND; db++) {
+      vofs0[db] = r0 * 256 + (((4 * db + c0) ^ swz(r0)) << 4) + (j16 & 1) * 8;
+      vofs1[db] = r0 * 256 + (((4 * db + c0) ^ swz(8 + r0)) << 4) + (j16 & 1) * 8;
+    }
   }
-  // this wave's DMA lanes: instructions jj = 0, 1 cover tile rows 8*wave + 4*jj .. +3
+  // this wave's DMA lanes: instruction jj covers tile rows 8*wave + 4*jj .. +3;
+  // lane (lr, pc) fills chunk position pc of row 4*jj + lr from the global
+  // chunk that belongs there
   int voff[2];
 #pragma unroll
   for (int jj = 0; jj < 2; jj++) {
     const int lr = lane >> 4, pc = lane & 15;
-    voff[jj] = lr * 256 + ((pc ^ (((4 * jj + lr) & 7) << 1)) << 4);
+    voff[jj] = lr * 256 + ((pc ^ swz(8 * wave + 4 * jj + lr)) << 4);
   }
   const unsigned char *kc = (const unsigned char *)a.c.k;
   const unsigned char *vc = (const unsigned char *)a.c.v;
@@ -514,8 +522,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ks++)
 #pragma unroll
       for (int db = 0; db < ND; db++) {
-        const bf16x4 h0 = lds_read_tr(Vb + ks * 4096 + vofs[db]);
-        const bf16x4 h1 = lds_read_tr(Vb + ks * 4096 + 2048 + vofs[db]);
+        const bf16x4 h0 = lds_read_tr(Vb + ks * 4096 + vofs0[db]);
+        const bf16x4 h1 = lds_read_tr(Vb + ks * 4096 + 2048 + vofs1[db]);
         vf[ks * ND + db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
@@ -693,6 +701,20 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
         *(f32x4 *)(prow + db * 32 + 8 * i + 4 * hh) = v;
       }
     if (hh == 0) a.part_lse[(int64_t)it.part * kDmaTileRows + row] = lse2;
+  }
+}
+
+// A work-group runs its items one after another: one item per work-group,
+// or with a persistent plan the balanced list wg_first assigns it.
+template <int BS>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kPpStages * 2 * kPpTileBytes];
+  __shared__ int bt_lds[kMaxDmaItemKeys / BS + 2];
+  const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
+  const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
+  for (int i = first; i < last; i++) {
+    if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
+    pp_item<BS>(a, a.items[i], (lds_u8 *)smem_raw, bt_lds);
   }
 }
 

@@ -59,6 +59,7 @@ struct AttnArgs {
   void *out;              // bf16 [total_q][hq][d]
   float *lse_out;         // optional fp32 [total_q][hq] (natural log)
   const Item *items;
+  const int32_t *wg_first;  // persistent launch: work-group w runs items [wg_first[w], wg_first[w+1])
   float *part_o;          // [slots][rows_per_slot][d] fp32, normalised partial outputs
   float *part_lse;        // [slots][rows_per_slot], log2 units
 };

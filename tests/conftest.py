@@ -30,11 +30,21 @@ def _lib_stale():
     return max(os.path.getmtime(s) for s in srcs) > os.path.getmtime(lib)
 
 
+def load_builder():
+    """The package's build script, loaded without importing the package
+    (whose import loads the library)."""
+    import importlib.util
+    path = os.path.join(ROOT, "paged_kv_cache_gqa_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("paged_kv_cache_gqa_amd_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 @pytest.fixture(scope="session")
 def palib():
     """The product library's Python binding (built first if missing or stale)."""
     if _lib_stale():
-        from paged_kv_cache_gqa_amd import build as B
-        B.build()
+        load_builder().build()
     import paged_kv_cache_gqa_amd as pa
     return pa

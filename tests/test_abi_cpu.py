@@ -168,6 +168,16 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
     return items, counts
 
 
+def test_planner_balances_persistent_prefill(palib):
+    check_balance(palib, [0, 45_700, 3], [45_7, 2_700, 1], 32, 8)
+    check_balance(palib, [131_072], [2_700], 32, 8)
+    check_balance(palib, [100, 7, 999], [300, 200, 170], 16, 1)
+    check_balance(palib, [1000, 70], [129, 300], 8, 8)
+    check_balance(palib, [256], [32], 4, 1, d=64)                # register-staged kernel: none
+    first = check_balance(palib, [0], [64], 4, 1)                # tiny: few work-groups
+    assert 1 <= len(first) - 1 < 256
+
+
 def test_planner_covers_causal_pattern_exactly(palib):
     check_cover(palib, [256], [32], 4, 1, d=64)                  # tiny workload
     check_cover(palib, [0, 45_700, 3], [45_7, 2_700, 1], 32, 8)  # mixed classes
@@ -176,8 +186,39 @@ def test_planner_covers_causal_pattern_exactly(palib):
     check_cover(palib, [1000, 70], [129, 300], 8, 8)             # group 1
 
 
+def check_balance(pa, hist, incr, hq, hkv, d=128, bs=16):
+    """Persistent prefill plan: each work-group's items are pieces of the
+    flattened (KV head, tile, 64-key step) work, and every work-group gets
+    the same number of steps to within one."""
+    c = cache(pa, num_kv_heads=hkv, head_dim=d, block_size=bs)
+    items, counts = pa.pa_debug_plan(hist, incr, hq, c)
+    first = pa.pa_debug_plan_groups(hist, incr, hq, c)
+    if d != 128:
+        assert len(first) == 0
+        return first
+    G = hq // hkv
+    pre = items[:counts[0]]
+    assert len(first) >= 2 and first[0] == 0 and first[-1] == counts[0]
+    assert np.all(np.diff(first) >= 1) and len(first) - 1 <= 256
+    steps = []
+    for w in range(len(first) - 1):
+        tot = 0
+        for it in pre[first[w]:first[w + 1]]:
+            lo, hi = int(it[5]), int(it[6])
+            assert int(it[4]) * G > 16
+            tot += (hi + 63) // 64 - lo // 64
+        steps.append(tot)
+    assert max(steps) - min(steps) <= 1, (min(steps), max(steps))
+    return first
+
+
 def test_planner_splits_long_work_and_merges(palib):
     items, counts = check_cover(palib, [45_700], [2_700], 32, 8)
-    assert counts[0] > 680 and counts[2] > 0        # 85 tiles x 8 heads, split
+    assert counts[0] >= 43 * 8 and counts[2] > 0    # 43 tiles x 8 heads, split
+    first = check_balance(palib, [45_700], [2_700], 32, 8)
+    assert len(first) - 1 == 256
+    # (tile, head) units are split into a few key chunks plus the pieces cut
+    # at work-group boundaries
+    assert counts[3] <= 4 * 43 * 8 + 256
     items, counts = check_cover(palib, [1_048_575], [1], 32, 8, bs=64)
     assert counts[1] >= 256 and counts[2] == 8      # one long decode, split per head

@@ -14,7 +14,9 @@ import subprocess
 
 import pytest
 
-from paged_kv_cache_gqa_amd import build as pabuild
+from conftest import load_builder
+
+pabuild = load_builder()
 
 pytestmark = pytest.mark.skipif(not os.path.exists(pabuild.HIPCC), reason="hipcc not installed")
 
