@@ -967,61 +967,104 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 // =============================================================================
 // LSE merge of split items ([Agentic] §4.3.3): for each row,
 // out = sum_i w_i o_i / sum_i w_i with w_i = 2^(lse_i - M), M = max_i lse_i,
-// lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing.
-// The weights of a task are computed once into LDS; each thread then reduces
-// four consecutive d of one row over the parts with 16-byte loads.
+// lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing
+// (their stored o is 0).  A work-group takes kMergeRows rows of one task:
+// one wave per row computes the weights (lanes split the parts) into LDS,
+// then each thread reduces four consecutive d of one row over the parts with
+// 16-byte loads that do not wait on each other.
+constexpr int kMergeRows = 64;
 constexpr int kMergeWeights = 8192;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const Merge mt = a.merges[blockIdx.x];
+  const int rows = mt.nq << a.lg;
+  const int rb = blockIdx.y * kMergeRows;
+  if (rb >= rows) return;
+  const int nr = min(kMergeRows, rows - rb);
   const float *po = mt.is_decode ? a.part_o_decode : a.part_o_prefill;
   const float *pl = mt.is_decode ? a.part_lse_decode : a.part_lse_prefill;
-  const int rows = mt.nq << a.lg;
   const int rpp = mt.rows_per_part;
   const int np = mt.nparts;
-  const bool cached = rows * np <= kMergeWeights;
+  const bool cached = nr * np <= kMergeWeights;
   __shared__ float sm_w[kMergeWeights];
-  __shared__ float sm_max[kPrefillRowsMax], sm_inv[kPrefillRowsMax];
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+  __shared__ float sm_max[kMergeRows], sm_inv[kMergeRows];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto row_out = [&](int r) {
+    const int rr = rb + r;
+    return (int64_t)(mt.row0 + (rr >> a.lg)) * a.hq + mt.kvh * a.group + (rr & (a.group - 1));
+  };
+  for (int r = wave; r < nr; r += 4) {
+    const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
     float M = -INFINITY;
-    for (int i = 0; i < np; i++) M = fmaxf(M, pl[(int64_t)(mt.part0 + i) * rpp + r]);
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, lrow[(int64_t)i * rpp]);
+    M = wave_max(M);
     float S = 0.f;
-    for (int i = 0; i < np; i++) {
-      const float li = pl[(int64_t)(mt.part0 + i) * rpp + r];
+    for (int i = lane; i < np; i += 64) {
+      const float li = lrow[(int64_t)i * rpp];
       const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
       S += w;
       if (cached) sm_w[r * np + i] = w;
     }
-    sm_max[r] = M;
-    sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
-    if (a.lse_out) {
-      const int64_t orow = (int64_t)(mt.row0 + (r >> a.lg)) * a.hq + mt.kvh * a.group + (r & (a.group - 1));
-      a.lse_out[orow] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+    S = wave_sum(S);
+    if (lane == 0) {
+      sm_max[r] = M;
+      sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
+      if (a.lse_out) a.lse_out[row_out(r)] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
   const int d = a.d, d4 = d / 4;
-  for (int idx = threadIdx.x; idx < rows * d4; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < nr * d4; idx += blockDim.x) {
     const int r = idx / d4, e = (idx % d4) * 4;
     const float M = sm_max[r];
+    const float *orow = po + ((int64_t)mt.part0 * rpp + rb + r) * d + e;
+    const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < np; i++) {
-      const int64_t slot = (int64_t)(mt.part0 + i) * rpp + r;
+    int i = 0;
+    for (; i + 4 <= np; i += 4) {
+      f32x4 v[4];
+      float w[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) v[k] = *(const f32x4 *)(orow + (int64_t)(i + k) * rpp * d);
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        if (cached) {
+          w[k] = sm_w[r * np + i + k];
+        } else {
+          const float li = lrow[(int64_t)(i + k) * rpp];
+          w[k] = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) O += w[k] * v[k];
+    }
+    for (; i < np; i++) {
+      const f32x4 v = *(const f32x4 *)(orow + (int64_t)i * rpp * d);
       float w;
       if (cached) {
         w = sm_w[r * np + i];
       } else {
-        const float li = pl[slot];
+        const float li = lrow[(int64_t)i * rpp];
         w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
       }
-      if (w != 0.f) O += w * *(const f32x4 *)(po + slot * d + e);
+      O += w * v;
     }
     const float inv = sm_inv[r];
-    const int64_t orow = (int64_t)(mt.row0 + (r >> a.lg)) * a.hq + mt.kvh * a.group + (r & (a.group - 1));
     bf16x4 v;
 #pragma unroll
     for (int k = 0; k < 4; k++) v[k] = (__bf16)(O[k] * inv);
-    *(bf16x4 *)((__bf16 *)a.out + orow * d + e) = v;
+    *(bf16x4 *)((__bf16 *)a.out + row_out(r) * d + e) = v;
   }
 }
 
@@ -1066,7 +1109,7 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, bool fp8, hipS
 }
 hipError_t launch_merge(const MergeArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(n, kPrefillRowsMax / kMergeRows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
