@@ -148,7 +148,9 @@ def run_cpu_baseline(spec, budget_s):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILE_CMDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o kt -- "
-              "python3 REPO/bench.py --steps 10 --warmup 2 --no-cpu",
+              "python3 REPO/bench.py --steps 10 --warmup 2 --no-cpu --no-128k",
+    "ktrace_incremental_128k": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace128 "
+                               "-o kt -- python3 REPO/bench.py --only incremental_128k --steps 10 --warmup 2",
     "pmc": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/{w}_{counter} -o p -- "
            "python3 REPO/bench.py --only {w} --steps 2 --warmup 1",
     "copy": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/copy_{counter} -o p -- "
@@ -156,9 +158,10 @@ PROFILE_CMDS = {
 }
 KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_device.h",
-                  "paged_kv_cache_gqa_amd/csrc/pa_internal.h"]
+                  "paged_kv_cache_gqa_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-PREFILL_KERNEL = "void pa::prefill_kernel<128, 16, false>(pa::AttnArgs)"
+PREFILL_KERNEL = "void pa::prefill_pp_kernel<16>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_kernel<128, 16, false>(pa::AttnArgs)"
 
 
@@ -183,8 +186,10 @@ def _counter_means(path):
 def summarize_profiles(out):
     import csv
     import glob
-    stats = list(csv.DictReader(open(glob.glob(os.path.join(out, "ktrace", "*kernel_stats.csv"))[0])))
-    by_name = {r["Name"]: r for r in stats}
+    def load_stats(sub):
+        return list(csv.DictReader(open(glob.glob(os.path.join(out, sub, "*kernel_stats.csv"))[0])))
+
+    all_stats = {"ktrace": load_stats("ktrace"), "ktrace_incremental_128k": load_stats("ktrace128")}
     copy_f = _counter_means(os.path.join(out, "pmc", "copy_FETCH_SIZE"))["__amd_rocclr_copyBuffer"][0]
     copy_w = _counter_means(os.path.join(out, "pmc", "copy_WRITE_SIZE"))["__amd_rocclr_copyBuffer"][0]
     gib = float(1 << 30)
@@ -192,18 +197,21 @@ def summarize_profiles(out):
     src = kernel_source_hash()
     traffic = {}
     for w, kname, unit_desc in (("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k"),
+                                ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k"),
                                 ("decode", DECODE_KERNEL, "decode_batch_64x142k")):
         fetch, nf = _counter_means(os.path.join(out, "pmc", f"{w}_FETCH_SIZE"))[kname]
         write, nw = _counter_means(os.path.join(out, "pmc", f"{w}_WRITE_SIZE"))[kname]
         tb = fetch * 1024 * f_scale + write * 1024 * w_scale
         traffic[w] = tb
-        st = by_name[kname]
+        tkey = "ktrace_incremental_128k" if w == "incremental_128k" else "ktrace"
+        stats = all_stats[tkey]
+        st = {r["Name"]: r for r in stats}[kname]
         kshort = kname.split("pa::")[1].split("(")[0].replace("<", "_").replace(">", "").replace(", ", "_")
         fn = os.path.join(ROOT, "profiles", f"{kshort}__{unit_desc}.txt")
         with open(fn, "w") as fh:
             fh.write(f"Kernel: {kname}\nWorkload: {unit_desc}\n\n")
             fh.write("Commands (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root):\n")
-            fh.write("  " + PROFILE_CMDS["ktrace"] + "\n")
+            fh.write("  " + PROFILE_CMDS[tkey] + "\n")
             for c in ("FETCH_SIZE", "WRITE_SIZE"):
                 fh.write("  " + PROFILE_CMDS["pmc"].format(counter=c, w=w) + "\n")
                 fh.write("  " + PROFILE_CMDS["copy"].format(counter=c) + "\n")
@@ -214,7 +222,14 @@ def summarize_profiles(out):
                 if r["Name"].startswith(("void pa::", "pa::")):
                     fh.write(f"  {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                              f"{r['MinNs']} | {r['MaxNs']}\n")
-            fh.write(f"\nThis kernel: average {float(st['AverageNs']) / 1e6:.4f} ms over {st['Calls']} calls\n\n")
+            fh.write(f"\nThis kernel: average {float(st['AverageNs']) / 1e6:.4f} ms over {st['Calls']} calls\n")
+            sub = "ktrace128" if w == "incremental_128k" else "ktrace"
+            durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    for r in csv.DictReader(open(glob.glob(os.path.join(out, sub, "*kernel_trace.csv"))[0]))
+                    if r["Kernel_Name"] == kname]
+            timed = durs[-10:]  # the 10 timed steps; the first calls are warm-up
+            fh.write(f"  timed steps only (last {len(timed)} dispatches, from kernel_trace.csv): "
+                     f"average {sum(timed) / len(timed) / 1e6:.4f} ms\n\n")
             fh.write("HBM counters per dispatch (mean over dispatches of this kernel):\n")
             fh.write(f"  FETCH_SIZE {fetch:.1f} KiB ({nf} dispatches), WRITE_SIZE {write:.1f} KiB ({nw})\n")
             fh.write(f"  copy calibration (1 GiB device copy): FETCH_SIZE {copy_f:.1f} KiB, WRITE_SIZE {copy_w:.1f} KiB\n")
@@ -225,6 +240,7 @@ def summarize_profiles(out):
         fh.write("# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE, scaled by a 1 GiB copy\n")
         fh.write(f"source_hash={src}\n")
         fh.write(f"prefill_incremental_bytes={traffic['incremental']:.0f}\n")
+        fh.write(f"prefill_incremental_128k_bytes={traffic['incremental_128k']:.0f}\n")
         fh.write(f"decode_batch_bytes={traffic['decode']:.0f}\n")
     print(f"wrote profiles for source {src}")
 
@@ -247,8 +263,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--with-128k", action="store_true",
-                    help="also time the 128K-history incremental prefill (same kernel as the headline)")
+    ap.add_argument("--no-128k", action="store_true",
+                    help="skip the 128K-history incremental prefill (same kernel as the headline)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/*.txt from rocprofv3 outputs under DIR and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -321,7 +337,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill_incremental_bytes"),
-                     "kernel": "prefill_kernel<128,16,false>",
+                     "kernel": "prefill_pp_kernel<16>",
                      "kernel_ms": round(k_ms, 4)},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
     }
@@ -351,7 +367,7 @@ def main():
         }
         del r
         torch.cuda.empty_cache()
-    if args.with_128k:
+    if not args.no_extra and not args.no_128k:
         # incremental prefill at 128K history
         pspec = W.incremental(131_072, 2_700, "incremental_128k")
         r = Runner(pa, torch, pspec, dev)
@@ -364,7 +380,9 @@ def main():
             "kernels_ms": {k: round(v[0], 4) for k, v in pk.items()},
             "roofline": {"bound": "mfma", "achieved": round(pfl / (pk_ms * 1e-3) / 1e12, 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                         "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_incremental_128k_bytes"),
+                         "kernel": "prefill_pp_kernel<16>", "kernel_ms": round(pk_ms, 4)},
         }
         del r
         torch.cuda.empty_cache()
