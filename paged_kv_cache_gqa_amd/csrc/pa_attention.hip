@@ -412,6 +412,8 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
   const int pos = it.pos0 + tok;
   const int qh = kvh * a.group + g;
 
+  // Q is held pre-multiplied by scale * log2(e) (rounded to bf16), so the
+  // score MFMAs produce base-2 exponents directly.
   bf16x8 qf[NC];
   {
     const unsigned char *qrow =
@@ -419,7 +421,9 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
 #pragma unroll
     for (int c = 0; c < NC; c++) {
       uint4 v = active ? gload16(qrow + (c * 16 + hh * 8) * 2) : make_uint4(0, 0, 0, 0);
-      qf[c] = as_bf16x8(v);
+      const bf16x8 q = as_bf16x8(v);
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[c][e] = (__bf16)((float)q[e] * scale_log2);
     }
   }
 
@@ -502,7 +506,10 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
     return (const lds_u8 *)(smem + ((t - t_begin) & (NST - 1)) * STAGEB);
   };
 
-  float m = kNegBig, l = 0.f;
+  // m: per-row reference exponent (base 2).  Score MFMAs start from -m, so
+  // they yield s - m; m moves up only when a tile's maximum exceeds it by
+  // kRescaleSlack, and while the row has no weight yet it follows the max.
+  float m = 0.f, l = 0.f;
   f32x16 o[ND];
 #pragma unroll
   for (int i = 0; i < ND; i++) o[i] = f32x16{};
@@ -536,8 +543,9 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
       for (int c = 0; c < NC; c++)
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) kf[2 * c + kb] = as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c]));
+      const f32x16 neg_m = f32x16{} - m;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[kb], qf[0], f32x16{});
+      for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[kb], qf[0], neg_m);
 #pragma unroll
       for (int c = 1; c < NC; c++)
 #pragma unroll
@@ -569,7 +577,7 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
   auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[0])), qf[0], f32x16{});
+      S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[0])), qf[0], f32x16{} - m);
 #pragma unroll
       for (int c = 1; c < NC; c++)
         S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c])), qf[c], S[kb]);
@@ -586,28 +594,30 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
           S[kb][e] = key <= lim ? S[kb][e] : -INFINITY;
         }
     }
+    // S holds s - m (base 2); mx is the tile's maximum of it
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) mx = fmaxf(mx, S[kb][e]);
     mx = xor32_max(mx);
-    const float mxs = mx * scale_log2;
-    if (__any(mxs > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mxs);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
+    const bool move = mx > kRescaleSlack || (l == 0.f && mx > -INFINITY);
+    if (__any(move)) {
+      const float shift = move ? mx : 0.f;
+      const float alpha = fast_exp2(-shift);
+      m += shift;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < ND; db++) o[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) S[kb] -= shift;
     }
-    const float nm = -m;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
-        const float p = fast_exp2(__builtin_fmaf(S[kb][e], scale_log2, nm));
+        const float p = fast_exp2(S[kb][e]);
         S[kb][e] = p;
         psum += p;
       }
@@ -690,7 +700,7 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
       }
     if (a.lse_out && hh == 0) a.lse_out[(int64_t)(it.row0 + tok) * a.hq + qh] = lse2 * kLn2;
   } else {
-    float *prow = a.part_o + ((int64_t)it.part * kDmaTileRows + row) * D;
+    float *prow = a.part_o + ((int64_t)it.part * kPpTileRows + row) * D;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -700,7 +710,7 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
         for (int r = 0; r < 4; r++) v[r] = o[db][4 * i + r] * inv;
         *(f32x4 *)(prow + db * 32 + 8 * i + 4 * hh) = v;
       }
-    if (hh == 0) a.part_lse[(int64_t)it.part * kDmaTileRows + row] = lse2;
+    if (hh == 0) a.part_lse[(int64_t)it.part * kPpTileRows + row] = lse2;
   }
 }
 
@@ -715,6 +725,350 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
   for (int i = first; i < last; i++) {
     if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
     pp_item<BS>(a, a.items[i], (lds_u8 *)smem_raw, bt_lds);
+  }
+}
+
+// =============================================================================
+// 384-row prefill for bf16 KV, head_dim 128: the same ping-pong of two
+// groups of four waves and the same LDS-DMA ring as the 256-row kernel, with
+// 48 query rows per wave (three 16-row blocks) on v_mfma_f32_16x16x32_bf16
+// and 32-key steps.  Each K/V byte brought into the CU now serves 384 rows
+// instead of 256, and each LDS read 48 rows instead of 32.
+//   Sᵀ = K Qᵀ per (16-key block kb, 16-row block rb): A = K (lane: key c16,
+//   d 32c + 8g..+7, one 16-byte LDS read), B = Qᵀ (lane: row c16, same d, in
+//   registers), D: lane holds row c16, keys 16kb + 4g + r.
+//   Oᵀ += Vᵀ Pᵀ per (16-d block db, rb) over the step's 32 keys: B = Pᵀ is
+//   (S[0][rb][0..3], S[1][rb][0..3]) converted in place, which orders the
+//   contraction index as keys 4g..4g+3, 16+4g..16+4g+3 of lane group g; A =
+//   Vᵀ is read in that order by two transposing LDS reads (lane: d = 16db +
+//   c16).  D: lane holds row c16, d = 16db + 4g + r.
+// A row's 32 scores of a step sit in the four lanes c16 + 16g, reduced with
+// the permlane swaps.
+constexpr int kW48Step = 32;                        // keys per step
+constexpr int kW48TileBytes = kW48Step * 128 * 2;  // K (or V) of one step, 8 KB
+#ifndef PA_W48_STAGES
+#define PA_W48_STAGES 8
+#endif
+constexpr int kW48Stages = PA_W48_STAGES;
+
+template <int BS>
+__device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
+  constexpr int D = 128;
+  constexpr int NCQ = D / 32;  // k-steps of the score product
+  constexpr int NDB = D / 16;  // d-blocks of the value product
+  constexpr int RB = 3;        // 16-row blocks per wave
+  constexpr int TILEB = kW48TileBytes;
+  constexpr int STAGEB = 2 * TILEB;
+  constexpr int NST = kW48Stages;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const float scale_log2 = a.scale_log2;
+  const int kv_hi = it.kv_hi, kvh = it.kvh, hkv = a.c.hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int c16 = lane & 15, g = lane >> 4;
+
+  // Q is held pre-multiplied by scale * log2(e) (rounded to bf16), so the
+  // score MFMAs produce base-2 exponents directly.
+  bf16x8 qf[RB][NCQ];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    const int row = wave * 48 + rb * 16 + c16;
+    const int tok = row >> a.lg, gq = row & (a.group - 1);
+    const bool act = tok < it.nq;
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < NCQ; c++) {
+      uint4 v = act ? gload16(qrow + (32 * c + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
+      const bf16x8 q = as_bf16x8(v);
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[rb][c][e] = (__bf16)((float)q[e] * scale_log2);
+    }
+  }
+
+  const int t_begin = it.kv_lo / kW48Step;
+  const int t_end = (kv_hi + kW48Step - 1) / kW48Step;
+  const int t_full = max(t_begin, min(t_end, min(it.pos0 + 1, kv_hi) / kW48Step));
+  const int blk0 = it.kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+
+  {  // stage the item's block ids
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
+  }
+
+  // LDS tile: key row r is 256 bytes, logical 16-byte chunk q at position
+  // q ^ swz(r) (see the 256-row kernel; swz depends on r & 15 only, so rows r
+  // and r + 16 share it and the second key block is an immediate offset).
+  // The chunk index's high bits come from c (K: chunk 4c + g) and db (V:
+  // chunk 2db + h), so each read's offset is one per-lane base XOR c << 6
+  // (K) or db << 5 (V).
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  const int kbase = c16 * 256 + ((g ^ swz(c16)) << 4);
+  const int vr = 4 * g + (c16 >> 2);
+  const int vbase = vr * 256 + ((((c16 & 3) >> 1) ^ swz(vr)) << 4) + (c16 & 1) * 8;
+  auto kofs = [&](int c) { return kbase ^ (c << 6); };
+  auto vofs = [&](int db) { return vbase ^ (db << 5); };
+  // this wave's DMA lanes: tile rows 4*wave .. 4*wave+3, lane (lr, pc) fills
+  // chunk position pc of row 4*wave + lr
+  const int voff = (lane >> 4) * 256 + (((lane & 15) ^ swz(4 * wave + (lane >> 4))) << 4);
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+
+  __syncthreads();  // block ids visible
+
+  auto block_of = [&](int t) __attribute__((always_inline)) {
+    const int tt = min(t, t_end - 1);
+    return bt_lds[min((tt * kW48Step + 4 * wave) / BS, last_blk) - blk0];
+  };
+  int blk_next = block_of(t_begin);
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int tt = min(t, t_end - 1);
+    const int64_t blk = __builtin_amdgcn_readfirstlane(blk_next);
+    blk_next = block_of(t + 1);
+    const uint32_t st = smem_addr + ((t - t_begin) % NST) * STAGEB;
+    const int rpos = tt * kW48Step + 4 * wave;
+    const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
+    const int nrec = __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos, 0), 4) * (D * 2) : 0);
+    const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+    const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
+                        __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+    const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
+                        __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+    dma_load16(rk, voff, st + wave * 1024);
+    dma_load16(rv, voff, st + TILEB + wave * 1024);
+  };
+  auto stage = [&](int t) __attribute__((always_inline)) {
+    return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
+  };
+
+  // m[rb]: the row's reference exponent (base 2).  The score MFMAs start
+  // from -m, so they yield s - m and a probability is one exp2; m moves up
+  // only when a step's maximum exceeds it by kRescaleSlack, and while the
+  // row has no weight yet it follows the maximum.
+  // o[NDB][rb] is the row sum l: the value product runs one more d-block
+  // whose A operand is all ones, so l comes from the matrix cores (over the
+  // same bf16 probabilities the output uses) and is rescaled with o.
+  float m[RB];
+  f32x4 o[NDB + 1][RB];
+  f32x4 S[2][RB];
+  bf16x8 pb[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    m[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
+  }
+
+  // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
+  // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
+  auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
+    constexpr bool with_qk = decltype(with_qk_tag)::value;
+    bf16x8 vf[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; db++) {
+      const bf16x4 h0 = lds_read_tr(Vb + vofs(db));
+      const bf16x4 h1 = lds_read_tr(Vb + 4096 + vofs(db));
+      vf[db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; db++)
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) o[db][rb] = mfma16x16x32(vf[db], pb[rb], o[db][rb]);
+    {
+      bf16x8 ones;
+#pragma unroll
+      for (int e = 0; e < 8; e++) ones[e] = (__bf16)1.0f;
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
+    }
+    if constexpr (with_qk) {
+      bf16x8 kf[NCQ][2];
+#pragma unroll
+      for (int c = 0; c < NCQ; c++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) kf[c][kb] = as_bf16x8(lds_load16(Kb + kb * 4096 + kofs(c)));
+#pragma unroll
+      for (int c = 0; c < NCQ; c++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int rb = 0; rb < RB; rb++)
+            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} - m[rb] : S[kb][rb]);
+      // order: the first three V fragments' reads; then per three MFMAs
+      // (one fragment's worth) the reads of the fragment three ahead -- V
+      // reads during the value product's first 15 MFMAs, K reads during its
+      // last 9 and the score product's first 6 -- so about three fragments
+      // are in flight at any time
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 21, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 5; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    }
+  };
+  auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NCQ; c++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) {
+        const bf16x8 kf = as_bf16x8(lds_load16(Kb + kb * 4096 + kofs(c)));
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? f32x4{} - m[rb] : S[kb][rb]);
+      }
+  };
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    if (t >= t_full) {
+      const int key0 = t * kW48Step + 4 * g;
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) {
+        const int lim = min(it.pos0 + ((wave * 48 + rb * 16 + c16) >> a.lg), kv_hi - 1);
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) S[kb][rb][r] = key0 + kb * 16 + r <= lim ? S[kb][rb][r] : -INFINITY;
+      }
+    }
+    // S holds s - m.  A row's maximum is needed only when m has to move:
+    // test each lane's own maximum first, reduce across the row's four lanes
+    // only if some lane exceeds the slack (rare once m has settled).
+    float lmx[RB];
+    bool need = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
+      lmx[rb] = mx;
+      need |= mx > kRescaleSlack || (o[NDB][rb][0] == 0.f && mx > -INFINITY);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) {
+        const float mx = xor32_max(xor16_max(lmx[rb]));
+        const bool mv = mx > kRescaleSlack || (o[NDB][rb][0] == 0.f && mx > -INFINITY);
+        const float shift = mv ? mx : 0.f;
+        const float alpha = fast_exp2(-shift);
+        m[rb] += shift;
+#pragma unroll
+        for (int db = 0; db <= NDB; db++) o[db][rb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) S[kb][rb] -= shift;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        pb[rb][r] = (__bf16)fast_exp2(S[0][rb][r]);
+        pb[rb][4 + r] = (__bf16)fast_exp2(S[1][rb][r]);
+      }
+    }
+  };
+
+  // prologue: NST-1 steps requested; S(t0) for both groups, P(t0) for group 0
+#pragma unroll
+  for (int k = 0; k < NST - 1; k++) issue(t_begin + k);
+  PA_WAIT_VMCNT(2 * (NST - 2));
+  wg_barrier();
+  qk_only(stage(t_begin));
+  // step t opens once this wave's share of step t+1 has landed (steps t+2 ..
+  // t+NST-2 may be in flight); step t+NST-1 is requested into the stage step
+  // t-1 left, during the wave's softmax phase.
+  if (grp == 0) {
+    wg_barrier();
+    softmax(t_begin);
+    int t = t_begin;
+    for (; t + 1 < t_end; t++) {
+      PA_WAIT_VMCNT(2 * (NST - 3));
+      wg_barrier();
+      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
+      wg_barrier();
+      issue(t + NST - 1);                                      // phase B: loads, vector ALUs
+      softmax(t + 1);
+    }
+    PA_WAIT_VMCNT(2 * (NST - 3));
+    wg_barrier();
+    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
+    wg_barrier();
+    issue(t + NST - 1);
+  } else {
+    wg_barrier();
+    int t = t_begin;
+    for (; t + 1 < t_end; t++) {
+      PA_WAIT_VMCNT(2 * (NST - 3));
+      wg_barrier();
+      issue(t + NST - 1);
+      softmax(t);                                              // phase A: vector ALUs
+      wg_barrier();
+      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
+    }
+    PA_WAIT_VMCNT(2 * (NST - 3));
+    wg_barrier();
+    issue(t + NST - 1);
+    softmax(t);
+    wg_barrier();
+    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
+  }
+  PA_WAIT_VMCNT(0);  // the trailing (empty) step requests complete before exit
+
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    const int row = wave * 48 + rb * 16 + c16;
+    const int tok = row >> a.lg, gq = row & (a.group - 1);
+    const float lt = o[NDB][rb][0];
+    if (tok >= it.nq) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m[rb] + __log2f(lt) : -INFINITY;
+    if (it.part < 0) {
+      const int64_t orow = (int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq;
+      unsigned char *op = (unsigned char *)a.out + orow * D * 2;
+#pragma unroll
+      for (int db = 0; db < NDB; db++) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; r++) v[r] = (__bf16)(o[db][rb][r] * inv);
+        *(bf16x4 *)(op + (16 * db + 4 * g) * 2) = v;
+      }
+      if (a.lse_out && g == 0) a.lse_out[orow] = lse2 * kLn2;
+    } else {
+      float *prow = a.part_o + ((int64_t)it.part * kW48TileRows + row) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; db++) *(f32x4 *)(prow + 16 * db + 4 * g) = o[db][rb] * inv;
+      if (g == 0) a.part_lse[(int64_t)it.part * kW48TileRows + row] = lse2;
+    }
+  }
+}
+
+template <int BS>
+__global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kW48Stages * 2 * kW48TileBytes];
+  __shared__ int bt_lds[kMaxDmaItemKeys / BS + 2];
+  const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
+  const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
+  for (int i = first; i < last; i++) {
+    if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
+    w48_item<BS>(a, a.items[i], (lds_u8 *)smem_raw, bt_lds);
   }
 }
 
@@ -1072,8 +1426,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128) {
-    if (a.tile_rows == kDmaTileRows) {
+    if (a.tile_rows == kPpTileRows) {
       hipLaunchKernelGGL((prefill_pp_kernel<BS>), dim3(n), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+    if (a.tile_rows == kW48TileRows) {
+      hipLaunchKernelGGL((prefill_w48_kernel<BS>), dim3(n), dim3(512), 0, s, a);
       return hipGetLastError();
     }
   }

@@ -105,8 +105,13 @@ struct GatherArgs {
 };
 
 constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
-constexpr int kDmaTileRows = 256;  // query rows per tile of prefill_dma_kernel
-constexpr int kPrefillRowsMax = 256;
+#ifndef PA_WIDE_TILE
+#define PA_WIDE_TILE 1
+#endif
+constexpr int kPpTileRows = 256;   // query rows per tile of prefill_pp_kernel
+constexpr int kW48TileRows = 384;  // query rows per tile of prefill_w48_kernel
+constexpr int kDmaTileRows = PA_WIDE_TILE ? kW48TileRows : kPpTileRows;  // bf16 KV, d 128
+constexpr int kPrefillRowsMax = 384;
 constexpr int kMaxDmaItemKeys = 65536;  // keys per item of prefill_pp_kernel (block ids staged in LDS)
 constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
