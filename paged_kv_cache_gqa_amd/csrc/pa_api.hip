@@ -131,7 +131,10 @@ int32_t prefill_tile_rows(const pa_kv_cache *c) {
 // (nwg / 8) + w / 8 when nwg is a multiple of 8: work-group ids are dispatched
 // round-robin over the eight XCDs, so each XCD (and its L2) holds one
 // contiguous stretch of the work, i.e. mostly one KV head.
-constexpr int kGroupPieces = 3;  // target pieces of work per work-group
+#ifndef PA_GROUP_PIECES
+#define PA_GROUP_PIECES 2
+#endif
+constexpr int kGroupPieces = PA_GROUP_PIECES;  // target pieces of work per work-group
 
 void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, Plan &P) {
   std::vector<int32_t> pre;  // prefill tiles
