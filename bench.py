@@ -161,7 +161,7 @@ KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_internal.h",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-PREFILL_KERNEL = "void pa::prefill_pp_kernel<16>(pa::AttnArgs)"
+PREFILL_KERNEL = "void pa::prefill_w48_kernel<16>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_kernel<128, 16, false>(pa::AttnArgs)"
 
 
@@ -337,7 +337,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill_incremental_bytes"),
-                     "kernel": "prefill_pp_kernel<16>",
+                     "kernel": "prefill_w48_kernel<16>",
                      "kernel_ms": round(k_ms, 4)},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
     }
@@ -382,7 +382,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_incremental_128k_bytes"),
-                         "kernel": "prefill_pp_kernel<16>", "kernel_ms": round(pk_ms, 4)},
+                         "kernel": "prefill_w48_kernel<16>", "kernel_ms": round(pk_ms, 4)},
         }
         del r
         torch.cuda.empty_cache()
