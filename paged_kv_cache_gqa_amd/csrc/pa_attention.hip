@@ -1323,11 +1323,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 // out = sum_i w_i o_i / sum_i w_i with w_i = 2^(lse_i - M), M = max_i lse_i,
 // lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing
 // (their stored o is 0).  A work-group takes kMergeRows rows of one task:
-// one wave per row computes the weights (lanes split the parts) into LDS,
-// then each thread reduces four consecutive d of one row over the parts with
-// 16-byte loads that do not wait on each other.
+// the part weights go to LDS first (one thread per row for a few parts, one
+// wave per row with the lanes splitting the parts otherwise), then each
+// thread reduces four consecutive d of one row over the parts with 16-byte
+// loads that do not wait on each other.
 constexpr int kMergeRows = 64;
 constexpr int kMergeWeights = 8192;
+constexpr int kMergeSerialParts = 16;  // up to this many parts, one thread per row weighs them
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -1358,23 +1360,46 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int rr = rb + r;
     return (int64_t)(mt.row0 + (rr >> a.lg)) * a.hq + mt.kvh * a.group + (rr & (a.group - 1));
   };
-  for (int r = wave; r < nr; r += 4) {
-    const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, lrow[(int64_t)i * rpp]);
-    M = wave_max(M);
-    float S = 0.f;
-    for (int i = lane; i < np; i += 64) {
-      const float li = lrow[(int64_t)i * rpp];
-      const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
-      S += w;
-      if (cached) sm_w[r * np + i] = w;
-    }
-    S = wave_sum(S);
-    if (lane == 0) {
+  if (np <= kMergeSerialParts) {
+    // few parts (the common case): one thread per row
+    const int r = threadIdx.x;
+    if (r < nr) {
+      const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
+      float li[kMergeSerialParts];
+      float M = -INFINITY;
+      for (int i = 0; i < np; i++) {
+        li[i] = lrow[(int64_t)i * rpp];
+        M = fmaxf(M, li[i]);
+      }
+      float S = 0.f;
+      for (int i = 0; i < np; i++) {
+        const float w = (M > -INFINITY && li[i] > -INFINITY) ? fast_exp2(li[i] - M) : 0.f;
+        S += w;
+        sm_w[r * np + i] = w;
+      }
       sm_max[r] = M;
       sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
       if (a.lse_out) a.lse_out[row_out(r)] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+    }
+  } else {
+    for (int r = wave; r < nr; r += 4) {
+      const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
+      float M = -INFINITY;
+      for (int i = lane; i < np; i += 64) M = fmaxf(M, lrow[(int64_t)i * rpp]);
+      M = wave_max(M);
+      float S = 0.f;
+      for (int i = lane; i < np; i += 64) {
+        const float li = lrow[(int64_t)i * rpp];
+        const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
+        S += w;
+        if (cached) sm_w[r * np + i] = w;
+      }
+      S = wave_sum(S);
+      if (lane == 0) {
+        sm_max[r] = M;
+        sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
+        if (a.lse_out) a.lse_out[row_out(r)] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+      }
     }
   }
   __syncthreads();
