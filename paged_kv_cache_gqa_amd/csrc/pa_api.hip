@@ -240,8 +240,8 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
       np0 += hkv;
     }
   }
-  const int64_t dchunk =
-      std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), kDecodeTargetItems));
+  const int64_t dchunk = std::min<int64_t>(
+      kMaxDecItemKeys, std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), kDecodeTargetItems)));
   int64_t pchunk = INT32_MAX;
   if (np0 > 0 && np0 < kPrefillTargetItems)
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, kPrefillTargetItems));

@@ -367,8 +367,9 @@ __device__ __forceinline__ void dma_load16(i32x4_t rsrc, int voff, uint32_t lds_
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
-// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 16)
-#define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 64: the count's
+// low four bits sit in bits 3:0 of the immediate, its high two in bits 15:14)
+#define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 // Work-group barrier without a memory fence: LDS hazards around it are
 // handled by explicit waits; the compiler-only fences keep memory operations
@@ -1319,6 +1320,210 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 }
 
 // =============================================================================
+// Decode for bf16 KV, head_dim 128, streamed through LDS.  One work-group per
+// item; wave w takes the 16-key slices w, w+4, w+8, ... of the item's range
+// with its own softmax state, combined through LDS at the end as above.  A
+// slice of K (and of V) is 4 KB contiguous in the cache (16 rows of one
+// block; the item's block ids are staged in LDS, items span at most
+// kMaxDecItemKeys keys), moved into the wave's own 4-stage LDS ring by four LDS-filling
+// buffer loads with the non-temporal hint (each byte is read once): full 1 KB
+// requests, which stream from HBM faster than register loads of 64-byte row
+// slices.  No wave reads another wave's ring, so only vmcnt waits are needed.
+// K is read back as the A operand of v_mfma_f32_16x16x32_bf16 (lane: key n,
+// d 32c + 8*q4 .. +7), V with ds_read_b64_tr_b16 as the A operand of
+// v_mfma_f32_16x16x16_bf16 (lane: d 16*db + n, keys 4*q4 .. +3), in the
+// row-swizzled layout of the 384-row prefill kernel.
+__device__ __forceinline__ void dma_load16_nt(i32x4_t rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+constexpr int kDecSlice = 16;                      // keys per wave step
+constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4 KB
+constexpr int kDecStages = 4;
+
+template <int BS>
+__global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int NCK = D / 32;  // score MFMAs per slice
+  constexpr int ND = D / 16;   // 16-wide d blocks of the output
+  constexpr int SB = kDecSliceBytes;
+  constexpr int NST = kDecStages;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * NST * 2 * SB];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  lds_u8 *smem = (lds_u8 *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const Item it = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q4 = lane >> 4;
+  const int tok = n >> a.lg, g = n & (a.group - 1);
+  const bool active = tok < it.nq;
+  const int pos = it.pos0 + tok;
+  const int qh = it.kvh * a.group + g;
+  const int hkv = a.c.hkv;
+  const int kv_lo = it.kv_lo, kv_hi = it.kv_hi;
+
+  bf16x8 qf[NCK];
+  {
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < NCK; c++) {
+      uint4 v = active ? gload16(qrow + (32 * c + 8 * q4) * 2) : make_uint4(0, 0, 0, 0);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+
+  float m = kNegBig, l = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; i++) o[i] = f32x4{};
+
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+  const int n_slices = (kv_hi - kv_lo + kDecSlice - 1) / kDecSlice;
+  const int nw = n_slices > wave ? (n_slices - wave + 3) / 4 : 0;  // this wave's slices
+  const int blk0 = kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+  const int lim = min(pos, kv_hi - 1);
+  {  // stage the item's block ids in LDS: a global load inside the loop would
+     // make the compiler wait for every outstanding load, the K/V stream too
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 256) bt_lds[i] = btr[i];
+  }
+  // Q and the block ids have landed (stated explicitly: otherwise the
+  // compiler, which does not see the stream's loads, places its wait for Q
+  // inside the loop as a full vmcnt(0))
+  PA_WAIT_VMCNT(0);
+  __syncthreads();
+  const int lim_min = min(it.pos0, kv_hi - 1);  // slices ending at or below it need no mask
+
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    voff[q] = (lane >> 4) * 256 + (((lane & 15) ^ swz(4 * q + (lane >> 4))) << 4);
+  const uint32_t ring = smem_addr + wave * NST * 2 * SB;
+  lds_u8 *ring_p = smem + wave * NST * 2 * SB;
+
+  auto slice_key = [&](int k) { return kv_lo + kDecSlice * (wave + 4 * k); };
+  // slice k's 4 KB of K and of V into stage k % NST; slices past this wave's
+  // share are requested with an empty buffer range (nothing is read), which
+  // keeps the vmcnt accounting uniform
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int key0 = slice_key(min(k, max(nw - 1, 0)));
+    const int64_t blk = __builtin_amdgcn_readfirstlane(bt_lds[min(key0 / BS, last_blk) - blk0]);
+    const int64_t base = ((blk * hkv + it.kvh) * BS + key0 % BS) * (D * 2);
+    const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+    const uint32_t st = ring + (k % NST) * 2 * SB;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int nrec = __builtin_amdgcn_readfirstlane(k < nw ? min(max(kv_hi - (key0 + 4 * q), 0), 4) * (D * 2) : 0);
+      const uint64_t kq = ka + q * 4 * D * 2, vq = va + q * 4 * D * 2;
+      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kq),
+                          __builtin_amdgcn_readfirstlane((int)((kq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vq),
+                          __builtin_amdgcn_readfirstlane((int)((vq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16_nt(rk, voff[q], st + q * 1024);
+      dma_load16_nt(rv, voff[q], st + SB + q * 1024);
+    }
+  };
+
+  auto compute = [&](int k) __attribute__((always_inline)) {
+    const lds_u8 *Ks = ring_p + (k % NST) * 2 * SB;
+    const lds_u8 *Vs = Ks + SB;
+    const int key0 = slice_key(k);
+    f32x4 s;
+#pragma unroll
+    for (int c = 0; c < NCK; c++) {
+      const bf16x8 kf = as_bf16x8(lds_load16(Ks + n * 256 + (((4 * c + q4) ^ swz(n)) << 4)));
+      s = mfma16x16x32(kf, qf[c], c == 0 ? f32x4{} : s);
+    }
+    if (key0 + kDecSlice - 1 > lim_min) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) s[r] = key0 + 4 * q4 + r <= lim ? s[r] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = xor32_max(xor16_max(mx));
+    const float mxs = mx * a.scale_log2;
+    if (__any(mxs > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+    const float nm = -m;
+    bf16x4 pb;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, nm));
+      l += p;
+      pb[r] = (__bf16)p;
+    }
+    const int vr = 4 * q4 + (n >> 2);
+    const int vbase = vr * 256 + ((((n & 3) >> 1) ^ swz(vr)) << 4) + (n & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < ND; db++) o[db] = mfma16x16x16(lds_read_tr(Vs + (vbase ^ (db << 5))), pb, o[db]);
+  };
+
+#pragma unroll
+  for (int k = 0; k < NST - 1; k++) issue(k);
+  for (int k = 0; k < nw; k++) {
+    PA_WAIT_VMCNT(8 * (NST - 2));  // slice k has landed (slices k+1 .. k+2 may be in flight)
+    compute(k);
+    issue(k + NST - 1);  // into the stage slice k-1 used
+  }
+  PA_WAIT_VMCNT(0);
+
+  // ---- combine the four waves' states through LDS
+  l = xor16_sum(l);
+  l = xor32_sum(l);
+  __syncthreads();
+  float *red_o = (float *)smem_raw;                  // [4][16][D]
+  float *red_m = red_o + 4 * 16 * D;                 // [4][16]
+  float *red_l = red_m + 4 * 16;                     // [4][16]
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+    *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
+  if (q4 == 0) {
+    red_m[wave * 16 + n] = m;
+    red_l[wave * 16 + n] = l;
+  }
+  __syncthreads();
+  const int rows = it.nq << a.lg;
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int cn = idx / D, e = idx % D;
+    if (cn >= rows) continue;
+    float M = red_m[cn];
+#pragma unroll
+    for (int w = 1; w < 4; w++) M = fmaxf(M, red_m[w * 16 + cn]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float sc = fast_exp2(red_m[w * 16 + cn] - M);
+      L += sc * red_l[w * 16 + cn];
+      O += sc * red_o[(w * 16 + cn) * D + e];
+    }
+    const float val = L > 0.f ? O / L : 0.f;
+    const int ctok = cn >> a.lg, cg = cn & (a.group - 1);
+    const int64_t orow = (int64_t)(it.row0 + ctok) * a.hq + it.kvh * a.group + cg;
+    if (it.part < 0) {
+      ((__bf16 *)a.out)[orow * D + e] = (__bf16)val;
+      if (e == 0 && a.lse_out) a.lse_out[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      a.part_o[((int64_t)it.part * kDecodeRows + cn) * D + e] = val;
+      if (e == 0)
+        a.part_lse[(int64_t)it.part * kDecodeRows + cn] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
+// =============================================================================
 // LSE merge of split items ([Agentic] §4.3.3): for each row,
 // out = sum_i w_i o_i / sum_i w_i with w_i = 2^(lse_i - M), M = max_i lse_i,
 // lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing
@@ -1463,8 +1668,15 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
   hipLaunchKernelGGL((prefill_kernel<D, BS, FP8>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+#ifndef PA_DECODE_DMA
+#define PA_DECODE_DMA 1
+#endif
 template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
+  if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
+    hipLaunchKernelGGL((decode_dma_kernel<BS>), dim3(n), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((decode_kernel<D, BS, FP8>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
