@@ -162,7 +162,7 @@ KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "void pa::prefill_w48_kernel<16>(pa::AttnArgs)"
-DECODE_KERNEL = "void pa::decode_kernel<128, 16, false>(pa::AttnArgs)"
+DECODE_KERNEL = "void pa::decode_dma_kernel<16>(pa::AttnArgs)"
 
 
 def kernel_source_hash():
@@ -363,7 +363,8 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_batch_bytes"),
-                         "algorithmic_bytes": int(byts)},
+                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_kernel<16>",
+                         "kernel_ms": round(dk_ms, 4)},
         }
         del r
         torch.cuda.empty_cache()

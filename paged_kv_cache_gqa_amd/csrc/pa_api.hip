@@ -77,7 +77,10 @@ pa_status check_cache(const pa_kv_cache *c) {
 // enough similar-sized items to fill every compute unit; split items write
 // partials merged by LSE ([Agentic] §4.3.3).
 constexpr int kNumCUs = 256;
-constexpr int kDecodeTargetItems = 32 * kNumCUs;
+#ifndef PA_DEC_ITEMS_PER_CU
+#define PA_DEC_ITEMS_PER_CU 32
+#endif
+constexpr int kDecodeTargetItems = PA_DEC_ITEMS_PER_CU * kNumCUs;
 constexpr int kDecodeMinChunk = 2048;
 constexpr int kPrefillTargetItems = 8 * kNumCUs;
 constexpr int kPrefillMinChunk = 4096;

@@ -1340,7 +1340,10 @@ __device__ __forceinline__ void dma_load16_nt(i32x4_t rsrc, int voff, uint32_t l
 
 constexpr int kDecSlice = 16;                      // keys per wave step
 constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4 KB
-constexpr int kDecStages = 4;
+#ifndef PA_DEC_STAGES
+#define PA_DEC_STAGES 4
+#endif
+constexpr int kDecStages = PA_DEC_STAGES;
 
 template <int BS>
 __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
