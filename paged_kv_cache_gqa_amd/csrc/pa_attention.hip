@@ -751,6 +751,25 @@ constexpr int kW48TileBytes = kW48Step * 128 * 2;  // K (or V) of one step, 8 KB
 #define PA_W48_STAGES 8
 #endif
 constexpr int kW48Stages = PA_W48_STAGES;
+// PA_W48_BARRIERS: work-group barriers per key step (2: strict alternation of
+// the two groups' phases; 1: one barrier, each group runs both phases back to
+// back).  PA_W48_PRIO: wave priority raised during the matrix-core phase.
+#ifndef PA_W48_BARRIERS
+#define PA_W48_BARRIERS 1
+#endif
+#ifndef PA_W48_PRIO
+#define PA_W48_PRIO 1
+#endif
+// PA_W48_FASTCHK: the per-step test for moving m is one maximum over the
+// lane's 24 scores against the slack, plus a wave-wide flag that every row
+// already has weight (rows without weight take the full test).
+// PA_W48_NEGM: -m held broadcast in registers as the score MFMAs' C operand.
+#ifndef PA_W48_FASTCHK
+#define PA_W48_FASTCHK 1
+#endif
+#ifndef PA_W48_NEGM
+#define PA_W48_NEGM 1
+#endif
 
 template <int BS>
 __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
@@ -857,13 +876,27 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   f32x4 o[NDB + 1][RB];
   f32x4 S[2][RB];
   bf16x8 pb[RB];
+#if PA_W48_NEGM
+  f32x4 negm[RB];  // -m[rb] in all four elements
+#endif
+  bool all_live = false;  // every row of the wave has weight (wave-uniform)
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
     m[rb] = 0.f;
+#if PA_W48_NEGM
+    negm[rb] = f32x4{};
+#endif
 #pragma unroll
     for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
   }
 
+  auto cinit = [&](int rb) __attribute__((always_inline)) {
+#if PA_W48_NEGM
+    return negm[rb];
+#else
+    return f32x4{} - m[rb];
+#endif
+  };
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
   // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
   auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
@@ -898,7 +931,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
           for (int rb = 0; rb < RB; rb++)
-            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} - m[rb] : S[kb][rb]);
+            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? cinit(rb) : S[kb][rb]);
       // order: the first three V fragments' reads; then per three MFMAs
       // (one fragment's worth) the reads of the fragment three ahead -- V
       // reads during the value product's first 15 MFMAs, K reads during its
@@ -933,11 +966,11 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       for (int kb = 0; kb < 2; kb++) {
         const bf16x8 kf = as_bf16x8(lds_load16(Kb + kb * 4096 + kofs(c)));
 #pragma unroll
-        for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? f32x4{} - m[rb] : S[kb][rb]);
+        for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? cinit(rb) : S[kb][rb]);
       }
   };
-  auto softmax = [&](int t) __attribute__((always_inline)) {
-    if (t >= t_full) {
+  auto softmax = [&](auto masked_tag, int t) __attribute__((always_inline)) {
+    if constexpr (decltype(masked_tag)::value) {
       const int key0 = t * kW48Step + 4 * g;
 #pragma unroll
       for (int rb = 0; rb < RB; rb++) {
@@ -949,9 +982,45 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       }
     }
     // S holds s - m.  A row's maximum is needed only when m has to move:
-    // test each lane's own maximum first, reduce across the row's four lanes
-    // only if some lane exceeds the slack (rare once m has settled).
-    float lmx[RB];
+    // test the lane's own maximum first, reduce across the row's four lanes
+    // only if some lane exceeds the slack (rare once m has settled) or some
+    // row has no weight yet (m then follows the row maximum).
+    auto rescale = [&]() __attribute__((always_inline)) {
+      bool live = true;
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) {
+        float lmx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) lmx = fmaxf(lmx, S[kb][rb][r]);
+        const float mx = xor32_max(xor16_max(lmx));
+        const bool empty = o[NDB][rb][0] == 0.f;
+        const bool mv = mx > kRescaleSlack || (empty && mx > -INFINITY);
+        live = live && (!empty || mx > -INFINITY);
+        const float shift = mv ? mx : 0.f;
+        const float alpha = fast_exp2(-shift);
+        m[rb] += shift;
+#if PA_W48_NEGM
+        negm[rb] = f32x4{} - m[rb];
+#endif
+#pragma unroll
+        for (int db = 0; db <= NDB; db++) o[db][rb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) S[kb][rb] -= shift;
+      }
+      all_live = __all(live);
+    };
+#if PA_W48_FASTCHK
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
+    if (__any((mx > kRescaleSlack) | !all_live)) rescale();
+#else
     bool need = false;
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
@@ -960,23 +1029,10 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
-      lmx[rb] = mx;
       need |= mx > kRescaleSlack || (o[NDB][rb][0] == 0.f && mx > -INFINITY);
     }
-    if (__any(need)) {
-#pragma unroll
-      for (int rb = 0; rb < RB; rb++) {
-        const float mx = xor32_max(xor16_max(lmx[rb]));
-        const bool mv = mx > kRescaleSlack || (o[NDB][rb][0] == 0.f && mx > -INFINITY);
-        const float shift = mv ? mx : 0.f;
-        const float alpha = fast_exp2(-shift);
-        m[rb] += shift;
-#pragma unroll
-        for (int db = 0; db <= NDB; db++) o[db][rb] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) S[kb][rb] -= shift;
-      }
-    }
+    if (__any(need)) rescale();
+#endif
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
@@ -996,39 +1052,67 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   // step t opens once this wave's share of step t+1 has landed (steps t+2 ..
   // t+NST-2 may be in flight); step t+NST-1 is requested into the stage step
   // t-1 left, during the wave's softmax phase.
+  // With one barrier per step the groups stay half a step apart: the
+  // barrier of step t finds group 0 about to start its matrix-core phase and
+  // group 1 its vector phase.
+  auto mid_barrier = [&]() __attribute__((always_inline)) {
+    if constexpr (PA_W48_BARRIERS == 2) wg_barrier();
+  };
+  auto prio_hi = [&]() __attribute__((always_inline)) {
+    if constexpr (PA_W48_PRIO) __builtin_amdgcn_s_setprio(PA_W48_PRIO);
+  };
+  auto prio_lo = [&]() __attribute__((always_inline)) {
+    if constexpr (PA_W48_PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  // Steps before t_full need no causal mask: each group's loop runs in two
+  // parts, the mask code only in the second, so the first has no branch.
+  const std::false_type open{};
+  const std::true_type masked{};
+  auto softmax_rt = [&](int t) __attribute__((always_inline)) {
+    if (t >= t_full) softmax(masked, t);
+    else softmax(open, t);
+  };
   if (grp == 0) {
-    wg_barrier();
-    softmax(t_begin);
+    mid_barrier();
+    softmax_rt(t_begin);
     int t = t_begin;
-    for (; t + 1 < t_end; t++) {
+    auto body = [&](auto mtag) __attribute__((always_inline)) {
       PA_WAIT_VMCNT(2 * (NST - 3));
       wg_barrier();
+      prio_hi();
       gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
-      wg_barrier();
+      prio_lo();
+      mid_barrier();
       issue(t + NST - 1);                                      // phase B: loads, vector ALUs
-      softmax(t + 1);
-    }
+      softmax(mtag, t + 1);
+    };
+    for (const int t_open = min(t_full, t_end) - 1; t < t_open; t++) body(open);
+    for (; t + 1 < t_end; t++) body(masked);
     PA_WAIT_VMCNT(2 * (NST - 3));
     wg_barrier();
     gemm(std::false_type{}, stage(t) + TILEB, nullptr);
-    wg_barrier();
+    mid_barrier();
     issue(t + NST - 1);
   } else {
-    wg_barrier();
+    mid_barrier();
     int t = t_begin;
-    for (; t + 1 < t_end; t++) {
+    auto body = [&](auto mtag) __attribute__((always_inline)) {
       PA_WAIT_VMCNT(2 * (NST - 3));
       wg_barrier();
       issue(t + NST - 1);
-      softmax(t);                                              // phase A: vector ALUs
-      wg_barrier();
+      softmax(mtag, t);                                        // phase A: vector ALUs
+      mid_barrier();
+      prio_hi();
       gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
-    }
+      prio_lo();
+    };
+    for (const int t_open = min(t_full, t_end - 1); t < t_open; t++) body(open);
+    for (; t + 1 < t_end; t++) body(masked);
     PA_WAIT_VMCNT(2 * (NST - 3));
     wg_barrier();
     issue(t + NST - 1);
-    softmax(t);
-    wg_barrier();
+    softmax_rt(t);
+    mid_barrier();
     gemm(std::false_type{}, stage(t) + TILEB, nullptr);
   }
   PA_WAIT_VMCNT(0);  // the trailing (empty) step requests complete before exit
