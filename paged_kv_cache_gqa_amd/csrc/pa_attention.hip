@@ -840,27 +840,38 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
 
   __syncthreads();  // block ids visible
 
-  auto block_of = [&](int t) __attribute__((always_inline)) {
-    const int tt = min(t, t_end - 1);
-    return bt_lds[min((tt * kW48Step + 4 * wave) / BS, last_blk) - blk0];
-  };
-  int blk_next = block_of(t_begin);
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    const int tt = min(t, t_end - 1);
-    const int64_t blk = __builtin_amdgcn_readfirstlane(blk_next);
-    blk_next = block_of(t + 1);
-    const uint32_t st = smem_addr + ((t - t_begin) % NST) * STAGEB;
-    const int rpos = tt * kW48Step + 4 * wave;
-    const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
-    const int nrec = __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos, 0), 4) * (D * 2) : 0);
-    const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+  // K/V requests walk the item's steps in order (the prologue's NST-1 steps,
+  // then one per step), so their positions are running counters.  Items
+  // start on a step boundary (the planner cuts key ranges in multiples of
+  // 64 keys), so rpos >= kv_lo.  A request past the range end has a buffer
+  // size of zero: it moves no data but keeps the per-step vmcnt accounting.
+  constexpr int LGBS = BS == 16 ? 4 : 6;
+  static_assert(BS == 16 || BS == 64, "block size");
+  const uint32_t blk_bytes = (uint32_t)hkv * BS * D * 2;
+  const uint64_t kc_head = (uint64_t)(kc + (int64_t)kvh * BS * D * 2);
+  const uint64_t vc_head = (uint64_t)(vc + (int64_t)kvh * BS * D * 2);
+  const int bt_last = last_blk - blk0;
+  int rpos = t_begin * kW48Step + 4 * wave;  // first key row of this wave's next request
+  uint32_t st_off = 0;                         // its ring stage, in bytes
+  int blk_next = bt_lds[min((rpos >> LGBS) - blk0, bt_last)];
+  auto issue = [&](int) __attribute__((always_inline)) {
+    const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(blk_next);
+    const uint64_t off = (uint64_t)blk * blk_bytes + (uint32_t)((rpos & (BS - 1)) * (D * 2));
+    const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 4) * (D * 2));
+    const uint32_t st = smem_addr + st_off;
+    const uint64_t ka = kc_head + off, va = vc_head + off;
+    // (readfirstlane keeps the descriptor in SGPRs, as the asm operand needs)
     const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
                         __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
     const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
                         __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
     dma_load16(rk, voff, st + wave * 1024);
     dma_load16(rv, voff, st + TILEB + wave * 1024);
+    rpos += kW48Step;
+    st_off = (st_off + STAGEB) & (NST * STAGEB - 1);
+    blk_next = bt_lds[min((rpos >> LGBS) - blk0, bt_last)];
   };
+  static_assert((NST & (NST - 1)) == 0, "ring stages: a power of two");
   auto stage = [&](int t) __attribute__((always_inline)) {
     return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
   };
@@ -872,19 +883,22 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   // o[NDB][rb] is the row sum l: the value product runs one more d-block
   // whose A operand is all ones, so l comes from the matrix cores (over the
   // same bf16 probabilities the output uses) and is rescaled with o.
+#if !PA_W48_NEGM
   float m[RB];
+#endif
   f32x4 o[NDB + 1][RB];
   f32x4 S[2][RB];
   bf16x8 pb[RB];
 #if PA_W48_NEGM
-  f32x4 negm[RB];  // -m[rb] in all four elements
+  f32x4 negm[RB];  // -m[rb] in all four elements; m[rb] itself is not kept
 #endif
-  bool all_live = false;  // every row of the wave has weight (wave-uniform)
+  int all_live = 0;  // every row of the wave has weight (wave-uniform)
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
-    m[rb] = 0.f;
 #if PA_W48_NEGM
     negm[rb] = f32x4{};
+#else
+    m[rb] = 0.f;
 #endif
 #pragma unroll
     for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
@@ -1000,16 +1014,17 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
         live = live && (!empty || mx > -INFINITY);
         const float shift = mv ? mx : 0.f;
         const float alpha = fast_exp2(-shift);
-        m[rb] += shift;
 #if PA_W48_NEGM
-        negm[rb] = f32x4{} - m[rb];
+        negm[rb] -= shift;
+#else
+        m[rb] += shift;
 #endif
 #pragma unroll
         for (int db = 0; db <= NDB; db++) o[db][rb] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) S[kb][rb] -= shift;
       }
-      all_live = __all(live);
+      all_live = __builtin_amdgcn_readfirstlane(__all(live));
     };
 #if PA_W48_FASTCHK
     float mx = -INFINITY;
@@ -1019,7 +1034,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
-    if (__any((mx > kRescaleSlack) | !all_live)) rescale();
+    if (__any(mx > kRescaleSlack) || !all_live) rescale();
 #else
     bool need = false;
 #pragma unroll
@@ -1124,7 +1139,12 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     const float lt = o[NDB][rb][0];
     if (tok >= it.nq) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse2 = lt > 0.f ? m[rb] + __log2f(lt) : -INFINITY;
+#if PA_W48_NEGM
+    const float mrow = -negm[rb][0];
+#else
+    const float mrow = m[rb];
+#endif
+    const float lse2 = lt > 0.f ? mrow + __log2f(lt) : -INFINITY;
     if (it.part < 0) {
       const int64_t orow = (int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq;
       unsigned char *op = (unsigned char *)a.out + orow * D * 2;
