@@ -64,7 +64,21 @@ class Runner:
         self.pa, self.torch, self.spec = pa, torch, spec
         b = W.make_batch(spec, dev)
         self.b = b
-        self.cache = pa.make_cache(b.k_pool, b.v_pool)
+        if spec.kv_dtype == "e4m3":
+            # E4M3 codes of the history under the per-(block, head) scales
+            # (input preparation; the step's own tokens go through kv_append)
+            def codes(pool, sc):
+                out = torch.empty(pool.shape, dtype=torch.uint8, device=dev)
+                for i in range(0, pool.shape[0], 4096):
+                    x = pool[i:i + 4096].float() / sc[i:i + 4096, :, None, None]
+                    out[i:i + 4096] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+                return out
+            self.k_codes, self.v_codes = codes(b.k_pool, b.k_scale), codes(b.v_pool, b.v_scale)
+            b.k_pool = b.v_pool = None
+            torch.cuda.empty_cache()
+            self.cache = pa.make_cache(self.k_codes, self.v_codes, b.k_scale, b.v_scale)
+        else:
+            self.cache = pa.make_cache(b.k_pool, b.v_pool)
         self.bt = torch.from_numpy(b.block_tables).to(dev)
         self.slots = b.slot_mapping.to(dev)
         ws = pa.pa_workspace_size(b.hist, b.incr, spec.num_q_heads, self.cache)

@@ -78,7 +78,7 @@ pa_status check_cache(const pa_kv_cache *c) {
 // partials merged by LSE ([Agentic] §4.3.3).
 constexpr int kNumCUs = 256;
 #ifndef PA_DEC_ITEMS_PER_CU
-#define PA_DEC_ITEMS_PER_CU 32
+#define PA_DEC_ITEMS_PER_CU 4
 #endif
 constexpr int kDecodeTargetItems = PA_DEC_ITEMS_PER_CU * kNumCUs;
 constexpr int kDecodeMinChunk = 2048;

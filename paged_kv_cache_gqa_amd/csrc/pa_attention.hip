@@ -1177,6 +1177,59 @@ __global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
   }
 }
 
+// The four waves of a decode work-group hold softmax states (m in log2
+// units, per-lane partial l, o[d-block]) over disjoint keys of one item's
+// 16 rows; combine them through LDS and write the rows (or the item's partial).
+template <int D>
+__device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it, unsigned char *smem_raw,
+                                               float m, float l, const f32x4 (&o)[D / 16]) {
+  constexpr int ND = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15, q4 = lane >> 4;
+  l = xor16_sum(l);
+  l = xor32_sum(l);
+  __syncthreads();
+  float *red_o = (float *)smem_raw;                  // [4][16][D]
+  float *red_m = red_o + 4 * 16 * D;                 // [4][16]
+  float *red_l = red_m + 4 * 16;                     // [4][16]
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+    *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
+  if (q4 == 0) {
+    red_m[wave * 16 + n] = m;
+    red_l[wave * 16 + n] = l;
+  }
+  __syncthreads();
+  const int rows = it.nq << a.lg;
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int cn = idx / D, e = idx % D;
+    if (cn >= rows) continue;
+    float M = red_m[cn];
+#pragma unroll
+    for (int w = 1; w < 4; w++) M = fmaxf(M, red_m[w * 16 + cn]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float sc = fast_exp2(red_m[w * 16 + cn] - M);
+      L += sc * red_l[w * 16 + cn];
+      O += sc * red_o[(w * 16 + cn) * D + e];
+    }
+    const float val = L > 0.f ? O / L : 0.f;
+    const int ctok = cn >> a.lg, cg = cn & (a.group - 1);
+    const int64_t orow = (int64_t)(it.row0 + ctok) * a.hq + it.kvh * a.group + cg;
+    if (it.part < 0) {
+      ((__bf16 *)a.out)[orow * D + e] = (__bf16)val;
+      if (e == 0 && a.lse_out) a.lse_out[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      a.part_o[((int64_t)it.part * kDecodeRows + cn) * D + e] = val;
+      if (e == 0)
+        a.part_lse[(int64_t)it.part * kDecodeRows + cn] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
 // =============================================================================
 // Decode (and short increments, tokens x G <= 16): one work-group per item;
 // its four waves stream disjoint 64-key tiles of the item's range, each with
@@ -1380,47 +1433,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
     tw += 4;
   }
 
-  // ---- combine the four waves' states through LDS
-  l = xor16_sum(l);
-  l = xor32_sum(l);
-  __syncthreads();
-  float *red_o = (float *)smem_raw;                  // [4][16][D]
-  float *red_m = red_o + 4 * 16 * D;                 // [4][16]
-  float *red_l = red_m + 4 * 16;                     // [4][16]
-#pragma unroll
-  for (int db = 0; db < ND; db++)
-    *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
-  if (q4 == 0) {
-    red_m[wave * 16 + n] = m;
-    red_l[wave * 16 + n] = l;
-  }
-  __syncthreads();
-  const int rows = it.nq << a.lg;
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int cn = idx / D, e = idx % D;
-    if (cn >= rows) continue;
-    float M = red_m[cn];
-#pragma unroll
-    for (int w = 1; w < 4; w++) M = fmaxf(M, red_m[w * 16 + cn]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const float sc = fast_exp2(red_m[w * 16 + cn] - M);
-      L += sc * red_l[w * 16 + cn];
-      O += sc * red_o[(w * 16 + cn) * D + e];
-    }
-    const float val = L > 0.f ? O / L : 0.f;
-    const int ctok = cn >> a.lg, cg = cn & (a.group - 1);
-    const int64_t orow = (int64_t)(it.row0 + ctok) * a.hq + it.kvh * a.group + cg;
-    if (it.part < 0) {
-      ((__bf16 *)a.out)[orow * D + e] = (__bf16)val;
-      if (e == 0 && a.lse_out) a.lse_out[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      a.part_o[((int64_t)it.part * kDecodeRows + cn) * D + e] = val;
-      if (e == 0)
-        a.part_lse[(int64_t)it.part * kDecodeRows + cn] = L > 0.f ? M + __log2f(L) : -INFINITY;
-    }
-  }
+  decode_combine<D>(a, it, smem_raw, m, l, o);
 }
 
 // =============================================================================
@@ -1539,16 +1552,27 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
     }
   };
 
+  const int vr = 4 * q4 + (n >> 2);
+  const int vbase = vr * 256 + ((((n & 3) >> 1) ^ swz(vr)) << 4) + (n & 1) * 8;
+  // Slice k is read from LDS into registers first; its stage is then free
+  // and slice k + NST is requested into it before the arithmetic, so all NST
+  // stages are in flight while the wave computes.
   auto compute = [&](int k) __attribute__((always_inline)) {
     const lds_u8 *Ks = ring_p + (k % NST) * 2 * SB;
     const lds_u8 *Vs = Ks + SB;
     const int key0 = slice_key(k);
+    uint4 kraw[NCK];
+    bf16x4 vraw[ND];
+#pragma unroll
+    for (int c = 0; c < NCK; c++) kraw[c] = lds_load16(Ks + n * 256 + (((4 * c + q4) ^ swz(n)) << 4));
+#pragma unroll
+    for (int db = 0; db < ND; db++) vraw[db] = lds_read_tr(Vs + (vbase ^ (db << 5)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's bytes are in registers
+    __builtin_amdgcn_sched_barrier(0);
+    issue(k + NST);
     f32x4 s;
 #pragma unroll
-    for (int c = 0; c < NCK; c++) {
-      const bf16x8 kf = as_bf16x8(lds_load16(Ks + n * 256 + (((4 * c + q4) ^ swz(n)) << 4)));
-      s = mfma16x16x32(kf, qf[c], c == 0 ? f32x4{} : s);
-    }
+    for (int c = 0; c < NCK; c++) s = mfma16x16x32(as_bf16x8(kraw[c]), qf[c], c == 0 ? f32x4{} : s);
     if (key0 + kDecSlice - 1 > lim_min) {
 #pragma unroll
       for (int r = 0; r < 4; r++) s[r] = key0 + 4 * q4 + r <= lim ? s[r] : -INFINITY;
@@ -1572,62 +1596,214 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
       l += p;
       pb[r] = (__bf16)p;
     }
-    const int vr = 4 * q4 + (n >> 2);
-    const int vbase = vr * 256 + ((((n & 3) >> 1) ^ swz(vr)) << 4) + (n & 1) * 8;
 #pragma unroll
-    for (int db = 0; db < ND; db++) o[db] = mfma16x16x16(lds_read_tr(Vs + (vbase ^ (db << 5))), pb, o[db]);
+    for (int db = 0; db < ND; db++) o[db] = mfma16x16x16(vraw[db], pb, o[db]);
   };
 
 #pragma unroll
-  for (int k = 0; k < NST - 1; k++) issue(k);
+  for (int k = 0; k < NST; k++) issue(k);
   for (int k = 0; k < nw; k++) {
-    PA_WAIT_VMCNT(8 * (NST - 2));  // slice k has landed (slices k+1 .. k+2 may be in flight)
-    compute(k);
-    issue(k + NST - 1);  // into the stage slice k-1 used
+    PA_WAIT_VMCNT(8 * (NST - 1));  // slice k has landed (slices k+1 .. k+NST-1 may be in flight)
+    compute(k);                    // requests slice k + NST into slice k's stage
   }
   PA_WAIT_VMCNT(0);
 
-  // ---- combine the four waves' states through LDS
-  l = xor16_sum(l);
-  l = xor32_sum(l);
-  __syncthreads();
-  float *red_o = (float *)smem_raw;                  // [4][16][D]
-  float *red_m = red_o + 4 * 16 * D;                 // [4][16]
-  float *red_l = red_m + 4 * 16;                     // [4][16]
+  decode_combine<D>(a, it, smem_raw, m, l, o);
+}
+
+// =============================================================================
+// Decode for E4M3 KV, head_dim 128, streamed through LDS like the bf16 one:
+// wave w takes the 32-key slices w, w+4, ... of the item's range; a slice of
+// K codes (and of V codes) is 4 KB, 32 rows of 128 bytes, moved into the
+// wave's ring by four 1 KB LDS-filling loads of 8 rows each (rows of a load
+// lie in one cache block for block sizes 16 and 64).  LDS row r holds its
+// 16-byte chunk q at q ^ f(r), f(r) = (r >> 1) & 7.
+//   Scores, per 16-key half h: S_h = K_h Q^T on v_mfma_f32_16x16x32_bf16, A =
+//   K codes widened to bf16 (lane: key n, d 32c + 8*q4 .. +7, one 8-byte LDS
+//   read); the half's K scale multiplies the scores (a half lies in one
+//   block).  Lane (n, q4) then holds row n's keys 16h + 4*q4 .. +3.
+//   Values: O^T += V^T P^T on the same MFMA over the slice's 32 keys, B = P^T
+//   as (half 0 keys 4*q4.., half 1 keys 16 + 4*q4..) with each half's V
+//   scale folded into its probabilities; A = V^T from one transposing 8-bit
+//   read per d-block, its lane pairs addressing the key rows in that order.
+constexpr int kDec8Slice = 32;                        // keys per wave step
+constexpr int kDec8SliceBytes = kDec8Slice * 128;     // K (or V) codes of one slice, 4 KB
+
+template <int BS>
+__global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int NCK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int SB = kDec8SliceBytes;
+  constexpr int NST = kDecStages;
+  static_assert(BS == 16 || BS == 64, "block size");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * NST * 2 * SB];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  lds_u8 *smem = (lds_u8 *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const Item it = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q4 = lane >> 4;
+  const int tok = n >> a.lg, g = n & (a.group - 1);
+  const bool active = tok < it.nq;
+  const int pos = it.pos0 + tok;
+  const int qh = it.kvh * a.group + g;
+  const int hkv = a.c.hkv;
+  const int kv_lo = it.kv_lo, kv_hi = it.kv_hi;
+
+  bf16x8 qf[NCK];
+  {
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
 #pragma unroll
-  for (int db = 0; db < ND; db++)
-    *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
-  if (q4 == 0) {
-    red_m[wave * 16 + n] = m;
-    red_l[wave * 16 + n] = l;
-  }
-  __syncthreads();
-  const int rows = it.nq << a.lg;
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int cn = idx / D, e = idx % D;
-    if (cn >= rows) continue;
-    float M = red_m[cn];
-#pragma unroll
-    for (int w = 1; w < 4; w++) M = fmaxf(M, red_m[w * 16 + cn]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const float sc = fast_exp2(red_m[w * 16 + cn] - M);
-      L += sc * red_l[w * 16 + cn];
-      O += sc * red_o[(w * 16 + cn) * D + e];
+    for (int c = 0; c < NCK; c++) {
+      uint4 v = active ? gload16(qrow + (32 * c + 8 * q4) * 2) : make_uint4(0, 0, 0, 0);
+      qf[c] = as_bf16x8(v);
     }
-    const float val = L > 0.f ? O / L : 0.f;
-    const int ctok = cn >> a.lg, cg = cn & (a.group - 1);
-    const int64_t orow = (int64_t)(it.row0 + ctok) * a.hq + it.kvh * a.group + cg;
-    if (it.part < 0) {
-      ((__bf16 *)a.out)[orow * D + e] = (__bf16)val;
-      if (e == 0 && a.lse_out) a.lse_out[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      a.part_o[((int64_t)it.part * kDecodeRows + cn) * D + e] = val;
-      if (e == 0)
-        a.part_lse[(int64_t)it.part * kDecodeRows + cn] = L > 0.f ? M + __log2f(L) : -INFINITY;
-    }
   }
+
+  float m = kNegBig, l = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; i++) o[i] = f32x4{};
+
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+  const int n_slices = (kv_hi - kv_lo + kDec8Slice - 1) / kDec8Slice;
+  const int nw = n_slices > wave ? (n_slices - wave + 3) / 4 : 0;  // this wave's slices
+  const int blk0 = kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+  const int lim = min(pos, kv_hi - 1);
+  {  // the item's block ids into LDS (see the bf16 kernel)
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 256) bt_lds[i] = btr[i];
+  }
+  PA_WAIT_VMCNT(0);
+  __syncthreads();
+  const int lim_min = min(it.pos0, kv_hi - 1);
+
+  auto f = [](int r) { return (r >> 1) & 7; };
+  // load q of a slice: rows 8q .. 8q+7; lane i fills chunk position i & 7 of
+  // row 8q + (i >> 3) with the row's chunk (i & 7) ^ f(row)
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) voff[q] = (lane >> 3) * 128 + (((lane & 7) ^ f(8 * q + (lane >> 3))) << 4);
+  const uint32_t ring = smem_addr + wave * NST * 2 * SB;
+  lds_u8 *ring_p = smem + wave * NST * 2 * SB;
+
+  auto slice_key = [&](int k) { return kv_lo + kDec8Slice * (wave + 4 * k); };
+  auto block_at = [&](int key) {
+    return __builtin_amdgcn_readfirstlane(bt_lds[min(key / BS, last_blk) - blk0]);
+  };
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int key0 = slice_key(min(k, max(nw - 1, 0)));
+    const uint32_t st = ring + (k % NST) * 2 * SB;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int row0 = key0 + 8 * q;
+      const int64_t blk = block_at(row0);
+      const int64_t base = ((blk * hkv + it.kvh) * BS + row0 % BS) * D;
+      const int nrec = __builtin_amdgcn_readfirstlane(k < nw ? min(max(kv_hi - row0, 0), 8) * D : 0);
+      const uint64_t kq = (uint64_t)(kc + base), vq = (uint64_t)(vc + base);
+      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kq),
+                          __builtin_amdgcn_readfirstlane((int)((kq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vq),
+                          __builtin_amdgcn_readfirstlane((int)((vq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16_nt(rk, voff[q], st + q * 1024);
+      dma_load16_nt(rv, voff[q], st + SB + q * 1024);
+    }
+  };
+
+  // per-lane LDS offsets: K fragment c of half h at kofs(h) ^ (c << 5); V^T
+  // fragment db at vofs ^ (db << 4)
+  auto kofs = [&](int h) {
+    const int r = 16 * h + n;
+    return r * 128 + (((q4 >> 1) ^ f(r)) << 4) + (q4 & 1) * 8;
+  };
+  const int vrow = (n >> 1) < 4 ? 4 * q4 + (n >> 1) : 16 + 4 * q4 + (n >> 1) - 4;
+  const int vofs = vrow * 128 + (f(vrow) << 4) + (n & 1) * 8;
+
+  // Slice k is read from LDS into registers first; its stage is then free
+  // and slice k + NST is requested into it before the arithmetic, so all NST
+  // stages are in flight while the wave computes.
+  auto compute = [&](int k) __attribute__((always_inline)) {
+    const lds_u8 *Ks = ring_p + (k % NST) * 2 * SB;
+    const lds_u8 *Vs = Ks + SB;
+    const int key0 = slice_key(k);
+    uint2 kraw[2][NCK], vraw[ND];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int c = 0; c < NCK; c++) kraw[h][c] = lds_load8(Ks + (kofs(h) ^ (c << 5)));
+#pragma unroll
+    for (int db = 0; db < ND; db++) vraw[db] = lds_read_tr8(Vs + (vofs ^ (db << 4)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's bytes are in registers
+    __builtin_amdgcn_sched_barrier(0);
+    issue(k + NST);
+    // the scales through the constant address space: uniform scalar loads
+    // (a vector load would be counted with the K/V stream by vmcnt)
+    typedef const __attribute__((address_space(4))) float cfloat;
+    float ksc[2], vsc[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int64_t blk = block_at(key0 + 16 * h);
+      ksc[h] = ((cfloat *)a.c.ks)[blk * hkv + it.kvh] * a.scale_log2;
+      vsc[h] = ((cfloat *)a.c.vs)[blk * hkv + it.kvh];
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int c = 0; c < NCK; c++) {
+        const bf16x8 kf = e4m3x8_to_bf16x8_hw(kraw[h][c]);
+        s[h] = mfma16x16x32(kf, qf[c], c == 0 ? f32x4{} : s[h]);
+      }
+      s[h] *= ksc[h];  // base-2 logits
+    }
+    if (key0 + kDec8Slice - 1 > lim_min) {
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[h][r] = key0 + 16 * h + 4 * q4 + r <= lim ? s[h][r] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = xor32_max(xor16_max(mx));
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+    bf16x8 pb;
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float p = fast_exp2(s[h][r] - m);
+        l += p;
+        pb[4 * h + r] = (__bf16)(p * vsc[h]);
+      }
+#pragma unroll
+    for (int db = 0; db < ND; db++) {
+      const bf16x8 vf = e4m3x8_to_bf16x8_hw(vraw[db]);
+      o[db] = mfma16x16x32(vf, pb, o[db]);
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < NST; k++) issue(k);
+  for (int k = 0; k < nw; k++) {
+    PA_WAIT_VMCNT(8 * (NST - 1));  // slice k has landed (slices k+1 .. k+NST-1 may be in flight)
+    compute(k);                    // requests slice k + NST into slice k's stage
+  }
+  PA_WAIT_VMCNT(0);
+  decode_combine<D>(a, it, smem_raw, m, l, o);
 }
 
 // =============================================================================
@@ -1782,6 +1958,10 @@ template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
     hipLaunchKernelGGL((decode_dma_kernel<BS>), dim3(n), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if constexpr (FP8 && D == 128 && PA_DECODE_DMA) {
+    hipLaunchKernelGGL((decode_dma_fp8_kernel<BS>), dim3(n), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_kernel<D, BS, FP8>), dim3(n), dim3(256), 0, s, a);

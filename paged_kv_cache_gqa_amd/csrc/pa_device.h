@@ -79,6 +79,20 @@ __device__ __forceinline__ uint4 lds_load16(const lds_u8 *p) {
   u32x4 v = *(const lds_u32x4 *)p;
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ uint2 lds_load8(const lds_u8 *p) {
+  u32x2 v = *(const lds_u32x2 *)p;
+  return make_uint2(v[0], v[1]);
+}
+// Transposing 8-byte read of 8-bit elements: within each 16-lane group,
+// lanes 2k and 2k+1 address the two 8-byte halves of "row" k (k = 0..7),
+// and lane j of the group receives byte j of each of the 8 rows, row k in
+// byte k of the result.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_read_tr8(const lds_u8 *p) {
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t *)p);
+  return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
 __device__ __forceinline__ void lds_store16(lds_u8 *p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   *(lds_u32x4 *)p = w;
@@ -129,6 +143,19 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
     out[i] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// The same widening with gfx950's conversion instruction (OCP E4M3 -> bf16,
+// two codes per instruction; a scale of 1.0 leaves the values exact).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8_hw(uint2 w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Round a float to E4M3, nearest-even, saturating finite and infinite

@@ -163,6 +163,9 @@ CASES = [
     ([640], [200], 32, 8, 128, 64, "e4m3"),              # E4M3, block 64
     ([900, 5000], [77, 1], 32, 8, 128, 16, "e4m3"),      # E4M3, block 16
     ([3000, 100], [1, 65], 8, 2, 64, 64, "e4m3"),        # E4M3, head dim 64
+    ([20000, 3000, 50], [1, 1, 1], 32, 8, 128, 64, "e4m3"),  # E4M3 decode, split and merged
+    ([9000, 130], [1, 3], 32, 8, 128, 16, "e4m3"),       # E4M3 decode, block 16
+    ([7000, 33], [2, 1], 64, 8, 128, 16, "e4m3"),        # E4M3 decode, group 8
 ]
 
 
