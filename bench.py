@@ -98,7 +98,7 @@ class Runner:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        for k in range(4):
+        for k in range(5):
             pa.pa_timing_read(k)  # drop anything recorded before
         pa.pa_timing_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -111,7 +111,7 @@ class Runner:
         pa.pa_timing_enable(False)
         ms = e0.elapsed_time(e1) / steps
         kern = {}
-        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge")):
+        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "dequant")):
             tot, cnt = pa.pa_timing_read(kind)
             if cnt:
                 kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step

@@ -135,9 +135,14 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  *   lse_out       optional fp32 [total_q][num_q_heads]: ln(sum_j exp(scale *
  *                 q.k_j)) over the keys the row sees; NULL to skip.
  *   workspace     device scratch of at least pa_workspace_size(...) bytes,
- *                 256-byte aligned; contents need no initialisation.
+ *                 256-byte aligned; contents need no initialisation.  With an
+ *                 E4M3 cache of head_dim 128 it also holds a bf16 copy of the
+ *                 context of every sequence with more than 16/G new tokens
+ *                 (4 KB per token for 8 KV heads), which the prefill reads.
  * Row i of sequence s is at position p = hist[s] + i, and
  *   out[row][h] = sum_{j<=p} softmax_j(scale * q[row][h] . K[j][h/G]) V[j][h/G].
+ * With an E4M3 cache, K[j] and V[j] are code * scale of their (block, head);
+ * decode uses that product in fp32, prefill rounds it to bf16 (nearest-even).
  * Neither q nor the caches are written.
  */
 PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
@@ -167,8 +172,9 @@ PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_
  * records HIP events on the call's stream around the kernel; the durations
  * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
  * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention,
- * 3 = LSE merge, the summed milliseconds and launch count since the last
- * reset (it synchronises on the recorded events), then resets that kind. */
+ * 3 = LSE merge, 4 = bf16 copy of E4M3 context for prefill, the summed
+ * milliseconds and launch count since the last reset (it synchronises on the
+ * recorded events), then resets that kind. */
 PA_API pa_status pa_timing_enable(int enable);
 PA_API pa_status pa_timing_read(int kind, double *ms, int64_t *count);
 

@@ -92,8 +92,15 @@ struct Plan {
   std::vector<int32_t> wg_first;  // persistent prefill launch: items of work-group w are
                                   // prefill[wg_first[w] .. wg_first[w+1]); empty otherwise
   int64_t n_part_prefill = 0, n_part_decode = 0;
-  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, plan_bytes = 0;
-  size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
+  // E4M3 caches with prefill work: bf16 copies of the prefilled sequences'
+  // context (dq items), read by the bf16 prefill kernels through compact
+  // block tables [num_seqs][dq_mb]
+  std::vector<DqItem> dq;
+  int64_t dq_blocks = 0;
+  int32_t dq_mb = 0;
+  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, off_dq = 0, plan_bytes = 0;
+  size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0;
+  size_t off_dq_bt = 0, off_dq_k = 0, off_dq_v = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -116,11 +123,16 @@ void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out)
   }
 }
 
-// Query rows per prefill tile: the LDS-DMA kernel (bf16 KV, head_dim 128)
-// takes 256, the register-staged kernel 128.
+// Query rows per prefill tile: the LDS-DMA kernel (head_dim 128; E4M3
+// context goes through a bf16 copy) takes 384, the register-staged kernel
+// (head_dim 64) 128.
 int32_t prefill_tile_rows(const pa_kv_cache *c) {
-  return (c->dtype == PA_KV_BF16 && c->head_dim == 128) ? kDmaTileRows : kRegTileRows;
+  return c->head_dim == 128 ? kDmaTileRows : kRegTileRows;
 }
+bool prefill_dequant(const pa_kv_cache *c) {
+  return c->dtype == PA_KV_FP8_E4M3 && c->head_dim == 128;
+}
+constexpr int32_t kDqBlocksPerGroup = 16;  // cache blocks per work-group of the bf16 copy
 
 // Persistent split for the 256-row kernel.  The prefill work -- every tile
 // times every KV head, measured in 64-key steps -- is laid out KV-head-major,
@@ -215,7 +227,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
 }
 
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
-               int32_t group, int32_t d, int32_t tile_rows, Plan &P) {
+               int32_t group, int32_t d, int32_t tile_rows, Plan &P, int32_t dq_bs = 0) {
   const int32_t dec_tokens = kDecodeRows / group;  // >= 1 for group <= 16
   const int32_t pre_tokens = tile_rows / group;
   std::vector<Tile> tiles;
@@ -290,6 +302,19 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
       if (i < pre_by_head[k].size()) P.prefill.push_back(pre_by_head[k][i]);
   std::stable_sort(P.decode.begin(), P.decode.end(), longer);
 
+  if (dq_bs > 0) {  // bf16 copies of the context of every sequence with prefill tiles
+    int32_t last = -1;
+    for (const Tile &t : tiles) {
+      if (t.decode || t.seq == last) continue;
+      last = t.seq;
+      const int32_t nblk = (int32_t)cdiv64((int64_t)hist[t.seq] + incr[t.seq], dq_bs);
+      for (int32_t j = 0; j < nblk; j += kDqBlocksPerGroup)
+        P.dq.push_back({t.seq, j, std::min(nblk, j + kDqBlocksPerGroup), (int32_t)P.dq_blocks});
+      P.dq_blocks += nblk;
+      P.dq_mb = std::max(P.dq_mb, nblk);
+    }
+  }
+
   size_t off = 0;
   P.off_prefill = off;
   off = align256(off + P.prefill.size() * sizeof(Item));
@@ -299,6 +324,8 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + P.merges.size() * sizeof(Merge));
   P.off_wg = off;
   off = align256(off + P.wg_first.size() * sizeof(int32_t));
+  P.off_dq = off;
+  off = align256(off + P.dq.size() * sizeof(DqItem));
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -308,6 +335,15 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + (size_t)P.n_part_decode * kDecodeRows * d * sizeof(float));
   P.off_pl_dec = off;
   off = align256(off + (size_t)P.n_part_decode * kDecodeRows * sizeof(float));
+  if (!P.dq.empty()) {
+    P.off_dq_bt = off;
+    off = align256(off + (size_t)num_seqs * P.dq_mb * sizeof(int32_t));
+    const size_t cache_bytes = (size_t)P.dq_blocks * hkv * dq_bs * d * 2;
+    P.off_dq_k = off;
+    off = align256(off + cache_bytes);
+    P.off_dq_v = off;
+    off = align256(off + cache_bytes);
+  }
   P.total = off;
 }
 
@@ -402,7 +438,7 @@ pa_status stage_copy(const void *src, size_t bytes, void *dst_dev, hipStream_t s
 
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
-constexpr int kKinds = 4;
+constexpr int kKinds = 5;
 std::mutex g_time_mu;
 bool g_timing = false;
 struct TimedLaunch {
@@ -525,7 +561,8 @@ size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int
     return 0;
   Plan P;
   make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
+            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P,
+            prefill_dequant(cache) ? cache->block_size : 0);
   return std::max<size_t>(P.total, 256);
 }
 
@@ -549,7 +586,8 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
-  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, tile_rows, P);
+  const bool dq = prefill_dequant(cache);
+  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, tile_rows, P, dq ? cache->block_size : 0);
   if (!workspace) return fail(PA_ERR_NULL_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(PA_ERR_BAD_SHAPE, "workspace not 256-byte aligned");
   if (workspace_bytes < P.total)
@@ -562,6 +600,7 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   if (!P.merges.empty()) memcpy(host.data() + P.off_merges, P.merges.data(), P.merges.size() * sizeof(Merge));
   if (!P.wg_first.empty())
     memcpy(host.data() + P.off_wg, P.wg_first.data(), P.wg_first.size() * sizeof(int32_t));
+  if (!P.dq.empty()) memcpy(host.data() + P.off_dq, P.dq.data(), P.dq.size() * sizeof(DqItem));
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   st = stage_copy(host.data(), P.plan_bytes, ws, s);
@@ -588,12 +627,42 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   const int bs = cache->block_size;
   hipError_t e;
   if (!P.prefill.empty()) {
-    a.items = (const Item *)(ws + P.off_prefill);
-    a.part_o = (float *)(ws + P.off_po_pre);
-    a.part_lse = (float *)(ws + P.off_pl_pre);
-    a.wg_first = P.wg_first.empty() ? nullptr : (const int32_t *)(ws + P.off_wg);
+    AttnArgs ap = a;
+    bool pre_fp8 = fp8;
+    if (!P.dq.empty()) {
+      // E4M3 context -> bf16 copy; the prefill reads the copy through
+      // compact block tables (block j of sequence s at compact block base + j)
+      DequantArgs da{};
+      da.k = cache->k_cache;
+      da.v = cache->v_cache;
+      da.ks = cache->k_scale;
+      da.vs = cache->v_scale;
+      da.bt = block_tables;
+      da.max_blocks = max_blocks_per_seq;
+      da.hkv = hkv;
+      da.bs = bs;
+      da.d = d;
+      da.items = (const DqItem *)(ws + P.off_dq);
+      da.k_out = ws + P.off_dq_k;
+      da.v_out = ws + P.off_dq_v;
+      da.bt_out = (int32_t *)(ws + P.off_dq_bt);
+      da.mb_out = P.dq_mb;
+      e = timed(4, s, [&] { return launch_dequant(da, (int)P.dq.size(), s); });
+      if (e != hipSuccess) return hip_fail(e, "E4M3 context copy launch");
+      ap.c.k = da.k_out;
+      ap.c.v = da.v_out;
+      ap.c.ks = ap.c.vs = nullptr;
+      ap.c.num_blocks = (int32_t)P.dq_blocks;
+      ap.bt = da.bt_out;
+      ap.max_blocks = P.dq_mb;
+      pre_fp8 = false;
+    }
+    ap.items = (const Item *)(ws + P.off_prefill);
+    ap.part_o = (float *)(ws + P.off_po_pre);
+    ap.part_lse = (float *)(ws + P.off_pl_pre);
+    ap.wg_first = P.wg_first.empty() ? nullptr : (const int32_t *)(ws + P.off_wg);
     const int n = P.wg_first.empty() ? (int)P.prefill.size() : (int)P.wg_first.size() - 1;
-    e = timed(1, s, [&] { return launch_prefill(a, n, d, bs, fp8, s); });
+    e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, pre_fp8, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
   if (!P.decode.empty()) {

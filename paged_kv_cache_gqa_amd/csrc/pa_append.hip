@@ -56,6 +56,56 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// bf16 copy of E4M3 context for the prefill kernels: value = bf16(code *
+// scale), the product rounded in fp32, then to bf16, both nearest-even (every
+// code is exact in fp32).  A work-group converts blocks j0 .. j1-1 of one
+// sequence for all KV heads, 16 codes per thread and step, and writes the
+// compact block table entries of those blocks.
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  const DqItem it = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks;
+  for (int j = it.j0 + tid; j < it.j1; j += 256) a.bt_out[(int64_t)it.seq * a.mb_out + j] = it.base + j;
+  const int cpb = a.bs * a.d / 16;  // 16-byte chunks of codes per (block, head)
+  const int64_t total = (int64_t)(it.j1 - it.j0) * a.hkv * cpb;
+  for (int64_t c = tid; c < total; c += 256) {
+    const int ch = (int)(c % cpb);
+    const int64_t jh = c / cpb;
+    const int h = (int)(jh % a.hkv);
+    const int j = it.j0 + (int)(jh / a.hkv);
+    const int64_t blk = btr[j];
+    const int64_t src = (blk * a.hkv + h) * a.bs * a.d + ch * 16;                  // code offset
+    const int64_t dst = ((int64_t)(it.base + j) * a.hkv + h) * a.bs * a.d + ch * 16;  // element offset
+    const float sc[2] = {a.ks[blk * a.hkv + h], a.vs[blk * a.hkv + h]};
+#pragma unroll
+    for (int kv = 0; kv < 2; kv++) {
+      const uint4 w = gload16_nt((const unsigned char *)(kv ? a.v : a.k) + src);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      uint32_t o[8];
+      auto pack = [&](float x, float y) {
+        const __bf16 lo = (__bf16)(x * sc[kv]), hi = (__bf16)(y * sc[kv]);
+        return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      };
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const auto f_lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);  // codes 4i, 4i+1
+        const auto f_hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);   // codes 4i+2, 4i+3
+        o[2 * i] = pack(f_lo[0], f_lo[1]);
+        o[2 * i + 1] = pack(f_hi[0], f_hi[1]);
+      }
+      unsigned char *dp = (unsigned char *)(kv ? a.v_out : a.k_out) + dst * 2;
+      *(uint4 *)dp = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4 *)(dp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_kernel, dim3(n_items), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // Raw gather of one sequence through its block-table row ([V1Sched]
 // "Scheduler.schedule — 记账与状态": a request's KV lives in the blocks its
 // id list names, in order).  One thread per 16-byte chunk of a row.

@@ -104,6 +104,30 @@ struct GatherArgs {
   int32_t row_bytes;      // d * element bytes
 };
 
+// E4M3 caches feed the bf16 prefill kernels through a bf16 copy of each
+// prefilled sequence's context: blocks j0 .. j1-1 of sequence seq go to
+// compact blocks base + j0 .. base + j1-1 (block j of the sequence at compact
+// block base + j, all KV heads).
+struct DqItem {
+  int32_t seq, j0, j1, base;
+};
+static_assert(sizeof(DqItem) == 16, "DqItem layout");
+
+struct DequantArgs {
+  const void *k;            // E4M3 codes [num_blocks][hkv][bs][d]
+  const void *v;
+  const float *ks;          // [num_blocks][hkv]
+  const float *vs;
+  const int32_t *bt;        // the caller's block tables [num_seqs][max_blocks]
+  int32_t max_blocks;
+  int32_t hkv, bs, d;
+  const DqItem *items;
+  void *k_out;              // bf16 [compact blocks][hkv][bs][d]
+  void *v_out;
+  int32_t *bt_out;          // compact block tables [num_seqs][mb_out]
+  int32_t mb_out;
+};
+
 constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
 #ifndef PA_WIDE_TILE
 #define PA_WIDE_TILE 1
@@ -123,5 +147,6 @@ hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8
 hipError_t launch_merge(const MergeArgs &a, int n_merges, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
 
 }  // namespace pa
