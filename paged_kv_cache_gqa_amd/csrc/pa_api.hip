@@ -210,13 +210,24 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
     by_range[pc.range].push_back({t.seq, pc.unit / (int32_t)pre.size(), t.row0, t.pos0, t.nq,
                                   pc.lo * kKeyTile, std::min(t.keys, pc.hi * kKeyTile), part});
   }
-  // Within a range, pieces that start at a chunk boundary run first: every
-  // work-group then starts its first piece at the start of a chunk at the
-  // same moment, and the work-groups on one chunk stay in step.
-  for (auto &v : by_range)
-    std::stable_sort(v.begin(), v.end(), [&](const Item &x, const Item &y) {
-      return (x.kv_lo % (C * kKeyTile) == 0) > (y.kv_lo % (C * kKeyTile) == 0);
-    });
+  // Within a range, runs of pieces that start at a chunk boundary come first
+  // (a run: consecutive pieces of one (tile, head) continuing each other,
+  // which the item length cap splits a chunk into), in key order: every
+  // work-group then starts at the start of a chunk at the same moment, and
+  // the work-groups on one chunk walk it in step.
+  for (auto &v : by_range) {
+    std::vector<char> aligned(v.size(), 0);
+    for (size_t i = 0; i < v.size(); i++) {
+      const Item &x = v[i];
+      const bool cont = i > 0 && v[i - 1].kvh == x.kvh && v[i - 1].row0 == x.row0 &&
+                        v[i - 1].kv_hi == x.kv_lo;
+      aligned[i] = x.kv_lo % (C * kKeyTile) == 0 || (cont && aligned[i - 1]);
+    }
+    std::vector<Item> first, rest;
+    for (size_t i = 0; i < v.size(); i++) (aligned[i] ? first : rest).push_back(v[i]);
+    first.insert(first.end(), rest.begin(), rest.end());
+    v.swap(first);
+  }
   P.wg_first.assign(nwg + 1, 0);
   for (int32_t w = 0; w < nwg; w++) {
     const int32_t rr = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;

@@ -387,6 +387,8 @@ __device__ __forceinline__ void wg_barrier() {
 #endif
 constexpr int kPpTileBytes = kKeyTile * 128 * 2;  // one 64-key K (or V) tile, 16 KB
 constexpr int kPpStages = 4;                        // K+V stages in the LDS ring
+constexpr int kPpMaxItemKeys = 65536;               // keys per item (the planner's cap when this kernel runs)
+static_assert(PA_WIDE_TILE || kMaxDmaItemKeys <= kPpMaxItemKeys, "256-row kernel item cap");
 
 // One work item of the 256-row kernel; the caller separates consecutive
 // items by a work-group barrier.
@@ -720,7 +722,7 @@ __device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 
 template <int BS>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kPpStages * 2 * kPpTileBytes];
-  __shared__ int bt_lds[kMaxDmaItemKeys / BS + 2];
+  __shared__ int bt_lds[kPpMaxItemKeys / BS + 2];
   const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
   const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
   for (int i = first; i < last; i++) {
@@ -748,7 +750,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
 constexpr int kW48Step = 32;                        // keys per step
 constexpr int kW48TileBytes = kW48Step * 128 * 2;  // K (or V) of one step, 8 KB
 #ifndef PA_W48_STAGES
-#define PA_W48_STAGES 8
+#define PA_W48_STAGES 4
 #endif
 constexpr int kW48Stages = PA_W48_STAGES;
 // PA_W48_BARRIERS: work-group barriers per key step (2: strict alternation of

@@ -136,7 +136,8 @@ constexpr int kPpTileRows = 256;   // query rows per tile of prefill_pp_kernel
 constexpr int kW48TileRows = 384;  // query rows per tile of prefill_w48_kernel
 constexpr int kDmaTileRows = PA_WIDE_TILE ? kW48TileRows : kPpTileRows;  // bf16 KV, d 128
 constexpr int kPrefillRowsMax = 384;
-constexpr int kMaxDmaItemKeys = 65536;  // keys per item of the LDS-DMA prefill kernels (block ids staged in LDS)
+// keys per item of the LDS-DMA prefill kernels (their block ids are staged in LDS)
+constexpr int kMaxDmaItemKeys = PA_WIDE_TILE ? 131072 : 65536;
 constexpr int kMaxDecItemKeys = 32768;  // keys per decode item (block ids staged in LDS)
 constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
