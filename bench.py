@@ -12,8 +12,13 @@ layer, 32 q / 8 KV heads, head_dim 128, block 16, bf16: 45,700 cached tokens,
 (4 * d * Hq flops per unmasked (query, key) pair) over the whole step.  Also
 measured in the same run and reported as sub-objects: batched decode (64
 sessions, lognormal contexts with median 142K) in KV GB/s, and incremental
-prefill at 128K history.  The oracle's CPU rate on a bounded sample of the
-headline workload is reported as `cpu_baseline`.
+prefill at 128K history.  Unless --no-reports, `reports` carries the other
+workloads of the same path, each timed the same way: initial prefill of
+45,700 tokens, the 128K history with 4,096 new tokens, a mixed step (4
+incremental prefills + 48 decodes, 8 of them over a shared 10,000-token
+prefix), the 1M-token E4M3 history (incremental prefill of 4,096 tokens and a
+decode step at 1,048,576), and kv_append bandwidth.  The oracle's CPU rate on
+a bounded sample of the headline workload is reported as `cpu_baseline`.
 
 Prints one JSON line.
 """
@@ -116,6 +121,107 @@ class Runner:
             if cnt:
                 kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step
         return ms, kern
+
+
+def _kern(kern):
+    return {k: round(v[0], 4) for k, v in kern.items()}
+
+
+def report_prefill(pa, torch, spec, dev, steps, warmup, label):
+    r = Runner(pa, torch, spec, dev)
+    ms, kern = r.timed(steps, warmup)
+    fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
+    k_ms = kern["prefill"][0] * kern["prefill"][1]
+    d = {"workload": label, "ms_per_step": round(ms, 4),
+         "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+         "tokens_per_s": round(spec.total_q / (ms * 1e-3), 1),
+         "kernels_ms": _kern(kern),
+         "roofline": {"bound": "mfma", "achieved": round(fl / (k_ms * 1e-3) / 1e12, 2),
+                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(fl / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "kernel": "prefill_w48_kernel<%d>" % spec.block_size}}
+    del r
+    torch.cuda.empty_cache()
+    return d
+
+
+def report_decode(pa, torch, spec, dev, steps, warmup, label):
+    r = Runner(pa, torch, spec, dev)
+    ms, kern = r.timed(steps, warmup)
+    byts = decode_bytes(spec)
+    k_ms = kern["decode"][0] * kern["decode"][1]
+    d = {"workload": label, "ms_per_step": round(ms, 4),
+         "GB/s": round(byts / (ms * 1e-3) / 1e9, 1),
+         "tokens_per_s": round(spec.total_q / (ms * 1e-3), 1),
+         "kernels_ms": _kern(kern),
+         "roofline": {"bound": "hbm", "achieved": round(byts / (k_ms * 1e-3) / 1e9, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "algorithmic_bytes": int(byts)}}
+    del r
+    torch.cuda.empty_cache()
+    return d
+
+
+def report_mixed(pa, torch, spec, dev, steps, warmup, label):
+    """One call holding 4 incremental prefills and 48 decodes: the prefill
+    part in TFLOP/s over its kernel, the decode part in GB/s over its kernel
+    (the shared prefix's blocks counted once)."""
+    r = Runner(pa, torch, spec, dev)
+    ms, kern = r.timed(steps, warmup)
+    pre = [i for i, n in enumerate(spec.incr) if n > 1]
+    dec = [i for i, n in enumerate(spec.incr) if n == 1]
+    fl = prefill_flops([spec.hist[i] for i in pre], [spec.incr[i] for i in pre],
+                       spec.num_q_heads, spec.head_dim)
+    kvb = kv_bytes_per_token(spec)
+    shared = [i for i in dec if i in spec.shared_seqs]
+    uniq = sum(spec.hist[i] + 1 for i in dec) - max(0, len(shared) - 1) * spec.shared_prefix_tokens
+    byts = uniq * kvb + 2 * len(dec) * spec.num_q_heads * spec.head_dim * 2
+    p_ms = kern["prefill"][0] * kern["prefill"][1]
+    d_ms = kern["decode"][0] * kern["decode"][1]
+    d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
+         "prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
+         "prefill_frac": round(fl / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+         "decode_GB/s_kernel": round(byts / (d_ms * 1e-3) / 1e9, 1),
+         "decode_frac": round(byts / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "decode_unique_bytes": int(byts)}
+    del r
+    torch.cuda.empty_cache()
+    return d
+
+
+def report_append(pa, torch, dev, tokens, steps, label):
+    """kv_append of `tokens` bf16 tokens (8 KV heads, d 128, block 16) into
+    a pool of exactly those slots, in a seeded permuted block order."""
+    import workloads as W
+    hkv, d, bs = 8, 128, 16
+    nb = (tokens + bs - 1) // bs
+    kc = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    cache = pa.make_cache(kc, vc)
+    k_new = W.randn_bf16((tokens, hkv, d), dev, 90, 3)
+    v_new = W.randn_bf16((tokens, hkv, d), dev, 90, 4)
+    perm = torch.from_numpy(np.random.default_rng(90).permutation(nb).astype(np.int64)).to(dev)
+    pos = torch.arange(tokens, device=dev, dtype=torch.int64)
+    slots = perm[pos // bs] * bs + pos % bs
+    s = torch.cuda.current_stream()
+    pa.kv_append(cache, k_new, v_new, slots, stream=s)
+    torch.cuda.synchronize()
+    pa.pa_timing_read(0)
+    pa.pa_timing_enable(True)
+    for _ in range(steps):
+        pa.kv_append(cache, k_new, v_new, slots, stream=s)
+    torch.cuda.synchronize()
+    pa.pa_timing_enable(False)
+    tot, cnt = pa.pa_timing_read(0)
+    k_ms = tot / cnt
+    byts = 2 * tokens * hkv * d * 2 * 2 + tokens * 8   # K and V read and written, slots read
+    out = {"workload": label, "tokens": tokens, "kernel_ms": round(k_ms, 4),
+           "GB/s": round(byts / (k_ms * 1e-3) / 1e9, 1),
+           "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byts)}
+    del kc, vc, k_new, v_new
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_cpu_baseline(spec, budget_s):
@@ -277,6 +383,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-reports", action="store_true",
+                    help="skip the other workloads (initial prefill, 128K x 4,096, mixed step, "
+                         "1M-token E4M3 prefill and decode, kv_append bandwidth)")
     ap.add_argument("--no-128k", action="store_true",
                     help="skip the 128K-history incremental prefill (same kernel as the headline)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -402,6 +511,31 @@ def main():
         del r
         torch.cuda.empty_cache()
 
+    if not args.no_extra and not args.no_reports:
+        rs, rw = max(3, args.steps // 2), max(1, args.warmup)
+        rep = {}
+        rep["initial_prefill"] = report_prefill(
+            pa, torch, W.initial(), dev, max(3, args.steps // 4), rw,
+            "initial_prefill: 45,700 tokens, no history, 32 q / 8 KV heads, d 128, block 16, bf16")
+        rep["incremental_128k_4096"] = report_prefill(
+            pa, torch, W.incremental(131_072, 4_096, "incremental_128k_4096"), dev, rs, rw,
+            "incremental_prefill: 131,072 cached + 4,096 new tokens, 32 q / 8 KV, d 128, bf16")
+        rep["mixed_step"] = report_mixed(
+            pa, torch, W.mixed(), dev, rs, rw,
+            "mixed: 4 incremental prefills (lognormal histories, median 100K) + 48 decodes "
+            "(8 over a shared 10,000-token prefix), 32 q / 8 KV, d 128, block 16, bf16, one call")
+        rep["long_context_prefill_e4m3"] = report_prefill(
+            pa, torch, W.long_context(), dev, max(3, args.steps // 4), rw,
+            "long_context: 1,044,480 cached + 4,096 new tokens, E4M3 KV with per-(block, head) "
+            "scales, block 64, 32 q / 8 KV, d 128")
+        rep["long_context_decode_e4m3"] = report_decode(
+            pa, torch, W.long_context(1_048_575, 1), dev, args.steps, rw,
+            "long_context decode step at context 1,048,576 (the first of 256), E4M3 KV, block 64")
+        rep["kv_append_45700"] = report_append(pa, torch, dev, 45_700, 20,
+                                               "kv_append of 45,700 bf16 tokens (initial prefill)")
+        rep["kv_append_1m"] = report_append(pa, torch, dev, 1_048_576, 5,
+                                            "kv_append of 1,048,576 bf16 tokens")
+        line["reports"] = rep
     if not args.no_cpu:
         line["cpu_baseline"] = run_cpu_baseline(spec, args.cpu_budget)
     print(json.dumps(line), flush=True)
