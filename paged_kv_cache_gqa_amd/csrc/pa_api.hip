@@ -389,7 +389,7 @@ pa_status check_lengths(const int32_t *hist, const int32_t *incr, int32_t num_se
 
 // ---------------------------------------------------------------------------
 // Pinned staging ring for work lists (one per device).  A slot is reused only
-// after the copy that last read it has completed.
+// after the kernel that last read it has completed.
 struct StageSlot {
   void *host = nullptr;
   size_t cap = 0;
@@ -439,8 +439,13 @@ pa_status stage_copy(const void *src, size_t bytes, void *dst_dev, hipStream_t s
     sl.cap = cap;
   }
   memcpy(sl.host, src, bytes);
-  e = hipMemcpyAsync(dst_dev, sl.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  // a kernel on the call's stream reads the pinned slot (no copy engine, so
+  // no hand-off between engines before the attention kernels)
+  void *src_dev = nullptr;
+  e = hipHostGetDevicePointer(&src_dev, sl.host, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer(staging)");
+  e = launch_stage(src_dev, dst_dev, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list copy launch");
   e = hipEventRecord(sl.done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
   sl.pending = true;

@@ -100,6 +100,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   }
 }
 
+// Work-list copy from a pinned host buffer into the workspace (bytes is a
+// multiple of 16, both addresses 16-byte aligned).
+__global__ __launch_bounds__(256) void stage_kernel(const uint4 *src, uint4 *dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 16 != 0 || (uintptr_t)src_host % 16 != 0 || (uintptr_t)dst % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(stage_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (const uint4 *)src_host,
+                     (uint4 *)dst, n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3(n_items), dim3(256), 0, s, a);

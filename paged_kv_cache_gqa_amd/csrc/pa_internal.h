@@ -149,5 +149,6 @@ hipError_t launch_merge(const MergeArgs &a, int n_merges, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
+hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s);
 
 }  // namespace pa
