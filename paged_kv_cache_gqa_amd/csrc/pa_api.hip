@@ -326,6 +326,10 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
     }
   }
 
+  // merges with many parts last (they take the one-row-per-work-group kernel)
+  std::stable_partition(P.merges.begin(), P.merges.end(),
+                        [](const Merge &m) { return m.nparts <= kMergeSerialParts; });
+
   size_t off = 0;
   P.off_prefill = off;
   off = align256(off + P.prefill.size() * sizeof(Item));
@@ -703,8 +707,13 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
     m.group = group;
     m.lg = a.lg;
     m.d = d;
-    const int n = (int)P.merges.size();
-    e = timed(3, s, [&] { return launch_merge(m, n, s); });
+    int n_few = 0, many_rows = 0;
+    for (const Merge &mg : P.merges) {
+      if (mg.nparts <= kMergeSerialParts) n_few++;
+      else many_rows = std::max(many_rows, mg.nq * group);
+    }
+    const int n_many = (int)P.merges.size() - n_few;
+    e = timed(3, s, [&] { return launch_merge(m, n_few, n_many, many_rows, s); });
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return PA_OK;

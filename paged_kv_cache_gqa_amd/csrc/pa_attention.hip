@@ -1819,7 +1819,6 @@ __global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
 // loads that do not wait on each other.
 constexpr int kMergeRows = 64;
 constexpr int kMergeWeights = 8192;
-constexpr int kMergeSerialParts = 16;  // up to this many parts, one thread per row weighs them
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -1937,6 +1936,79 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
+// Merges of many parts (more than kMergeSerialParts; long decodes split
+// over many items): one work-group per (task, row).  The 256 threads weigh the
+// parts together, then 8 groups of 32 threads each sum every eighth part over
+// the row's d (4 consecutive d per thread), combined through LDS.
+__global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a, int first) {
+  const Merge mt = a.merges[first + blockIdx.x];
+  const int rows = mt.nq << a.lg;
+  const int r = blockIdx.y;
+  if (r >= rows) return;
+  const float *po = mt.is_decode ? a.part_o_decode : a.part_o_prefill;
+  const float *pl = mt.is_decode ? a.part_lse_decode : a.part_lse_prefill;
+  const int rpp = mt.rows_per_part;
+  const int np = mt.nparts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sm_w[kMergeWeights];
+  __shared__ float red[4];
+  __shared__ f32x4 ored[8][32];
+  const float *lrow = pl + (int64_t)mt.part0 * rpp + r;
+  float M = -INFINITY;
+  for (int i = tid; i < np; i += 256) M = fmaxf(M, lrow[(int64_t)i * rpp]);
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  auto weight = [&](int i) {
+    const float li = lrow[(int64_t)i * rpp];
+    return (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
+  };
+  float S = 0.f;
+  for (int i = tid; i < np; i += 256) {
+    const float w = weight(i);
+    S += w;
+    if (i < kMergeWeights) sm_w[i] = w;
+  }
+  S = wave_sum(S);
+  if (lane == 0) red[wave] = S;
+  __syncthreads();
+  S = red[0] + red[1] + red[2] + red[3];
+  const int d = a.d, d4 = d / 4;
+  const int u = tid & 31, pg = tid >> 5;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  if (u < d4) {
+    const float *orow = po + ((int64_t)mt.part0 * rpp + r) * d + 4 * u;
+    int i = pg;
+    for (; i + 24 < np; i += 32) {
+      f32x4 v[4];
+      float w[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) v[k] = *(const f32x4 *)(orow + (int64_t)(i + 8 * k) * rpp * d);
+#pragma unroll
+      for (int k = 0; k < 4; k++) w[k] = i + 8 * k < kMergeWeights ? sm_w[i + 8 * k] : weight(i + 8 * k);
+#pragma unroll
+      for (int k = 0; k < 4; k++) O += w[k] * v[k];
+    }
+    for (; i < np; i += 8) O += (i < kMergeWeights ? sm_w[i] : weight(i)) * *(const f32x4 *)(orow + (int64_t)i * rpp * d);
+  }
+  ored[pg][u] = O;
+  __syncthreads();
+  const int64_t orow_out = (int64_t)(mt.row0 + (r >> a.lg)) * a.hq + mt.kvh * a.group + (r & (a.group - 1));
+  if (tid < d4) {
+    f32x4 T = ored[0][tid];
+#pragma unroll
+    for (int g = 1; g < 8; g++) T += ored[g][tid];
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    bf16x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = (__bf16)(T[k] * inv);
+    *(bf16x4 *)((__bf16 *)a.out + orow_out * d + 4 * tid) = v;
+  }
+  if (tid == 0 && a.lse_out) a.lse_out[orow_out] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+}
+
 // =============================================================================
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
@@ -1991,9 +2063,9 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, bool fp8, hipS
   if (n <= 0) return hipSuccess;
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
-hipError_t launch_merge(const MergeArgs &a, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n, kPrefillRowsMax / kMergeRows), dim3(256), 0, s, a);
+hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s) {
+  if (n_few > 0) hipLaunchKernelGGL(merge_kernel, dim3(n_few, kPrefillRowsMax / kMergeRows), dim3(256), 0, s, a);
+  if (n_many > 0) hipLaunchKernelGGL(merge_many_kernel, dim3(n_many, many_rows), dim3(256), 0, s, a, n_few);
   return hipGetLastError();
 }
 

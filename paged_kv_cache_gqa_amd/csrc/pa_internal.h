@@ -145,7 +145,10 @@ constexpr int kKeyTile = 64;       // keys per inner-loop tile
 // Launchers (defined next to their kernels).
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
-hipError_t launch_merge(const MergeArgs &a, int n_merges, hipStream_t s);
+// merges [0, n_few) have at most kMergeSerialParts parts, [n_few, n_few +
+// n_many) more, with at most many_rows rows each
+hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
+constexpr int kMergeSerialParts = 16;
 hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
