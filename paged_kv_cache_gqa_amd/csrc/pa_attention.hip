@@ -1840,17 +1840,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float *po = mt.is_decode ? a.part_o_decode : a.part_o_prefill;
   const float *pl = mt.is_decode ? a.part_lse_decode : a.part_lse_prefill;
   const int rpp = mt.rows_per_part;
-  const int np = mt.nparts;
-  const bool cached = nr * np <= kMergeWeights;
-  __shared__ float sm_w[kMergeWeights];
-  __shared__ float sm_max[kMergeRows], sm_inv[kMergeRows];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int np = mt.nparts;  // <= kMergeSerialParts
+  __shared__ float sm_w[kMergeRows * kMergeSerialParts];
+  __shared__ float sm_inv[kMergeRows];
   auto row_out = [&](int r) {
     const int rr = rb + r;
     return (int64_t)(mt.row0 + (rr >> a.lg)) * a.hq + mt.kvh * a.group + (rr & (a.group - 1));
   };
-  if (np <= kMergeSerialParts) {
-    // few parts (the common case): one thread per row
+  {  // one thread per row weighs the parts
     const int r = threadIdx.x;
     if (r < nr) {
       const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
@@ -1864,75 +1861,47 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       for (int i = 0; i < np; i++) {
         const float w = (M > -INFINITY && li[i] > -INFINITY) ? fast_exp2(li[i] - M) : 0.f;
         S += w;
-        sm_w[r * np + i] = w;
+        sm_w[r * kMergeSerialParts + i] = w;
       }
-      sm_max[r] = M;
       sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
       if (a.lse_out) a.lse_out[row_out(r)] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
     }
-  } else {
-    for (int r = wave; r < nr; r += 4) {
-      const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
-      float M = -INFINITY;
-      for (int i = lane; i < np; i += 64) M = fmaxf(M, lrow[(int64_t)i * rpp]);
-      M = wave_max(M);
-      float S = 0.f;
-      for (int i = lane; i < np; i += 64) {
-        const float li = lrow[(int64_t)i * rpp];
-        const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
-        S += w;
-        if (cached) sm_w[r * np + i] = w;
-      }
-      S = wave_sum(S);
-      if (lane == 0) {
-        sm_max[r] = M;
-        sm_inv[r] = S > 0.f ? 1.f / S : 0.f;
-        if (a.lse_out) a.lse_out[row_out(r)] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
-      }
-    }
   }
   __syncthreads();
+  // each thread: four consecutive d of a row, two such units at a time so
+  // that their parts' loads are in flight together
   const int d = a.d, d4 = d / 4;
-  for (int idx = threadIdx.x; idx < nr * d4; idx += blockDim.x) {
+  const int n_units = nr * d4;
+  auto unit = [&](int idx, f32x4 &O) {
     const int r = idx / d4, e = (idx % d4) * 4;
-    const float M = sm_max[r];
     const float *orow = po + ((int64_t)mt.part0 * rpp + rb + r) * d + e;
-    const float *lrow = pl + (int64_t)mt.part0 * rpp + rb + r;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    const float *w = sm_w + r * kMergeSerialParts;
+    O = f32x4{0.f, 0.f, 0.f, 0.f};
     int i = 0;
     for (; i + 4 <= np; i += 4) {
       f32x4 v[4];
-      float w[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) v[k] = *(const f32x4 *)(orow + (int64_t)(i + k) * rpp * d);
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        if (cached) {
-          w[k] = sm_w[r * np + i + k];
-        } else {
-          const float li = lrow[(int64_t)(i + k) * rpp];
-          w[k] = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; k++) O += w[k] * v[k];
+      for (int k = 0; k < 4; k++) O += w[i + k] * v[k];
     }
-    for (; i < np; i++) {
-      const f32x4 v = *(const f32x4 *)(orow + (int64_t)i * rpp * d);
-      float w;
-      if (cached) {
-        w = sm_w[r * np + i];
-      } else {
-        const float li = lrow[(int64_t)i * rpp];
-        w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
-      }
-      O += w * v;
-    }
+    for (; i < np; i++) O += w[i] * *(const f32x4 *)(orow + (int64_t)i * rpp * d);
+  };
+  auto store = [&](int idx, const f32x4 &O) {
+    const int r = idx / d4, e = (idx % d4) * 4;
     const float inv = sm_inv[r];
     bf16x4 v;
 #pragma unroll
     for (int k = 0; k < 4; k++) v[k] = (__bf16)(O[k] * inv);
     *(bf16x4 *)((__bf16 *)a.out + row_out(r) * d + e) = v;
+  };
+  for (int idx = threadIdx.x; idx < n_units; idx += 2 * blockDim.x) {
+    const int idx2 = idx + blockDim.x;
+    f32x4 O, O2;
+    unit(idx, O);
+    if (idx2 < n_units) unit(idx2, O2);
+    store(idx, O);
+    if (idx2 < n_units) store(idx2, O2);
   }
 }
 
