@@ -155,6 +155,10 @@ constexpr int32_t kDqBlocksPerGroup = 16;  // cache blocks per work-group of the
 #define PA_GROUP_PIECES 0
 #endif
 constexpr int kGroupPieces = PA_GROUP_PIECES;
+#ifndef PA_PLAN_LPT
+#define PA_PLAN_LPT 1
+#endif
+constexpr bool kPlanLpt = PA_PLAN_LPT;
 
 void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, Plan &P) {
   std::vector<int32_t> pre;  // prefill tiles
@@ -183,7 +187,40 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   constexpr int32_t kMaxSegSteps = kMaxDmaItemKeys / kKeyTile;
   int64_t pos = 0;
   int32_t r = 0;
-  for (int32_t kvh = 0; kvh < hkv; kvh++)
+  // Many tiles per KV head (an initial prefill: tiles of every length up to
+  // the context): whole (tile, head) units instead, longest first, each to
+  // the least loaded range of the XCD that holds the head (greedy LPT: the
+  // loads end within the shortest tiles' length of each other).  The XCD's
+  // work-groups then start tiles of nearly equal length at key 0 together,
+  // round after round, and share K/V in L2; no tile is split (no partials)
+  // unless it exceeds the item cap.
+  constexpr int kXcds = 8;
+  const int32_t per_xcd = nwg / kXcds;
+  const bool lpt = kPlanLpt && nwg % kXcds == 0 && hkv % kXcds == 0 &&
+                   (int64_t)pre.size() * (hkv / kXcds) >= 8 * per_xcd;
+  if (lpt) {
+    std::vector<int32_t> order(pre.size());
+    for (size_t k = 0; k < pre.size(); k++) order[k] = (int32_t)k;
+    auto steps_of = [&](int32_t k) { return (int32_t)cdiv64(tiles[pre[k]].keys, kKeyTile); };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return steps_of(x) > steps_of(y); });
+    for (int32_t x = 0; x < kXcds; x++) {
+      std::vector<int64_t> load(per_xcd, 0);
+      for (int32_t kvh = x; kvh < hkv; kvh += kXcds)
+        for (int32_t k : order) {
+          int32_t j = 0;
+          for (int32_t q = 1; q < per_xcd; q++)
+            if (load[q] < load[j]) j = q;
+          const int32_t steps = steps_of(k);
+          for (int32_t lo = 0; lo < steps;) {
+            const int32_t hi = std::min(steps, lo + kMaxSegSteps);
+            pieces.push_back({kvh * (int32_t)pre.size() + k, lo, hi, x * per_xcd + j});
+            lo = hi;
+          }
+          load[j] += steps;
+        }
+    }
+  }
+  for (int32_t kvh = 0; kvh < (lpt ? 0 : hkv); kvh++)
     for (int32_t c0 = 0; c0 < max_steps; c0 += C)
       for (size_t k = 0; k < pre.size(); k++) {
         const int32_t steps = (int32_t)cdiv64(tiles[pre[k]].keys, kKeyTile);
