@@ -1182,7 +1182,7 @@ __global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
 // The four waves of a decode work-group hold softmax states (m in log2
 // units, per-lane partial l, o[d-block]) over disjoint keys of one item's
 // 16 rows; combine them through LDS and write the rows (or the item's partial).
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it, unsigned char *smem_raw,
                                                float m, float l, const f32x4 (&o)[D / 16]) {
   constexpr int ND = D / 16;
@@ -1193,9 +1193,9 @@ __device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it
   l = xor16_sum(l);
   l = xor32_sum(l);
   __syncthreads();
-  float *red_o = (float *)smem_raw;                  // [4][16][D]
-  float *red_m = red_o + 4 * 16 * D;                 // [4][16]
-  float *red_l = red_m + 4 * 16;                     // [4][16]
+  float *red_o = (float *)smem_raw;                  // [NW][16][D]
+  float *red_m = red_o + NW * 16 * D;                // [NW][16]
+  float *red_l = red_m + NW * 16;                    // [NW][16]
 #pragma unroll
   for (int db = 0; db < ND; db++)
     *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
@@ -1205,15 +1205,15 @@ __device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it
   }
   __syncthreads();
   const int rows = it.nq << a.lg;
-  for (int idx = tid; idx < 16 * D; idx += 256) {
+  for (int idx = tid; idx < 16 * D; idx += 64 * NW) {
     const int cn = idx / D, e = idx % D;
     if (cn >= rows) continue;
     float M = red_m[cn];
 #pragma unroll
-    for (int w = 1; w < 4; w++) M = fmaxf(M, red_m[w * 16 + cn]);
+    for (int w = 1; w < NW; w++) M = fmaxf(M, red_m[w * 16 + cn]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
+    for (int w = 0; w < NW; w++) {
       const float sc = fast_exp2(red_m[w * 16 + cn] - M);
       L += sc * red_l[w * 16 + cn];
       O += sc * red_o[(w * 16 + cn) * D + e];
@@ -1631,15 +1631,15 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
 constexpr int kDec8Slice = 32;                        // keys per wave step
 constexpr int kDec8SliceBytes = kDec8Slice * 128;     // K (or V) codes of one slice, 4 KB
 
-template <int BS>
-__global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;
   constexpr int ND = D / 16;
   constexpr int SB = kDec8SliceBytes;
-  constexpr int NST = kDecStages;
   static_assert(BS == 16 || BS == 64, "block size");
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * NST * 2 * SB];
+  static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
@@ -1675,13 +1675,13 @@ __global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
   const unsigned char *kc = (const unsigned char *)a.c.k;
   const unsigned char *vc = (const unsigned char *)a.c.v;
   const int n_slices = (kv_hi - kv_lo + kDec8Slice - 1) / kDec8Slice;
-  const int nw = n_slices > wave ? (n_slices - wave + 3) / 4 : 0;  // this wave's slices
+  const int nw = n_slices > wave ? (n_slices - wave + NW - 1) / NW : 0;  // this wave's slices
   const int blk0 = kv_lo / BS;
   const int last_blk = (kv_hi - 1) / BS;
   const int lim = min(pos, kv_hi - 1);
   {  // the item's block ids into LDS (see the bf16 kernel)
     const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
-    for (int i = tid; i <= last_blk - blk0; i += 256) bt_lds[i] = btr[i];
+    for (int i = tid; i <= last_blk - blk0; i += 64 * NW) bt_lds[i] = btr[i];
   }
   PA_WAIT_VMCNT(0);
   __syncthreads();
@@ -1696,7 +1696,7 @@ __global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
   const uint32_t ring = smem_addr + wave * NST * 2 * SB;
   lds_u8 *ring_p = smem + wave * NST * 2 * SB;
 
-  auto slice_key = [&](int k) { return kv_lo + kDec8Slice * (wave + 4 * k); };
+  auto slice_key = [&](int k) { return kv_lo + kDec8Slice * (wave + NW * k); };
   auto block_at = [&](int key) {
     return __builtin_amdgcn_readfirstlane(bt_lds[min(key / BS, last_blk) - blk0]);
   };
@@ -1805,7 +1805,7 @@ __global__ __launch_bounds__(256, 1) void decode_dma_fp8_kernel(AttnArgs a) {
     compute(k);                    // requests slice k + NST into slice k's stage
   }
   PA_WAIT_VMCNT(0);
-  decode_combine<D>(a, it, smem_raw, m, l, o);
+  decode_combine<D, NW>(a, it, smem_raw, m, l, o);
 }
 
 // =============================================================================
@@ -1997,6 +1997,13 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 #ifndef PA_DECODE_DMA
 #define PA_DECODE_DMA 1
 #endif
+// E4M3 decode: waves per work-group and ring stages per wave
+#ifndef PA_DEC8_WAVES
+#define PA_DEC8_WAVES 8
+#endif
+#ifndef PA_DEC8_STAGES
+#define PA_DEC8_STAGES 2
+#endif
 template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
@@ -2004,7 +2011,7 @@ static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
     return hipGetLastError();
   }
   if constexpr (FP8 && D == 128 && PA_DECODE_DMA) {
-    hipLaunchKernelGGL((decode_dma_fp8_kernel<BS>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_dma_fp8_kernel<BS, PA_DEC8_WAVES, PA_DEC8_STAGES>), dim3(n), dim3(64 * PA_DEC8_WAVES), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_kernel<D, BS, FP8>), dim3(n), dim3(256), 0, s, a);
