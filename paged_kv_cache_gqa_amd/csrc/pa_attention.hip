@@ -1464,14 +1464,14 @@ constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4
 #endif
 constexpr int kDecStages = PA_DEC_STAGES;
 
-template <int BS>
-__global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;  // score MFMAs per slice
   constexpr int ND = D / 16;   // 16-wide d blocks of the output
   constexpr int SB = kDecSliceBytes;
-  constexpr int NST = kDecStages;
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * NST * 2 * SB];
+  static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
@@ -1507,14 +1507,14 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
   const unsigned char *kc = (const unsigned char *)a.c.k;
   const unsigned char *vc = (const unsigned char *)a.c.v;
   const int n_slices = (kv_hi - kv_lo + kDecSlice - 1) / kDecSlice;
-  const int nw = n_slices > wave ? (n_slices - wave + 3) / 4 : 0;  // this wave's slices
+  const int nw = n_slices > wave ? (n_slices - wave + NW - 1) / NW : 0;  // this wave's slices
   const int blk0 = kv_lo / BS;
   const int last_blk = (kv_hi - 1) / BS;
   const int lim = min(pos, kv_hi - 1);
   {  // stage the item's block ids in LDS: a global load inside the loop would
      // make the compiler wait for every outstanding load, the K/V stream too
     const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
-    for (int i = tid; i <= last_blk - blk0; i += 256) bt_lds[i] = btr[i];
+    for (int i = tid; i <= last_blk - blk0; i += 64 * NW) bt_lds[i] = btr[i];
   }
   // Q and the block ids have landed (stated explicitly: otherwise the
   // compiler, which does not see the stream's loads, places its wait for Q
@@ -1531,7 +1531,7 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
   const uint32_t ring = smem_addr + wave * NST * 2 * SB;
   lds_u8 *ring_p = smem + wave * NST * 2 * SB;
 
-  auto slice_key = [&](int k) { return kv_lo + kDecSlice * (wave + 4 * k); };
+  auto slice_key = [&](int k) { return kv_lo + kDecSlice * (wave + NW * k); };
   // slice k's 4 KB of K and of V into stage k % NST; slices past this wave's
   // share are requested with an empty buffer range (nothing is read), which
   // keeps the vmcnt accounting uniform
@@ -1610,7 +1610,7 @@ __global__ __launch_bounds__(256, 1) void decode_dma_kernel(AttnArgs a) {
   }
   PA_WAIT_VMCNT(0);
 
-  decode_combine<D>(a, it, smem_raw, m, l, o);
+  decode_combine<D, NW>(a, it, smem_raw, m, l, o);
 }
 
 // =============================================================================
@@ -1997,7 +1997,10 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 #ifndef PA_DECODE_DMA
 #define PA_DECODE_DMA 1
 #endif
-// E4M3 decode: waves per work-group and ring stages per wave
+// decode: waves per work-group and ring stages per wave (bf16, E4M3)
+#ifndef PA_DEC_WAVES
+#define PA_DEC_WAVES 4
+#endif
 #ifndef PA_DEC8_WAVES
 #define PA_DEC8_WAVES 8
 #endif
@@ -2007,7 +2010,7 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
-    hipLaunchKernelGGL((decode_dma_kernel<BS>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_dma_kernel<BS, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(n), dim3(64 * PA_DEC_WAVES), 0, s, a);
     return hipGetLastError();
   }
   if constexpr (FP8 && D == 128 && PA_DECODE_DMA) {
