@@ -144,7 +144,7 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
         seq, kvh, row0, pos0, nq, lo, hi, part = (int(x) for x in it)
         assert 0 <= kvh < hkv and nq >= 1 and nq * G <= (384 if d == 128 else 128)
         if d == 128 and nq * G > 16:  # LDS-staged block ids bound the item's span
-            assert hi - lo <= 65536
+            assert hi - lo <= 131072
         assert lo % 64 == 0 and hi > lo
         assert rowstart[seq] <= row0 and row0 + nq <= rowstart[seq] + incr[seq]
         assert pos0 == hist[seq] + (row0 - rowstart[seq])
@@ -222,3 +222,24 @@ def test_planner_splits_long_work_and_merges(palib):
     assert counts[3] <= 4 * 29 * 8 + 256
     items, counts = check_cover(palib, [1_048_575], [1], 32, 8, bs=64)
     assert counts[1] >= 256 and counts[2] == 8      # one long decode, split per head
+
+
+def test_planner_initial_prefill_whole_tiles(palib):
+    """Many tiles per KV head (an initial prefill): whole tiles go to the
+    work-groups of the head's XCD (work-group w on XCD w % 8), longest first,
+    with loads within 1% and no split tile."""
+    hist, incr = [0], [45_700]
+    items, counts = check_cover(palib, hist, incr, 32, 8)
+    assert counts[2] == 0 and counts[3] == 0          # no merges, no partial slots
+    c = cache(palib, num_kv_heads=8)
+    first = palib.pa_debug_plan_groups(hist, incr, 32, c)
+    assert len(first) - 1 == 256
+    pre = items[:counts[0]]
+    loads = []
+    for w in range(256):
+        its = pre[first[w]:first[w + 1]]
+        assert np.all(its[:, 1] == w % 8)             # the XCD's KV head
+        lens = its[:, 6] - its[:, 5]
+        assert np.all(np.diff(lens) <= 0)             # longest first
+        loads.append(int(lens.sum()))
+    assert (max(loads) - min(loads)) / max(loads) < 0.01, (min(loads), max(loads))
