@@ -99,13 +99,27 @@ class Runner:
                               self.ws, stream=self.stream)
 
     def timed(self, steps, warmup):
+        """(ms per step, {kernel: (ms per launch, launches per step)}).  After
+        the warm-up, a pass of the steps with HIP events around each launch
+        gives the kernel times; the step time comes from the timed pass that
+        follows, without per-launch events (they cost ~10 us per step)."""
         torch, pa = self.torch, self.pa
-        for _ in range(warmup):
+        # warm-up: W steps, and at least ~150 ms of them (the clock settles)
+        t0 = time.time()
+        n = 0
+        while n < warmup or time.time() - t0 < 0.15:
             self.step()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         for k in range(5):
             pa.pa_timing_read(k)  # drop anything recorded before
         pa.pa_timing_enable(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        pa.pa_timing_enable(False)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(self.stream)
@@ -113,7 +127,6 @@ class Runner:
             self.step()
         e1.record(self.stream)
         torch.cuda.synchronize()
-        pa.pa_timing_enable(False)
         ms = e0.elapsed_time(e1) / steps
         kern = {}
         for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "dequant")):
