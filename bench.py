@@ -158,7 +158,7 @@ def report_prefill(pa, torch, spec, dev, steps, warmup, label):
     return d
 
 
-def report_decode(pa, torch, spec, dev, steps, warmup, label):
+def report_decode(pa, torch, spec, dev, steps, warmup, label, kernel=None, traffic_key=None):
     r = Runner(pa, torch, spec, dev)
     ms, kern = r.timed(steps, warmup)
     byts = decode_bytes(spec)
@@ -170,7 +170,8 @@ def report_decode(pa, torch, spec, dev, steps, warmup, label):
          "roofline": {"bound": "hbm", "achieved": round(byts / (k_ms * 1e-3) / 1e9, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "algorithmic_bytes": int(byts)}}
+                      "traffic": measured_traffic(traffic_key) if traffic_key else None,
+                      "algorithmic_bytes": int(byts), "kernel": kernel}}
     del r
     torch.cuda.empty_cache()
     return d
@@ -281,9 +282,9 @@ def run_cpu_baseline(spec, budget_s):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILE_CMDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o kt -- "
-              "python3 REPO/bench.py --steps 10 --warmup 2 --no-cpu --no-128k",
-    "ktrace_incremental_128k": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace128 "
-                               "-o kt -- python3 REPO/bench.py --only incremental_128k --steps 10 --warmup 2",
+              "python3 REPO/bench.py --steps 10 --warmup 2 --no-cpu",
+    "ktrace_only": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace_{w} -o kt -- "
+                   "python3 REPO/bench.py --only {w} --steps 10 --warmup 2",
     "pmc": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/{w}_{counter} -o p -- "
            "python3 REPO/bench.py --only {w} --steps 2 --warmup 1",
     "copy": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/copy_{counter} -o p -- "
@@ -295,7 +296,20 @@ KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "void pa::prefill_w48_kernel<16>(pa::AttnArgs)"
-DECODE_KERNEL = "void pa::decode_dma_kernel<16>(pa::AttnArgs)"
+DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
+DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
+# (--only workload, kernel, summary name, key in TRAFFIC_FILE)
+PROFILED = [("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k", "prefill_incremental_bytes"),
+            ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k", "prefill_incremental_128k_bytes"),
+            ("decode", DECODE_KERNEL, "decode_batch_64x142k", "decode_batch_bytes"),
+            ("long_decode", DECODE_FP8_KERNEL, "decode_e4m3_context_1m", "decode_long_e4m3_bytes")]
+
+
+def only_spec(W, name):
+    """The workload of bench.py --only NAME."""
+    return {"incremental": lambda: W.incremental(), "decode": lambda: W.decode_batch(),
+            "incremental_128k": lambda: W.incremental(131_072, 2_700, "incremental_128k"),
+            "long_decode": lambda: W.long_context(1_048_575, 1)}[name]()
 
 
 def kernel_source_hash():
@@ -316,51 +330,49 @@ def _counter_means(path):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def _stats_table(fh, stats):
+    fh.write("  Name | Calls | AverageNs | MinNs | MaxNs\n")
+    for r in stats:
+        if r["Name"].startswith(("void pa::", "pa::")):
+            fh.write(f"  {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']}\n")
+
+
 def summarize_profiles(out):
     import csv
     import glob
-    def load_stats(sub):
-        return list(csv.DictReader(open(glob.glob(os.path.join(out, sub, "*kernel_stats.csv"))[0])))
+    def load(sub, what):
+        return list(csv.DictReader(open(glob.glob(os.path.join(out, sub, f"*{what}.csv"))[0])))
 
-    all_stats = {"ktrace": load_stats("ktrace"), "ktrace_incremental_128k": load_stats("ktrace128")}
     copy_f = _counter_means(os.path.join(out, "pmc", "copy_FETCH_SIZE"))["__amd_rocclr_copyBuffer"][0]
     copy_w = _counter_means(os.path.join(out, "pmc", "copy_WRITE_SIZE"))["__amd_rocclr_copyBuffer"][0]
     gib = float(1 << 30)
     f_scale, w_scale = gib / (copy_f * 1024), gib / (copy_w * 1024)
     src = kernel_source_hash()
     traffic = {}
-    for w, kname, unit_desc in (("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k"),
-                                ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k"),
-                                ("decode", DECODE_KERNEL, "decode_batch_64x142k")):
+    for w, kname, unit_desc, key in PROFILED:
         fetch, nf = _counter_means(os.path.join(out, "pmc", f"{w}_FETCH_SIZE"))[kname]
         write, nw = _counter_means(os.path.join(out, "pmc", f"{w}_WRITE_SIZE"))[kname]
         tb = fetch * 1024 * f_scale + write * 1024 * w_scale
-        traffic[w] = tb
-        tkey = "ktrace_incremental_128k" if w == "incremental_128k" else "ktrace"
-        stats = all_stats[tkey]
+        traffic[key] = tb
+        stats = load(f"ktrace_{w}", "kernel_stats")
         st = {r["Name"]: r for r in stats}[kname]
         kshort = kname.split("pa::")[1].split("(")[0].replace("<", "_").replace(">", "").replace(", ", "_")
         fn = os.path.join(ROOT, "profiles", f"{kshort}__{unit_desc}.txt")
         with open(fn, "w") as fh:
-            fh.write(f"Kernel: {kname}\nWorkload: {unit_desc}\n\n")
+            fh.write(f"Kernel: {kname}\nWorkload: {unit_desc} (bench.py --only {w})\n\n")
             fh.write("Commands (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root):\n")
-            fh.write("  " + PROFILE_CMDS[tkey] + "\n")
+            fh.write("  " + PROFILE_CMDS["ktrace_only"].format(w=w) + "\n")
             for c in ("FETCH_SIZE", "WRITE_SIZE"):
                 fh.write("  " + PROFILE_CMDS["pmc"].format(counter=c, w=w) + "\n")
                 fh.write("  " + PROFILE_CMDS["copy"].format(counter=c) + "\n")
             fh.write(f"  python3 REPO/bench.py --summarize-profiles OUT\n\n")
             fh.write("rocprofv3 --kernel-trace --stats (kernel_stats.csv rows of this run):\n")
-            fh.write("  Name | Calls | AverageNs | MinNs | MaxNs\n")
-            for r in stats:
-                if r["Name"].startswith(("void pa::", "pa::")):
-                    fh.write(f"  {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                             f"{r['MinNs']} | {r['MaxNs']}\n")
+            _stats_table(fh, stats)
             fh.write(f"\nThis kernel: average {float(st['AverageNs']) / 1e6:.4f} ms over {st['Calls']} calls\n")
-            sub = "ktrace128" if w == "incremental_128k" else "ktrace"
             durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-                    for r in csv.DictReader(open(glob.glob(os.path.join(out, sub, "*kernel_trace.csv"))[0]))
-                    if r["Kernel_Name"] == kname]
-            timed = durs[-10:]  # the 10 timed steps; the first calls are warm-up
+                    for r in load(f"ktrace_{w}", "kernel_trace") if r["Kernel_Name"] == kname]
+            timed = durs[-10:]  # the clean timed pass of 10 steps; earlier calls are warm-up and the instrumented pass
             fh.write(f"  timed steps only (last {len(timed)} dispatches, from kernel_trace.csv): "
                      f"average {sum(timed) / len(timed) / 1e6:.4f} ms\n\n")
             fh.write("HBM counters per dispatch (mean over dispatches of this kernel):\n")
@@ -369,12 +381,20 @@ def summarize_profiles(out):
             fh.write(f"  scale factors: read x{f_scale:.4f}, write x{w_scale:.4f}\n")
             fh.write(f"  HBM traffic per launch = {tb / 1e9:.4f} GB\n")
             fh.write(f"\nKernel sources sha256[:16] = {src}\n")
+    # every kernel of a default bench run (headline, decode, 128K and the reports)
+    with open(os.path.join(ROOT, "profiles", "all_kernels__bench_default_run.txt"), "w") as fh:
+        fh.write("All kernels of one bench.py run (headline, decode batch, 128K history and the\n"
+                 "reports: initial prefill, 128K x 4,096, mixed step, 1M-token E4M3 prefill and\n"
+                 "decode, kv_append); per-kernel averages mix the workloads that launch it.\n\n")
+        fh.write("Command (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root):\n")
+        fh.write("  " + PROFILE_CMDS["ktrace"] + "\n\n")
+        _stats_table(fh, load("ktrace", "kernel_stats"))
+        fh.write(f"\nKernel sources sha256[:16] = {src}\n")
     with open(TRAFFIC_FILE, "w") as fh:
         fh.write("# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE, scaled by a 1 GiB copy\n")
         fh.write(f"source_hash={src}\n")
-        fh.write(f"prefill_incremental_bytes={traffic['incremental']:.0f}\n")
-        fh.write(f"prefill_incremental_128k_bytes={traffic['incremental_128k']:.0f}\n")
-        fh.write(f"decode_batch_bytes={traffic['decode']:.0f}\n")
+        for key, v in traffic.items():
+            fh.write(f"{key}={v:.0f}\n")
     print(f"wrote profiles for source {src}")
 
 
@@ -405,7 +425,7 @@ def main():
                     help="write profiles/*.txt from rocprofv3 outputs under DIR and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k"],
+    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode"],
                     help="run one workload (for profiling); prints its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (HBM counter calibration)")
@@ -437,8 +457,7 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": max(1, args.steps)}))
         return
     if args.only:
-        spec = {"incremental": W.incremental(), "decode": W.decode_batch(),
-                "incremental_128k": W.incremental(131_072, 2_700, "incremental_128k")}[args.only]
+        spec = only_spec(W, args.only)
         r = Runner(pa, torch, spec, dev)
         ms, kern = r.timed(args.steps, args.warmup)
         print(json.dumps({"workload": args.only, "ms_per_step": round(ms, 4),
@@ -499,7 +518,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_batch_bytes"),
-                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_kernel<16>",
+                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_kernel<16, 4, 4>",
                          "kernel_ms": round(dk_ms, 4)},
         }
         del r
@@ -543,7 +562,8 @@ def main():
             "scales, block 64, 32 q / 8 KV, d 128")
         rep["long_context_decode_e4m3"] = report_decode(
             pa, torch, W.long_context(1_048_575, 1), dev, args.steps, rw,
-            "long_context decode step at context 1,048,576 (the first of 256), E4M3 KV, block 64")
+            "long_context decode step at context 1,048,576 (the first of 256), E4M3 KV, block 64",
+            kernel="decode_dma_fp8_kernel<64, 8, 2>", traffic_key="decode_long_e4m3_bytes")
         rep["kv_append_45700"] = report_append(pa, torch, dev, 45_700, 20,
                                                "kv_append of 45,700 bf16 tokens (initial prefill)")
         rep["kv_append_1m"] = report_append(pa, torch, dev, 1_048_576, 5,
