@@ -1687,7 +1687,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) 
   __syncthreads();
   const int lim_min = min(it.pos0, kv_hi - 1);
 
-  auto f = [](int r) { return (r >> 1) & 7; };
+  // LDS rows of 128 bytes, logical 16-byte chunk q of row r at position
+  // q ^ f(r).  A transposing 8-byte read is served a half-wave at a time
+  // (256 bytes: 64 four-byte banks, measured with SQ_LDS_BANK_CONFLICT); the
+  // V^T reads of half-wave 0 touch rows 0..7 and 16..23 (half-wave 1: 8..15
+  // and 24..31), so f flips chunk bit 2 for rows 16..31 and the two row sets
+  // land on distinct banks (without it, a 2-way conflict).  The K reads stay
+  // conflict-free: rows 2k and 2k+1 share f and sit 128 bytes apart.
+  auto f = [](int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); };
   // load q of a slice: rows 8q .. 8q+7; lane i fills chunk position i & 7 of
   // row 8q + (i >> 3) with the row's chunk (i & 7) ^ f(row)
   int voff[4];
