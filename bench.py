@@ -140,8 +140,8 @@ def _kern(kern):
     return {k: round(v[0], 4) for k, v in kern.items()}
 
 
-def report_prefill(pa, torch, spec, dev, steps, warmup, label):
-    r = Runner(pa, torch, spec, dev)
+def report_prefill(pa, torch, spec, dev, steps, warmup, label, runner=None):
+    r = runner or Runner(pa, torch, spec, dev)
     ms, kern = r.timed(steps, warmup)
     fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
     k_ms = kern["prefill"][0] * kern["prefill"][1]
@@ -153,9 +153,79 @@ def report_prefill(pa, torch, spec, dev, steps, warmup, label):
                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(fl / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                       "kernel": "prefill_w48_kernel<%d>" % spec.block_size}}
-    del r
-    torch.cuda.empty_cache()
+    if runner is None:
+        del r
+        torch.cuda.empty_cache()
     return d
+
+
+def report_decode_steps(pa, torch, r, dev, label, nsteps=256, warmup=16):
+    """The decode steps that follow an incremental prefill of one session: step
+    j appends one token at position hist + incr + j - 1 and attends over the
+    whole context.  The steps are run as a serving loop would (each plans on
+    the host and launches); one pass with HIP events around each launch gives
+    the kernel times, then a clean pass with one event per step gives each
+    step's time (median, min, max) and the total.  Re-running a step rewrites
+    the same bytes, so passes are repeatable."""
+    import workloads as W
+    spec, b = r.spec, r.b
+    first = int(b.hist[0]) + int(b.incr[0])
+    r.step()  # the prefill's own tokens are in the cache
+    toks = [W.decode_step_tokens(spec, j, dev) for j in range(1, nsteps + 1)]
+    slots = [torch.tensor([W.slot_of(b, 0, first + j - 1)], dtype=torch.int64, device=dev)
+             for j in range(1, nsteps + 1)]
+    hists = [np.array([first + j - 1], np.int32) for j in range(1, nsteps + 1)]
+    one = np.array([1], np.int32)
+    ws_need = pa.pa_workspace_size(hists[-1], one, spec.num_q_heads, r.cache)
+    ws = r.ws if r.ws.numel() >= ws_need else torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    out = torch.empty((1, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device=dev)
+
+    def step(j):
+        q, k, v = toks[j]
+        pa.kv_append(r.cache, k, v, slots[j], stream=r.stream)
+        pa.paged_attn_forward(q, r.cache, r.bt, hists[j], one, spec.scale, out, ws, stream=r.stream)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    for k in range(5):
+        pa.pa_timing_read(k)
+    pa.pa_timing_enable(True)
+    for j in range(nsteps):
+        step(j)
+    torch.cuda.synchronize()
+    pa.pa_timing_enable(False)
+    kern = {}
+    for kind, name in ((0, "kv_append"), (2, "decode"), (3, "merge")):
+        tot, cnt = pa.pa_timing_read(kind)
+        if cnt:
+            kern[name] = (tot / cnt, cnt / nsteps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    ev[0].record(r.stream)
+    for j in range(nsteps):
+        step(j)
+        ev[j + 1].record(r.stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[j].elapsed_time(ev[j + 1]) for j in range(nsteps)])
+    total = ev[0].elapsed_time(ev[nsteps])
+    med = float(np.median(per))
+    # algorithmic bytes of the middle step (the steps differ by < 0.03%)
+    mid = W.Spec(spec.name, spec.cfg, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                 spec.block_size, [first + nsteps // 2 - 1], [1], kv_dtype=spec.kv_dtype)
+    byts = decode_bytes(mid)
+    k_ms = kern["decode"][0] * kern["decode"][1] + kern.get("merge", (0, 0))[0] * kern.get("merge", (0, 0))[1]
+    dk_ms = kern["decode"][0] * kern["decode"][1]
+    return {"workload": label, "steps": nsteps,
+            "ms_per_step_median": round(med, 4), "ms_per_step_min": round(float(per.min()), 4),
+            "ms_per_step_max": round(float(per.max()), 4), "total_ms": round(total, 3),
+            "GB/s_median_step": round(byts / (med * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(nsteps / (total * 1e-3), 1),
+            "kernels_ms": _kern(kern), "decode_plus_merge_ms": round(k_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(byts / (dk_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_long_e4m3_bytes"),
+                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_fp8_kernel<64, 8, 2>"}}
 
 
 def report_decode(pa, torch, spec, dev, steps, warmup, label, kernel=None, traffic_key=None):
@@ -230,9 +300,22 @@ def report_append(pa, torch, dev, tokens, steps, label):
     tot, cnt = pa.pa_timing_read(0)
     k_ms = tot / cnt
     byts = 2 * tokens * hkv * d * 2 * 2 + tokens * 8   # K and V read and written, slots read
+    # a plain device copy of the same K and V bytes, for comparison
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kflat, vflat = kc.view(-1)[:k_new.numel()], vc.view(-1)[:v_new.numel()]
+    kflat.copy_(k_new.view(-1))
+    e0.record(s)
+    for _ in range(steps):
+        kflat.copy_(k_new.view(-1))
+        vflat.copy_(v_new.view(-1))
+    e1.record(s)
+    torch.cuda.synchronize()
+    c_ms = e0.elapsed_time(e1) / steps
     out = {"workload": label, "tokens": tokens, "kernel_ms": round(k_ms, 4),
            "GB/s": round(byts / (k_ms * 1e-3) / 1e9, 1),
-           "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byts)}
+           "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byts),
+           "plain_copy_GB/s": round(4 * tokens * hkv * d * 2 / (c_ms * 1e-3) / 1e9, 1),
+           "traffic": measured_traffic("kv_append_1m_bytes") if tokens == 1_048_576 else None}
     del kc, vc, k_new, v_new
     torch.cuda.empty_cache()
     return out
@@ -289,20 +372,30 @@ PROFILE_CMDS = {
            "python3 REPO/bench.py --only {w} --steps 2 --warmup 1",
     "copy": "rocprofv3 --pmc {counter} --output-format csv -d OUT/pmc/copy_{counter} -o p -- "
             "python3 REPO/bench.py --copy-calibration 1024 --steps 2",
+    "pmc_set": "rocprofv3 --pmc {counters} --output-format csv -d OUT/pmcx/{w}_{i} -o p -- "
+               "python3 REPO/bench.py --only {w} --steps 2 --warmup 1",
 }
+# counter passes behind profiles/design_counters.txt (each within one pass's
+# hardware limits: at most 8 SQ, 4 TCC, 2 GRBM counters)
+DESIGN_COUNTER_SETS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVES "
+                       "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
+                       "TCC_HIT_sum TCC_MISS_sum"]
 KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_device.h",
                   "paged_kv_cache_gqa_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_gqa_amd/csrc/pa_append.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "void pa::prefill_w48_kernel<16>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
+APPEND_KERNEL = "void pa::append_kernel<false>(pa::AppendArgs)"
 # (--only workload, kernel, summary name, key in TRAFFIC_FILE)
 PROFILED = [("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k", "prefill_incremental_bytes"),
             ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k", "prefill_incremental_128k_bytes"),
             ("decode", DECODE_KERNEL, "decode_batch_64x142k", "decode_batch_bytes"),
-            ("long_decode", DECODE_FP8_KERNEL, "decode_e4m3_context_1m", "decode_long_e4m3_bytes")]
+            ("long_decode", DECODE_FP8_KERNEL, "decode_e4m3_context_1m", "decode_long_e4m3_bytes"),
+            ("kv_append_1m", APPEND_KERNEL, "kv_append_1m_bf16", "kv_append_1m_bytes")]
 
 
 def only_spec(W, name):
@@ -310,6 +403,15 @@ def only_spec(W, name):
     return {"incremental": lambda: W.incremental(), "decode": lambda: W.decode_batch(),
             "incremental_128k": lambda: W.incremental(131_072, 2_700, "incremental_128k"),
             "long_decode": lambda: W.long_context(1_048_575, 1)}[name]()
+
+
+def algorithmic_work(W, name):
+    """(flops, bytes) of one launch of the profiled kernel of bench.py --only NAME."""
+    if name == "kv_append_1m":
+        return 0, 2 * 1_048_576 * 8 * 128 * 2 * 2 + 1_048_576 * 8
+    spec = only_spec(W, name)
+    fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
+    return fl, decode_bytes(spec) if name in ("decode", "long_decode") else prefill_bytes(spec)
 
 
 def kernel_source_hash():
@@ -390,12 +492,72 @@ def summarize_profiles(out):
         fh.write("  " + PROFILE_CMDS["ktrace"] + "\n\n")
         _stats_table(fh, load("ktrace", "kernel_stats"))
         fh.write(f"\nKernel sources sha256[:16] = {src}\n")
+    if os.path.isdir(os.path.join(out, "pmcx")):
+        summarize_design_counters(out, src)
     with open(TRAFFIC_FILE, "w") as fh:
         fh.write("# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE, scaled by a 1 GiB copy\n")
         fh.write(f"source_hash={src}\n")
         for key, v in traffic.items():
             fh.write(f"{key}={v:.0f}\n")
     print(f"wrote profiles for source {src}")
+
+
+def summarize_design_counters(out, src):
+    """profiles/design_counters.txt: the counters behind the design choices,
+    per profiled kernel (mean over its dispatches)."""
+    import csv
+    import glob
+    import workloads as W
+    n_simd, n_xcc = 1024, 8
+    with open(os.path.join(ROOT, "profiles", "design_counters.txt"), "w") as fh:
+        fh.write("rocprofv3 counters behind the design choices (MI355X: 256 CUs, 1,024 SIMDs, 8 XCDs).\n"
+                 "Commands (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root), per workload W:\n")
+        for i, cs in enumerate(DESIGN_COUNTER_SETS):
+            fh.write("  " + PROFILE_CMDS["pmc_set"].format(counters=cs, w="W", i=i) + "\n")
+        fh.write("  python3 REPO/bench.py --summarize-profiles OUT\n"
+                 "Derived: clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /\n"
+                 "(GRBM_GUI_ACTIVE / 8 * 1,024 SIMDs); MFMA work / algorithmic = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 /\n"
+                 "the workload's algorithmic flops (padding: the all-ones row-sum block, the last tile's\n"
+                 "padded rows, the causal diagonal; decode packs G = 4 heads into 16 MFMA columns);\n"
+                 "LDS conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).\n\n")
+        for w, kname, unit_desc, _ in PROFILED:
+            vals, durs = {}, []
+            for i in range(len(DESIGN_COUNTER_SETS)):
+                fs = glob.glob(os.path.join(out, "pmcx", f"{w}_{i}", "*counter_collection.csv"))
+                if not fs:
+                    continue
+                for r in csv.DictReader(open(fs[0])):
+                    if r["Kernel_Name"] != kname:
+                        continue
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    if i == 0 and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                        durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            if not vals:
+                continue
+            m = {k: sum(v) / len(v) for k, v in vals.items()}
+            fl, byts = algorithmic_work(W, w)
+            fh.write(f"{kname} -- {unit_desc} (bench.py --only {w}), {len(durs)} dispatches\n")
+            for k in sorted(m):
+                fh.write(f"  {k:32s} {m[k]:.6g}\n")
+            dur = sum(durs) / len(durs) * 1e-9 if durs else None
+            gui = m.get("GRBM_GUI_ACTIVE", 0) / n_xcc
+            if dur:
+                fh.write(f"  duration (counter run)           {dur * 1e3:.4f} ms\n")
+                fh.write(f"  clock                            {gui / dur / 1e9:.3f} GHz\n")
+            if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                fh.write(f"  MFMA busy                        {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * n_simd):.3f}\n")
+            if fl and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+                fh.write(f"  MFMA work / algorithmic flops    {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / fl:.3f}\n")
+            if m.get("SQ_LDS_IDX_ACTIVE"):
+                fh.write(f"  LDS conflict share               {m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.4f}\n")
+            if "TCC_HIT_sum" in m:
+                fh.write(f"  L2 hit                           {m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}\n")
+            if dur:
+                if fl:
+                    fh.write(f"  algorithmic rate (counter run)   {fl / dur / 1e12:.1f} TFLOP/s\n")
+                fh.write(f"  algorithmic bytes / duration     {byts / dur / 1e9:.1f} GB/s\n")
+            fh.write("\n")
+        fh.write(f"Kernel sources sha256[:16] = {src}\n")
 
 
 def measured_traffic(key):
@@ -425,7 +587,7 @@ def main():
                     help="write profiles/*.txt from rocprofv3 outputs under DIR and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode"],
+    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m"],
                     help="run one workload (for profiling); prints its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (HBM counter calibration)")
@@ -455,6 +617,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": max(1, args.steps)}))
+        return
+    if args.only == "kv_append_1m":
+        print(json.dumps(report_append(pa, torch, dev, 1_048_576, max(1, args.steps),
+                                       "kv_append of 1,048,576 bf16 tokens")))
         return
     if args.only:
         spec = only_spec(W, args.only)
@@ -556,14 +722,18 @@ def main():
             pa, torch, W.mixed(), dev, rs, rw,
             "mixed: 4 incremental prefills (lognormal histories, median 100K) + 48 decodes "
             "(8 over a shared 10,000-token prefix), 32 q / 8 KV, d 128, block 16, bf16, one call")
+        lspec = W.long_context()
+        lr = Runner(pa, torch, lspec, dev)
         rep["long_context_prefill_e4m3"] = report_prefill(
-            pa, torch, W.long_context(), dev, max(3, args.steps // 4), rw,
+            pa, torch, lspec, dev, max(3, args.steps // 4), rw,
             "long_context: 1,044,480 cached + 4,096 new tokens, E4M3 KV with per-(block, head) "
-            "scales, block 64, 32 q / 8 KV, d 128")
-        rep["long_context_decode_e4m3"] = report_decode(
-            pa, torch, W.long_context(1_048_575, 1), dev, args.steps, rw,
-            "long_context decode step at context 1,048,576 (the first of 256), E4M3 KV, block 64",
-            kernel="decode_dma_fp8_kernel<64, 8, 2>", traffic_key="decode_long_e4m3_bytes")
+            "scales, block 64, 32 q / 8 KV, d 128", runner=lr)
+        rep["long_context_decode_e4m3"] = report_decode_steps(
+            pa, torch, lr, dev,
+            "long_context: the 256 decode steps after the prefill (contexts 1,048,577 to "
+            "1,048,832), each appending one token, E4M3 KV, block 64")
+        del lr
+        torch.cuda.empty_cache()
         rep["kv_append_45700"] = report_append(pa, torch, dev, 45_700, 20,
                                                "kv_append of 45,700 bf16 tokens (initial prefill)")
         rep["kv_append_1m"] = report_append(pa, torch, dev, 1_048_576, 5,
