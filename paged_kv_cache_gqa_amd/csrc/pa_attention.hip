@@ -748,7 +748,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
 // A row's 32 scores of a step sit in the four lanes c16 + 16g, reduced with
 // the permlane swaps.
 constexpr int kW48Step = 32;                        // keys per step
-constexpr int kW48TileBytes = kW48Step * 128 * 2;  // K (or V) of one step, 8 KB
+// K (or V) of one 32-key step in LDS: 8 blocks of 4 key rows, each block
+// 1,024 bytes of data and 32 of padding (the layout is described at the
+// item function)
+constexpr int kW48BlockBytes = 4 * 128 * 2 + 32;
+constexpr int kW48TileBytes = 8 * kW48BlockBytes;
 #ifndef PA_W48_STAGES
 #define PA_W48_STAGES 4
 #endif
@@ -822,21 +826,29 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
   }
 
-  // LDS tile: key row r is 256 bytes, logical 16-byte chunk q at position
-  // q ^ swz(r) (see the 256-row kernel; swz depends on r & 15 only, so rows r
-  // and r + 16 share it and the second key block is an immediate offset).
-  // The chunk index's high bits come from c (K: chunk 4c + g) and db (V:
-  // chunk 2db + h), so each read's offset is one per-lane base XOR c << 6
-  // (K) or db << 5 (V).
-  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
-  const int kbase = c16 * 256 + ((g ^ swz(c16)) << 4);
-  const int vr = 4 * g + (c16 >> 2);
-  const int vbase = vr * 256 + ((((c16 & 3) >> 1) ^ swz(vr)) << 4) + (c16 & 1) * 8;
-  auto kofs = [&](int c) { return kbase ^ (c << 6); };
-  auto vofs = [&](int db) { return vbase ^ (db << 5); };
-  // this wave's DMA lanes: tile rows 4*wave .. 4*wave+3, lane (lr, pc) fills
-  // chunk position pc of row 4*wave + lr
-  const int voff = (lane >> 4) * 256 + (((lane & 15) ^ swz(4 * wave + (lane >> 4))) << 4);
+  // LDS tile of one step (32 keys, 256 bytes each): key row k lies in block
+  // k / 4 (blocks kW48BlockBytes apart: 1 KB of data + 32 bytes), and within
+  // its block, 16-byte chunk q of row r = k % 4 sits at byte
+  // 256 (q / 4) + 64 r + 16 (q % 4).  gfx950's LDS serves 256 bytes a cycle
+  // (64 four-byte banks).  A 16-byte read is served 16 lanes at a time, lanes
+  // equal in lane bit 5 and in the parity of lane bits 2..4; a transposing
+  // 8-byte read, a half-wave at a time (both measured with
+  // SQ_LDS_BANK_CONFLICT on patterns built for the purpose).  With the
+  // 32-byte block padding, the K reads (lane (g, c) reads chunk 4j + g of row
+  // c) and the V^T reads (lane (g, c): row 4g + c/4, chunk 2db + (c%4)/2,
+  // half c%2) both hit distinct banks, and every read is one per-lane base
+  // plus an immediate: j * 256 (K), (db / 2) * 256 + (db % 2) * 32 (V), and
+  // 4 blocks for the second 16 keys.  Each quarter-wave of a DMA request
+  // fetches 64 contiguous bytes of one row.
+  constexpr int KB16 = 4 * kW48BlockBytes;  // keys 16..31 of the step
+  const int kbase = (c16 >> 2) * kW48BlockBytes + (c16 & 3) * 64 + g * 16;
+  const int vbase = g * kW48BlockBytes + (c16 >> 2) * 64 + ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8;
+  auto kofs = [&](int c) { return kbase + c * 256; };
+  auto vofs = [&](int db) { return vbase + (db >> 1) * 256 + (db & 1) * 32; };
+  // this wave's DMA lanes fill block `wave` (tile rows 4*wave .. 4*wave+3):
+  // lane l writes byte 16 l of the block, i.e. row (l / 4) % 4, chunk
+  // 4 (l / 16) + l % 4
+  const int voff = ((lane >> 2) & 3) * 256 + (4 * (lane >> 4) + (lane & 3)) * 16;
   const unsigned char *kc = (const unsigned char *)a.c.k;
   const unsigned char *vc = (const unsigned char *)a.c.v;
 
@@ -867,10 +879,10 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
                         __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
     const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
                         __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-    dma_load16(rk, voff, st + wave * 1024);
-    dma_load16(rv, voff, st + TILEB + wave * 1024);
+    dma_load16(rk, voff, st + wave * kW48BlockBytes);
+    dma_load16(rv, voff, st + TILEB + wave * kW48BlockBytes);
     rpos += kW48Step;
-    st_off = (st_off + STAGEB) & (NST * STAGEB - 1);
+    st_off = st_off + STAGEB == NST * STAGEB ? 0 : st_off + STAGEB;
     blk_next = bt_lds[min((rpos >> LGBS) - blk0, bt_last)];
   };
   static_assert((NST & (NST - 1)) == 0, "ring stages: a power of two");
@@ -921,7 +933,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
 #pragma unroll
     for (int db = 0; db < NDB; db++) {
       const bf16x4 h0 = lds_read_tr(Vb + vofs(db));
-      const bf16x4 h1 = lds_read_tr(Vb + 4096 + vofs(db));
+      const bf16x4 h1 = lds_read_tr(Vb + KB16 + vofs(db));
       vf[db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 #pragma unroll
@@ -940,7 +952,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
 #pragma unroll
       for (int c = 0; c < NCQ; c++)
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) kf[c][kb] = as_bf16x8(lds_load16(Kb + kb * 4096 + kofs(c)));
+        for (int kb = 0; kb < 2; kb++) kf[c][kb] = as_bf16x8(lds_load16(Kb + kb * KB16 + kofs(c)));
 #pragma unroll
       for (int c = 0; c < NCQ; c++)
 #pragma unroll
@@ -980,7 +992,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     for (int c = 0; c < NCQ; c++)
 #pragma unroll
       for (int kb = 0; kb < 2; kb++) {
-        const bf16x8 kf = as_bf16x8(lds_load16(Kb + kb * 4096 + kofs(c)));
+        const bf16x8 kf = as_bf16x8(lds_load16(Kb + kb * KB16 + kofs(c)));
 #pragma unroll
         for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? cinit(rb) : S[kb][rb]);
       }
