@@ -596,8 +596,8 @@ def main():
         summarize_profiles(args.summarize_profiles)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the path is built and measured on one "
-              "MI355X only (multi-GPU sharding is not part of this build).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(no sharding or collectives), so only --gpus 1 is measured.", file=sys.stderr)
         sys.exit(2)
 
     import torch
