@@ -606,11 +606,12 @@ pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const void *v_n
   a.vs = cache->v_scale;
   a.hkv = cache->num_kv_heads;
   a.bs = cache->block_size;
+  a.lbs = a.bs == 16 ? 4 : 6;
   a.d = cache->head_dim;
-  a.total_chunks = (int64_t)num_tokens * a.hkv * (a.d / 8);
+  a.lcpr = a.d == 64 ? 3 : 4;
   const bool fp8 = cache->dtype == PA_KV_FP8_E4M3;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = timed(0, s, [&] { return launch_append(a, fp8, s); });
+  hipError_t e = timed(0, s, [&] { return launch_append(a, fp8, num_tokens, s); });
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return PA_OK;
 }

@@ -12,6 +12,8 @@
 // K and of V; a token with a negative slot is skipped.  8-bit caches store
 // E4M3(x / scale) with the correctly rounded fp32 quotient, nearest-even
 // rounding and saturation to +-448.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -19,17 +21,20 @@ namespace pa {
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= a.total_chunks) return;
-  const int cpr = a.d / 8;
-  const int ch = (int)(gid % cpr);
-  const int64_t th = gid / cpr;
-  const int h = (int)(th % a.hkv);
-  const int64_t t = th / a.hkv;
+  // 32-bit index arithmetic within a launch (the host keeps each launch
+  // below 2^31 chunks) and shifts for the power-of-two sizes: the 64-bit
+  // divisions this replaces cost more instructions than the copy itself
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  if (gid >= a.nchunks) return;
+  const uint32_t ch = gid & ((1u << a.lcpr) - 1);
+  const uint32_t row = gid >> a.lcpr;  // (token, KV head) row of this launch
+  const uint32_t tl = row / (uint32_t)a.hkv;
+  const int h = (int)(row - tl * (uint32_t)a.hkv);
+  const int64_t t = a.tok0 + tl;
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
-  const int64_t blk = slot / a.bs, off = slot % a.bs;
-  const int64_t src = th * a.d + ch * 8;                                // element offset
+  const int64_t blk = slot >> a.lbs, off = slot & (a.bs - 1);
+  const int64_t src = (t * a.hkv + h) * a.d + ch * 8;                   // element offset
   const int64_t dst = ((blk * a.hkv + h) * a.bs + off) * a.d + ch * 8;  // element offset
   const uint4 kv = gload16_nt((const unsigned char *)a.k_new + src * 2);
   const uint4 vv = gload16_nt((const unsigned char *)a.v_new + src * 2);
@@ -154,14 +159,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   *(uint4 *)((unsigned char *)a.v_out + dst) = *(const uint4 *)((const unsigned char *)a.v + src);
 }
 
-hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s) {
-  if (a.total_chunks <= 0) return hipSuccess;
-  const int64_t blocks = (a.total_chunks + 255) / 256;
-  if (fp8)
-    hipLaunchKernelGGL(append_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipStream_t s) {
+  // token pieces of at most 2^30 chunks each
+  const int64_t row_chunks = (int64_t)a.hkv << a.lcpr;
+  const int64_t piece = std::max<int64_t>(1, ((int64_t)1 << 30) / row_chunks);
+  for (int64_t t0 = 0; t0 < num_tokens; t0 += piece) {
+    AppendArgs b = a;
+    b.tok0 = t0;
+    b.nchunks = (uint32_t)(std::min(piece, num_tokens - t0) * row_chunks);
+    const unsigned blocks = (b.nchunks + 255) / 256;
+    if (fp8)
+      hipLaunchKernelGGL(append_kernel<true>, dim3(blocks), dim3(256), 0, s, b);
+    else
+      hipLaunchKernelGGL(append_kernel<false>, dim3(blocks), dim3(256), 0, s, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {

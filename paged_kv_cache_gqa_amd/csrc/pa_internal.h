@@ -86,10 +86,13 @@ struct AppendArgs {
   void *v_cache;
   const float *ks;
   const float *vs;
-  int64_t total_chunks;   // tokens * hkv * (d / 8)
+  int64_t tok0;           // first token of this launch
+  uint32_t nchunks;       // this launch's tokens * hkv * (d / 8), below 2^31
   int32_t hkv;
-  int32_t bs;
-  int32_t d;
+  int32_t bs;             // a power of two
+  int32_t lbs;            // log2(bs)
+  int32_t d;              // 64 or 128
+  int32_t lcpr;           // log2(d / 8)
 };
 
 struct GatherArgs {
@@ -149,7 +152,7 @@ hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8
 // n_many) more, with at most many_rows rows each
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
 constexpr int kMergeSerialParts = 16;
-hipError_t launch_append(const AppendArgs &a, bool fp8, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
 hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s);
