@@ -140,7 +140,7 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
     # coverage[row, kvh] = number of keys covered (must equal pos + 1, no overlaps)
     cover = {}
     parts = {}
-    for it in items:
+    for idx, it in enumerate(items):
         seq, kvh, row0, pos0, nq, lo, hi, part = (int(x) for x in it)
         assert 0 <= kvh < hkv and nq >= 1 and nq * G <= (384 if d == 128 else 128)
         if d == 128 and nq * G > 16:  # LDS-staged block ids bound the item's span
@@ -151,9 +151,9 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
         assert hi <= pos0 + nq  # never beyond the last row's key
         for r in range(row0, row0 + nq):
             cover.setdefault((r, kvh), []).append((lo, hi))
-        if part >= 0:
-            parts.setdefault(part, 0)
-            parts[part] += 1
+        if part >= 0:  # prefill and decode partials are separate slot arrays
+            key = (idx < counts[0], part)
+            parts[key] = parts.get(key, 0) + 1
     for r in range(total_q):
         seq = int(np.searchsorted(rowstart, r, side="right") - 1)
         pos = hist[seq] + (r - rowstart[seq])
@@ -243,3 +243,30 @@ def test_planner_initial_prefill_whole_tiles(palib):
         assert np.all(np.diff(lens) <= 0)             # longest first
         loads.append(int(lens.sum()))
     assert (max(loads) - min(loads)) / max(loads) < 0.01, (min(loads), max(loads))
+
+
+def test_planner_random_configs(palib):
+    """Seeded random step shapes (sequence count, history and increment
+    lengths including idle sequences, decodes and multi-tile increments; every
+    head dim, block size and GQA group): the work list covers every row's
+    causal key range exactly once, partial slots are unique and merged, and
+    the persistent prefill split stays balanced."""
+    rng = np.random.default_rng(20261202)
+    for trial in range(64):
+        n = int(rng.integers(1, 9))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        bs = int(rng.choice([16, 64]))
+        hist = [int(rng.choice([0, 1, 63, 64, 1000, 20_000, 140_000])) + int(rng.integers(0, 97))
+                for _ in range(n)]
+        incr = [int(rng.choice([0, 1, 2, 5, 17, 96, 383, 1200])) for _ in range(n)]
+        if sum(incr) == 0:
+            incr[0] = 1
+        print(f"[case] trial {trial}: hist={hist} incr={incr} hq={hkv * G} hkv={hkv} d={d} bs={bs}",
+              flush=True)
+        check_cover(palib, hist, incr, hkv * G, hkv, d=d, bs=bs)
+        items, counts = palib.pa_debug_plan(hist, incr, hkv * G,
+                                             cache(palib, num_kv_heads=hkv, head_dim=d, block_size=bs))
+        if d == 128 and counts[0] > 0:
+            check_balance(palib, hist, incr, hkv * G, hkv, d=d, bs=bs)

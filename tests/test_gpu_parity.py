@@ -175,6 +175,35 @@ def test_small_configs(palib, case):
     check_against_oracle(palib, _spec(hist, incr, hq, hkv, d, bs, dt, cfg=30 + CASES.index(case)))
 
 
+def _random_cases(n, seed=777):
+    """Seeded random step shapes within the supported domain: 1-5 sequences
+    mixing idle ones, decodes, short and multi-tile increments, histories up
+    to a few thousand tokens, every head dim, block size, GQA group and KV type."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        k = int(rng.integers(1, 6))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        hist = [int(rng.integers(0, 6000)) if rng.random() < 0.8 else 0 for _ in range(k)]
+        incr = [int(rng.choice([0, 1, 1, 3, 17, 64, 200, 500])) for _ in range(k)]
+        if sum(incr) == 0:
+            incr[-1] = 1
+        out.append((hist, incr, hkv * G, hkv, int(rng.choice([64, 128])), int(rng.choice([16, 64])),
+                    str(rng.choice(["bf16", "e4m3"]))))
+    return out
+
+
+RANDOM_CASES = _random_cases(10)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"r{i}" for i in range(len(RANDOM_CASES))])
+def test_random_configs(palib, case):
+    hist, incr, hq, hkv, d, bs, dt = case
+    print(f"[case] random hist={hist} incr={incr} hq={hq} hkv={hkv} d={d} bs={bs} {dt}", flush=True)
+    check_against_oracle(palib, _spec(hist, incr, hq, hkv, d, bs, dt, cfg=200 + RANDOM_CASES.index(case)))
+
+
 def test_long_decode_split_and_merge(palib):
     """A decode over 100K keys and an increment over 40K keys: both are cut
     into several items whose partials are merged."""
