@@ -321,6 +321,55 @@ def report_append(pa, torch, dev, tokens, steps, label):
     return out
 
 
+def measure_peaks(pa, torch, dev):
+    """The chip's practical ceilings, measured with the instructions the
+    kernels use (the library's measurement hooks): back-to-back bf16 MFMAs on
+    every CU, and a streaming read of 4 GiB through LDS with the decode
+    kernels' non-temporal LDS-filling loads.
+    Each runs ~0.2 s first so the clock has settled."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(launch, n):
+        t0 = time.time()
+        while time.time() - t0 < 0.2:
+            launch()
+            torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(n):
+            launch()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    iters = 8192
+    out = torch.empty(pa.PEAK_MFMA_THREADS, dtype=torch.float32, device=dev)
+    ms_m = timed(lambda: pa.pa_peak_mfma(out, iters, stream=s), 20)
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    outr = torch.empty(pa.PEAK_READ_THREADS, dtype=torch.int32, device=dev)
+    ms_r = timed(lambda: pa.pa_peak_read(buf, outr, stream=s), 10)
+    res = {"mfma_bf16_TFLOP/s": round(pa.PEAK_MFMA_FLOPS_PER_ITER * iters / (ms_m * 1e-3) / 1e12, 1),
+           "hbm_read_GB/s": round(buf.numel() / (ms_r * 1e-3) / 1e9, 1),
+           "how": "bf16 16x16x32 MFMA loop, 8 waves per CU; 4 GiB streaming read through LDS "
+                  "with the decode kernels' non-temporal LDS-filling loads; measured after the "
+                  "workloads, ~0.2 s warm-up each"}
+    del buf, out, outr
+    torch.cuda.empty_cache()
+    return res
+
+
+def add_measured_fractions(obj, peaks):
+    """Beside each roofline's fraction of the published peak, its fraction of
+    the measured ceiling for the same resource."""
+    if isinstance(obj, dict):
+        rl = obj.get("roofline")
+        if isinstance(rl, dict) and "achieved" in rl:
+            ref = peaks["mfma_bf16_TFLOP/s"] if rl.get("bound") == "mfma" else peaks["hbm_read_GB/s"]
+            rl["frac_of_measured"] = round(rl["achieved"] / ref, 4)
+        for v in obj.values():
+            add_measured_fractions(v, peaks)
+
+
 def run_cpu_baseline(spec, budget_s):
     """The oracle, as it stands, on a bounded sample of the workload's query rows
     (all heads), on this host's cores.  Rate in the metric's unit."""
@@ -586,6 +635,8 @@ def main():
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/*.txt from rocprofv3 outputs under DIR and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA and HBM-read ceilings")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m"],
                     help="run one workload (for profiling); prints its JSON object")
@@ -739,6 +790,10 @@ def main():
         rep["kv_append_1m"] = report_append(pa, torch, dev, 1_048_576, 5,
                                             "kv_append of 1,048,576 bf16 tokens")
         line["reports"] = rep
+    if not args.no_peaks:
+        peaks = measure_peaks(pa, torch, dev)
+        line["measured_peaks"] = peaks
+        add_measured_fractions(line, peaks)
     if not args.no_cpu:
         line["cpu_baseline"] = run_cpu_baseline(spec, args.cpu_budget)
     print(json.dumps(line), flush=True)

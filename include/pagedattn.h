@@ -190,8 +190,8 @@ PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_len
                                int32_t *items_out, int32_t items_cap, int32_t *counts_out);
 
 /* Test hook for the persistent prefill launch: when the plan for these HOST
- * lengths runs the 256-row kernel (bf16 KV, head_dim 128) with one
- * work-group per balanced range of work, *num_groups_out receives the number
+ * lengths runs the persistent 384-row kernel (head_dim 128: bf16 KV, or the
+ * bf16 copy of E4M3 KV) with one work-group per balanced range of work, *num_groups_out receives the number
  * of work-groups n and first_out[0..n] the offsets into the prefill items
  * (as listed by pa_debug_plan) where each work-group's items begin, with
  * first_out[n] = the number of prefill items.  n = 0 (nothing written) for
@@ -200,6 +200,22 @@ PA_API pa_status pa_debug_plan_groups(const int32_t *hist_lens, const int32_t *i
                                       int32_t num_seqs, int32_t num_q_heads,
                                       const pa_kv_cache *cache, int32_t *first_out, int32_t cap,
                                       int32_t *num_groups_out);
+
+/* Measurement hooks: the practical ceilings of the two resources the
+ * attention kernels are bound by, measured with the same instructions
+ * (MI355X: 256 compute units).  Both enqueue one kernel on `stream`; the
+ * caller times it (e.g. with events on that stream).
+ *   pa_peak_mfma: 256 work-groups of 8 waves each run iters x 8 independent
+ *     v_mfma_f32_16x16x32_bf16 (16,384 flops each): 2^28 * iters flops in
+ *     all.  out: device float[256 * 512], written with a checksum.
+ *   pa_peak_read: streams `bytes` (a positive multiple of 4096) of the
+ *     device buffer `buf` through LDS with the decode kernels' non-temporal
+ *     LDS-filling 16-byte loads: one work-group of 4 waves per compute unit,
+ *     each wave a 4-stage ring of 4 KB requests.  out: device
+ *     uint32[256 * 256], written with a checksum.
+ * Nothing else is read or written. */
+PA_API pa_status pa_peak_mfma(float *out, int32_t iters, void *stream);
+PA_API pa_status pa_peak_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
-           "pa_debug_plan_groups")
+           "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read")
 
 
 class pa_kv_cache(C.Structure):
@@ -57,8 +57,11 @@ def _load():
     L.pa_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
     L.pa_debug_plan.argtypes = [P, P, i32, i32, pc, P, i32, P]
     L.pa_debug_plan_groups.argtypes = [P, P, i32, i32, pc, P, i32, P]
+    L.pa_peak_mfma.argtypes = [P, i32, P]
+    L.pa_peak_read.argtypes = [P, sz, P, P]
     for f in ("kv_append", "paged_attn_forward", "pa_debug_gather", "pa_timing_enable",
-              "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups"):
+              "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
+              "pa_peak_read"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -130,6 +133,22 @@ def pa_debug_gather(cache: pa_kv_cache, block_table_row, ctx, k_out, v_out, stre
 
 def pa_last_error() -> str:
     return lib.pa_last_error().decode()
+
+
+PEAK_MFMA_THREADS = 256 * 512      # out entries of pa_peak_mfma
+PEAK_MFMA_FLOPS_PER_ITER = 1 << 28  # 256 groups x 8 waves x 8 MFMAs x 16,384 flops
+PEAK_READ_THREADS = 256 * 256      # out entries of pa_peak_read
+
+
+def pa_peak_mfma(out, iters, stream=None):
+    """Enqueue the MFMA-loop measurement kernel (out: float32 [PEAK_MFMA_THREADS])."""
+    _check(lib.pa_peak_mfma(_ptr(out), int(iters), _stream_ptr(stream)))
+
+
+def pa_peak_read(buf, out, stream=None):
+    """Enqueue a streaming read of the device buffer buf (out: int32 [PEAK_READ_THREADS])."""
+    _check(lib.pa_peak_read(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(out),
+                            _stream_ptr(stream)))
 
 
 def pa_timing_enable(on: bool):

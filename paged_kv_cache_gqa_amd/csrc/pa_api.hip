@@ -762,6 +762,23 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   return PA_OK;
 }
 
+pa_status pa_peak_mfma(float *out, int32_t iters, void *stream) {
+  if (!out) return fail(PA_ERR_NULL_ARG, "out is NULL");
+  if (iters < 1) return fail(PA_ERR_BAD_SHAPE, "iters %d < 1", iters);
+  hipError_t e = launch_peak_mfma(out, iters, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "peak_mfma launch");
+  return PA_OK;
+}
+
+pa_status pa_peak_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (!buf || !out) return fail(PA_ERR_NULL_ARG, "buf/out is NULL");
+  if (bytes < 4096 || bytes % 4096 != 0)
+    return fail(PA_ERR_BAD_SHAPE, "bytes %zu: a positive multiple of 4096 required", bytes);
+  hipError_t e = launch_peak_read(buf, (int64_t)bytes, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "peak_read launch");
+  return PA_OK;
+}
+
 pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_row, int32_t ctx,
                           void *k_out, void *v_out, void *stream) {
   pa_status st = check_cache(cache);

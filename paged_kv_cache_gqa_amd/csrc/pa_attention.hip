@@ -355,21 +355,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 // the row (conflict-free for both the 16-byte and the transposing reads).
 // The item's block ids are staged in LDS once (items span at most
 // kMaxDmaItemKeys keys) and read one tile ahead of their use.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
-
-// The compiler does not see inside the asm, so it cannot pad the hazards of
-// its operands: the resource words come from v_readfirstlane (a VALU write
-// of an SGPR needs 5 wait states before a vector-memory instruction reads
-// it) and M0 was just written by a scalar move (1 wait state before a load
-// that writes LDS).  The leading s_nop 4 provides both.
-__device__ __forceinline__ void dma_load16(i32x4_t rsrc, int voff, uint32_t lds_addr) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
-// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 64: the count's
-// low four bits sit in bits 3:0 of the immediate, its high two in bits 15:14)
-#define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+// (LDS-filling loads: dma_load16 / dma_load16_nt and PA_WAIT_VMCNT in pa_device.h)
 
 // Work-group barrier without a memory fence: LDS hazards around it are
 // handled by explicit waits; the compiler-only fences keep memory operations
@@ -1462,12 +1448,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 // slices.  No wave reads another wave's ring, so only vmcnt waits are needed.
 // K is read back as the A operand of v_mfma_f32_16x16x32_bf16 (lane: key n,
 // d 32c + 8*q4 .. +7), V with ds_read_b64_tr_b16 as the A operand of
-// v_mfma_f32_16x16x16_bf16 (lane: d 16*db + n, keys 4*q4 .. +3), in the
-// row-swizzled layout of the 384-row prefill kernel.
-__device__ __forceinline__ void dma_load16_nt(i32x4_t rsrc, int voff, uint32_t lds_addr) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
+// v_mfma_f32_16x16x16_bf16 (lane: d 16*db + n, keys 4*q4 .. +3); LDS rows
+// of 256 bytes with 16-byte chunk q of row r at q ^ ((r&7)<<1 | (r>>3)&1).
 
 constexpr int kDecSlice = 16;                      // keys per wave step
 constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4 KB

@@ -182,4 +182,29 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __builtin_bit_cast(float, b16 << 16);
 }
 
+// LDS-filling buffer loads: buffer_load_dwordx4 ... lds writes the 64 lanes'
+// 16-byte results to LDS at M0 + 16 * lane.  The resource descriptor is
+// {base lo, base hi & 0xFFFF, bytes in range, kRsrcFlags}; lanes whose
+// offset lies past the range read zeros.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+// The compiler does not see inside the asm, so it cannot pad the hazards of
+// its operands: the resource words come from v_readfirstlane (a VALU write
+// of an SGPR needs 5 wait states before a vector-memory instruction reads
+// it) and M0 was just written by a scalar move (1 wait state before a load
+// that writes LDS).  The leading s_nop 4 provides both.
+__device__ __forceinline__ void dma_load16(i32x4_t rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+// the same with the non-temporal hint, for data read once
+__device__ __forceinline__ void dma_load16_nt(i32x4_t rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 64: the count's
+// low four bits sit in bits 3:0 of the immediate, its high two in bits 15:14)
+#define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+
 }  // namespace pa

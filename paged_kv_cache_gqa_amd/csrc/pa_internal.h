@@ -153,6 +153,11 @@ hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
 constexpr int kMergeSerialParts = 16;
 hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipStream_t s);
+// measurement hooks (pa_peak.hip)
+constexpr int kPeakMfmaGroups = 256;   // one 512-thread work-group per CU
+constexpr int kPeakReadGroups = 256;   // streaming read: one 4-wave work-group per CU
+hipError_t launch_peak_mfma(float *out, int iters, hipStream_t s);
+hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
 hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s);

@@ -283,3 +283,32 @@ def test_error_path_writes_nothing(palib):
     assert e.value.status == palib.PA_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+def test_measurement_hooks(palib):
+    """The ceiling kernels bench.py times: the streaming read touches every
+    32-bit word of the buffer exactly once (the XOR of its per-thread
+    checksums is the XOR of the buffer), and the MFMA loop's accumulators
+    equal iters times one product of its constant operands."""
+    print("[case] measurement hooks", flush=True)
+    n = (1 << 20) + 3 * 4096  # whole 4 KB segments, not a multiple of the grid's waves
+    g = torch.Generator(device="cpu").manual_seed(5)
+    words = torch.randint(0, 1 << 31, (n // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    buf = words.to(DEV)
+    outr = torch.empty(palib.PEAK_READ_THREADS, dtype=torch.int32, device=DEV)
+    palib.pa_peak_read(buf, outr)
+    torch.cuda.synchronize()
+    x = np.bitwise_xor.reduce(outr.cpu().numpy().astype(np.uint32))
+    assert x == np.bitwise_xor.reduce(words.numpy().astype(np.uint32))
+    out = torch.empty(palib.PEAK_MFMA_THREADS, dtype=torch.float32, device=DEV)
+    palib.pa_peak_mfma(out, 3)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o)) and o.min() > 0
+    # every MFMA adds the same product: twice the iterations give twice the sums (exact)
+    o2 = torch.empty_like(out)
+    palib.pa_peak_mfma(o2, 6)
+    torch.cuda.synchronize()
+    assert np.allclose(o2.cpu().numpy(), 2 * o, rtol=1e-6)
+    with pytest.raises(palib.PagedAttnError):
+        palib.pa_peak_mfma(out, 0)

@@ -23,13 +23,17 @@ pytestmark = pytest.mark.skipif(not os.path.exists(pabuild.HIPCC), reason="hipcc
 
 @pytest.fixture(scope="module")
 def attention_asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "pa_attention.s"
-    flags = [f for f in pabuild.FLAGS if f not in ("-fPIC",)]
-    cmd = [pabuild.HIPCC, *flags, "--cuda-device-only", "-S",
-           os.path.join(pabuild.CSRC, "pa_attention.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
-    return out.read_text()
+    """The assembly of every source with LDS-filling loads."""
+    text = []
+    for src in ("pa_attention.hip", "pa_peak.hip"):
+        out = tmp_path_factory.mktemp("asm") / src.replace(".hip", ".s")
+        flags = [f for f in pabuild.FLAGS if f not in ("-fPIC",)]
+        cmd = [pabuild.HIPCC, *flags, "--cuda-device-only", "-S",
+               os.path.join(pabuild.CSRC, src), "-o", str(out)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 def _functions(asm):
