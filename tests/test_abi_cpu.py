@@ -270,3 +270,15 @@ def test_planner_random_configs(palib):
                                              cache(palib, num_kv_heads=hkv, head_dim=d, block_size=bs))
         if d == 128 and counts[0] > 0:
             check_balance(palib, hist, incr, hkv * G, hkv, d=d, bs=bs)
+
+
+def test_measurement_hooks_reject_bad_arguments(palib):
+    """Argument checks of the ceiling kernels run on the host, before any launch."""
+    pa = palib
+    assert pa.lib.pa_peak_mfma(None, 10, None) == pa.PA_ERR_NULL_ARG
+    assert pa.lib.pa_peak_mfma(FAKE, 0, None) == pa.PA_ERR_BAD_SHAPE
+    assert pa.lib.pa_peak_read(None, 4096, FAKE, None) == pa.PA_ERR_NULL_ARG
+    assert pa.lib.pa_peak_read(FAKE, 4096, None, None) == pa.PA_ERR_NULL_ARG
+    assert pa.lib.pa_peak_read(FAKE, 4096 + 16, FAKE, None) == pa.PA_ERR_BAD_SHAPE
+    assert pa.lib.pa_peak_read(FAKE, 0, FAKE, None) == pa.PA_ERR_BAD_SHAPE
+    assert "4096" in pa.pa_last_error()
