@@ -166,6 +166,8 @@ CASES = [
     ([20000, 3000, 50], [1, 1, 1], 32, 8, 128, 64, "e4m3"),  # E4M3 decode, split and merged
     ([9000, 130], [1, 3], 32, 8, 128, 16, "e4m3"),       # E4M3 decode, block 16
     ([7000, 33], [2, 1], 64, 8, 128, 16, "e4m3"),        # E4M3 decode, group 8
+    ([4096, 0], [192, 97], 32, 8, 128, 16, "bf16"),       # whole 96-token tiles, step-aligned history
+    ([8192], [384], 32, 8, 128, 64, "e4m3"),             # E4M3 prefill, whole tiles, block-aligned
 ]
 
 
