@@ -7,6 +7,7 @@ a multiply and an add each), and 2 * Hkv * d * elem bytes of K and V per
 context token.
 """
 import os
+import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -48,3 +49,10 @@ def test_decode_bytes_batch():
     ctx = [h + 1 for h in spec.hist]
     nb = sum(-(-c // 16) for c in ctx)
     assert bench.decode_bytes(spec) == sum(ctx) * 4096 + 2 * 64 * 32 * 128 * 2 + nb * 4
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; a request for more exits with a message."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0 and "one GPU" in r.stderr
