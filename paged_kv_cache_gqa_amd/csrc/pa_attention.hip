@@ -21,6 +21,16 @@
 // row's keys write normalised partial outputs and their log-sum-exp for the
 // merge kernel ([Agentic] §4.3.3: partial O_i with LSE merged the
 // online-softmax way; §5.2: split attention, then combine).
+//
+// Kernels, in file order:
+//   prefill_kernel<D, BS, FP8>     register-staged, 128-row tiles (head_dim 64)
+//   prefill_pp_kernel<BS>          256-row LDS-DMA variant (compile-time PA_WIDE_TILE=0)
+//   prefill_w48_kernel<BS>         persistent 384-row LDS-DMA prefill (head_dim 128; E4M3
+//                                  through its bf16 copy)
+//   decode_kernel<D, BS, FP8>      register-staged decode (head_dim 64)
+//   decode_dma_kernel<BS, NW, NST>, decode_dma_fp8_kernel<BS, NW, NST>
+//                                  LDS-DMA decode, bf16 and E4M3 (head_dim 128)
+//   merge_kernel, merge_many_kernel  LSE merge of split items
 #include "pa_device.h"
 #include "pa_internal.h"
 
