@@ -24,7 +24,6 @@
 //
 // Kernels, in file order:
 //   prefill_kernel<D, BS, FP8>     register-staged, 128-row tiles (head_dim 64)
-//   prefill_pp_kernel<BS>          256-row LDS-DMA variant (compile-time PA_WIDE_TILE=0)
 //   prefill_w48_kernel<BS>         persistent 384-row LDS-DMA prefill (head_dim 128; E4M3
 //                                  through its bf16 copy)
 //   decode_kernel<D, BS, FP8>      register-staged decode (head_dim 64)
@@ -346,25 +345,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 }
 
 // =============================================================================
-// Prefill for bf16 KV with head_dim 128 ("ping-pong"): one work-group of 8
-// waves per CU, 256 query rows; waves 0-3 (group 0) own rows 0-127, waves 4-7
-// (group 1) rows 128-255, each wave 32 rows.  Every tile step has two phases
-// separated by work-group barriers; in each phase one group issues the tile's
-// matrix-core work (S(t+1) = K(t+1) Q^T and O += V(t)^T P(t)^T) while the
-// other turns scores into probabilities on the vector ALUs, so each SIMD
-// always has one wave feeding its matrix core and one wave doing softmax.
-//
-// K/V tiles (64 keys) live in a four-stage LDS ring filled directly from HBM
-// by buffer loads that write LDS (no register staging); tile t+3 is requested
-// in step t by each wave during its softmax phase.  Each load covers four key rows
-// of one cache block; its buffer resource starts at those rows and ends at
-// the range's last key, so rows past the end read as zeros without touching
-// memory.  The loads are issued as inline assembly with explicit vmcnt waits:
-// the compiler neither reorders them nor inserts waits of its own for them.
-// LDS tile rows are 256 bytes with the 16-byte chunk index XOR-swizzled by
-// the row (conflict-free for both the 16-byte and the transposing reads).
-// The item's block ids are staged in LDS once (items span at most
-// kMaxDmaItemKeys keys) and read one tile ahead of their use.
+// LDS-DMA prefill for head_dim 128 (prefill_w48_kernel below).  K/V steps
+// live in a multi-stage LDS ring filled directly from HBM by buffer loads
+// that write LDS (no register staging), issued as inline assembly with
+// explicit vmcnt waits: the compiler neither reorders them nor inserts waits
+// of its own for them.  Each load covers four key rows of one cache block;
+// its buffer resource starts at those rows and ends at the range's last key,
+// so rows past the end read as zeros without touching memory.
 // (LDS-filling loads: dma_load16 / dma_load16_nt and PA_WAIT_VMCNT in pa_device.h)
 
 // Work-group barrier without a memory fence: LDS hazards around it are
@@ -378,361 +365,17 @@ __device__ __forceinline__ void wg_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-#ifndef PA_LOOKAHEAD
-#define PA_LOOKAHEAD 12
-#endif
-constexpr int kPpTileBytes = kKeyTile * 128 * 2;  // one 64-key K (or V) tile, 16 KB
-constexpr int kPpStages = 4;                        // K+V stages in the LDS ring
-constexpr int kPpMaxItemKeys = 65536;               // keys per item (the planner's cap when this kernel runs)
-static_assert(PA_WIDE_TILE || kMaxDmaItemKeys <= kPpMaxItemKeys, "256-row kernel item cap");
-
-// One work item of the 256-row kernel; the caller separates consecutive
-// items by a work-group barrier.
-template <int BS>
-__device__ __forceinline__ void pp_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
-  constexpr int D = 128;
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int TILEB = kPpTileBytes;
-  constexpr int STAGEB = 2 * TILEB;  // K + V of one tile
-  constexpr int NST = kPpStages;
-  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-
-  const float scale_log2 = a.scale_log2;
-  const int kv_hi = it.kv_hi, kvh = it.kvh, hkv = a.c.hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int col = lane & 31, hh = lane >> 5;
-  const int row = wave * 32 + col;
-  const int tok = row >> a.lg, g = row & (a.group - 1);
-  const bool active = tok < it.nq;
-  const int pos = it.pos0 + tok;
-  const int qh = kvh * a.group + g;
-
-  // Q is held pre-multiplied by scale * log2(e) (rounded to bf16), so the
-  // score MFMAs produce base-2 exponents directly.
-  bf16x8 qf[NC];
-  {
-    const unsigned char *qrow =
-        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
-#pragma unroll
-    for (int c = 0; c < NC; c++) {
-      uint4 v = active ? gload16(qrow + (c * 16 + hh * 8) * 2) : make_uint4(0, 0, 0, 0);
-      const bf16x8 q = as_bf16x8(v);
-#pragma unroll
-      for (int e = 0; e < 8; e++) qf[c][e] = (__bf16)((float)q[e] * scale_log2);
-    }
-  }
-
-  const int t_begin = it.kv_lo / kKeyTile;
-  const int t_end = (kv_hi + kKeyTile - 1) / kKeyTile;
-  const int t_full = max(t_begin, min(t_end, min(it.pos0 + 1, kv_hi) / kKeyTile));
-  const int blk0 = it.kv_lo / BS;
-  const int last_blk = (kv_hi - 1) / BS;
-  const int lim = min(pos, kv_hi - 1);
-
-  {  // stage the item's block ids
-    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
-    for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
-  }
-
-  // LDS tile layout: row r (a key) is 256 bytes; its logical 16-byte chunk q
-  // (elements 8q .. 8q+7) sits at chunk position q ^ swz(r).  The swizzle
-  // spreads the 16 rows a K read touches at one chunk (lanes 0-15, or
-  // 32-47) over 16 distinct positions, and keeps the transposing V reads,
-  // whose 16-lane groups span 4 rows x 2 chunks x 2 halves, conflict-free.
-  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
-  // per-lane LDS offsets: K A-operand reads (row col, chunk 2c + hh) and V
-  // transposing reads (rows r0 and 8 + r0 of each 16-key step, chunk 4db + c0)
-  int kofs[NC], vofs0[ND], vofs1[ND];
-  {
-#pragma unroll
-    for (int c = 0; c < NC; c++) kofs[c] = col * 256 + (((2 * c + hh) ^ swz(col)) << 4);
-    const int g16 = lane >> 4, j16 = lane & 15;
-    const int r0 = 4 * hh + (j16 >> 2);
-    const int c0 = (g16 & 1) * 2 + ((j16 & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < ND; db++) {
-      vofs0[db] = r0 * 256 + (((4 * db + c0) ^ swz(r0)) << 4) + (j16 & 1) * 8;
-      vofs1[db] = r0 * 256 + (((4 * db + c0) ^ swz(8 + r0)) << 4) + (j16 & 1) * 8;
-    }
-  }
-  // this wave's DMA lanes: instruction jj covers tile rows 8*wave + 4*jj .. +3;
-  // lane (lr, pc) fills chunk position pc of row 4*jj + lr from the global
-  // chunk that belongs there
-  int voff[2];
-#pragma unroll
-  for (int jj = 0; jj < 2; jj++) {
-    const int lr = lane >> 4, pc = lane & 15;
-    voff[jj] = lr * 256 + ((pc ^ swz(8 * wave + 4 * jj + lr)) << 4);
-  }
-  const unsigned char *kc = (const unsigned char *)a.c.k;
-  const unsigned char *vc = (const unsigned char *)a.c.v;
-
-  __syncthreads();  // block ids visible
-
-  // Rows 8*wave .. 8*wave+7 of a tile lie in one cache block (BS is a
-  // multiple of 8), so each wave needs one block id per tile; it is read
-  // from LDS one tile ahead so the read's latency is never waited on.
-  auto block_of = [&](int t) __attribute__((always_inline)) {
-    const int tt = min(t, t_end - 1);
-    return bt_lds[min((tt * kKeyTile + 8 * wave) / BS, last_blk) - blk0];
-  };
-  int blk_next = block_of(t_begin);
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    const int tt = min(t, t_end - 1);
-    const int64_t blk = __builtin_amdgcn_readfirstlane(blk_next);
-    blk_next = block_of(t + 1);
-    const uint32_t st = smem_addr + ((t - t_begin) & (NST - 1)) * STAGEB;
-    const int rpos = tt * kKeyTile + 8 * wave;
-    const int64_t base = ((blk * hkv + kvh) * BS + (rpos % BS)) * (D * 2);
-#pragma unroll
-    for (int jj = 0; jj < 2; jj++) {
-      const int nrec =
-          __builtin_amdgcn_readfirstlane(t < t_end ? min(max(kv_hi - rpos - 4 * jj, 0), 4) * (D * 2) : 0);
-      const uint64_t ka = (uint64_t)(kc + base + jj * 4 * D * 2), va = (uint64_t)(vc + base + jj * 4 * D * 2);
-      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
-                          __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
-                          __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-      dma_load16(rk, voff[jj], st + (2 * wave + jj) * 1024);
-      dma_load16(rv, voff[jj], st + TILEB + (2 * wave + jj) * 1024);
-    }
-  };
-  auto stage = [&](int t) __attribute__((always_inline)) {
-    return (const lds_u8 *)(smem + ((t - t_begin) & (NST - 1)) * STAGEB);
-  };
-
-  // m: per-row reference exponent (base 2).  Score MFMAs start from -m, so
-  // they yield s - m; m moves up only when a tile's maximum exceeds it by
-  // kRescaleSlack, and while the row has no weight yet it follows the max.
-  float m = 0.f, l = 0.f;
-  f32x16 o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; i++) o[i] = f32x16{};
-  f32x16 S[2];
-  bf16x8 pb[4];
-
-  // Matrix-core phase: O += V(t)^T P(t)^T (16 MFMAs, 32 transposing reads),
-  // then S(t+1) = K(t+1) Q^T (16 MFMAs, 16 reads).  The scheduling-group
-  // pattern keeps the LDS reads a few MFMAs ahead of their use, so read
-  // latency hides behind the matrix core and only a handful of fragments
-  // occupy registers at any time.  The score product alternates its two
-  // accumulators so consecutive MFMAs are independent.
-  auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
-    constexpr bool with_qk = decltype(with_qk_tag)::value;
-    bf16x8 vf[16];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-      for (int db = 0; db < ND; db++) {
-        const bf16x4 h0 = lds_read_tr(Vb + ks * 4096 + vofs0[db]);
-        const bf16x4 h1 = lds_read_tr(Vb + ks * 4096 + 2048 + vofs1[db]);
-        vf[ks * ND + db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-      for (int db = 0; db < ND; db++) o[db] = mfma32x32x16(vf[ks * ND + db], pb[ks], o[db]);
-    if constexpr (with_qk) {
-      bf16x8 kf[16];
-#pragma unroll
-      for (int c = 0; c < NC; c++)
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) kf[2 * c + kb] = as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c]));
-      const f32x16 neg_m = f32x16{} - m;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[kb], qf[0], neg_m);
-#pragma unroll
-      for (int c = 1; c < NC; c++)
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) S[kb] = mfma32x32x16(kf[2 * c + kb], qf[c], S[kb]);
-      // order: 12 reads ahead; (MFMA, 2 reads) x 16 over the value product;
-      // then the last score reads between the first score MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, PA_LOOKAHEAD, 0);
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < PA_LOOKAHEAD - 8; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - (PA_LOOKAHEAD - 8), 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x100, PA_LOOKAHEAD, 0);
-#pragma unroll
-      for (int i = 0; i < (32 - PA_LOOKAHEAD) / 2; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - (32 - PA_LOOKAHEAD) / 2, 0);
-    }
-  };
-  auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[0])), qf[0], f32x16{} - m);
-#pragma unroll
-      for (int c = 1; c < NC; c++)
-        S[kb] = mfma32x32x16(as_bf16x8(lds_load16(Kb + kb * 8192 + kofs[c])), qf[c], S[kb]);
-    }
-  };
-  auto softmax = [&](int t) __attribute__((always_inline)) {
-    if (t >= t_full) {
-      const int kbase = t * kKeyTile;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const int key = kbase + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          S[kb][e] = key <= lim ? S[kb][e] : -INFINITY;
-        }
-    }
-    // S holds s - m (base 2); mx is the tile's maximum of it
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) mx = fmaxf(mx, S[kb][e]);
-    mx = xor32_max(mx);
-    const bool move = mx > kRescaleSlack || (l == 0.f && mx > -INFINITY);
-    if (__any(move)) {
-      const float shift = move ? mx : 0.f;
-      const float alpha = fast_exp2(-shift);
-      m += shift;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < ND; db++) o[db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) S[kb] -= shift;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const float p = fast_exp2(S[kb][e]);
-        S[kb][e] = p;
-        psum += p;
-      }
-    l += psum;
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const int kb = ks >> 1, i0 = (ks & 1) * 2;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        pb[ks][r] = (__bf16)S[kb][4 * i0 + r];
-        pb[ks][4 + r] = (__bf16)S[kb][4 * (i0 + 1) + r];
-      }
-    }
-  };
-
-  // prologue: three tiles requested; S(t0) for both groups, P(t0) for group 0
-  issue(t_begin);
-  issue(t_begin + 1);
-  issue(t_begin + 2);
-  PA_WAIT_VMCNT(8);
-  wg_barrier();
-  qk_only(stage(t_begin));
-  // Each group runs its own loop (same number of barriers); step t opens
-  // once this wave's share of tile t+1 has landed (its tile t+2 loads may
-  // still be in flight).  Tile t+3 is requested into the stage tile t-1 left
-  // during the wave's softmax phase of step t, keeping the load issue off
-  // the matrix-core phase.
-  if (grp == 0) {
-    wg_barrier();
-    softmax(t_begin);
-    int t = t_begin;
-    for (; t + 1 < t_end; t++) {
-      PA_WAIT_VMCNT(4);
-      wg_barrier();
-      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
-      wg_barrier();
-      issue(t + 3);                                            // phase B: loads, vector ALUs
-      softmax(t + 1);
-    }
-    PA_WAIT_VMCNT(4);
-    wg_barrier();
-    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
-    wg_barrier();
-    issue(t + 3);
-  } else {
-    wg_barrier();
-    int t = t_begin;
-    for (; t + 1 < t_end; t++) {
-      PA_WAIT_VMCNT(4);
-      wg_barrier();
-      issue(t + 3);
-      softmax(t);                                              // phase A: vector ALUs
-      wg_barrier();
-      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
-    }
-    PA_WAIT_VMCNT(4);
-    wg_barrier();
-    issue(t + 3);
-    softmax(t);
-    wg_barrier();
-    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
-  }
-  PA_WAIT_VMCNT(0);  // the trailing (empty) tile requests complete before exit
-
-  const float lt = xor32_sum(l);
-  if (!active) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
-  if (it.part < 0) {
-    unsigned char *orow =
-        (unsigned char *)a.out + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
-#pragma unroll
-    for (int db = 0; db < ND; db++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        bf16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = (__bf16)(o[db][4 * i + r] * inv);
-        *(bf16x4 *)(orow + (db * 32 + 8 * i + 4 * hh) * 2) = v;
-      }
-    if (a.lse_out && hh == 0) a.lse_out[(int64_t)(it.row0 + tok) * a.hq + qh] = lse2 * kLn2;
-  } else {
-    float *prow = a.part_o + ((int64_t)it.part * kPpTileRows + row) * D;
-#pragma unroll
-    for (int db = 0; db < ND; db++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        f32x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = o[db][4 * i + r] * inv;
-        *(f32x4 *)(prow + db * 32 + 8 * i + 4 * hh) = v;
-      }
-    if (hh == 0) a.part_lse[(int64_t)it.part * kPpTileRows + row] = lse2;
-  }
-}
-
-// A work-group runs its items one after another: one item per work-group,
-// or with a persistent plan the balanced list wg_first assigns it.
-template <int BS>
-__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kPpStages * 2 * kPpTileBytes];
-  __shared__ int bt_lds[kPpMaxItemKeys / BS + 2];
-  const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
-  const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
-  for (int i = first; i < last; i++) {
-    if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
-    pp_item<BS>(a, a.items[i], (lds_u8 *)smem_raw, bt_lds);
-  }
-}
 
 // =============================================================================
-// 384-row prefill for bf16 KV, head_dim 128: the same ping-pong of two
-// groups of four waves and the same LDS-DMA ring as the 256-row kernel, with
-// 48 query rows per wave (three 16-row blocks) on v_mfma_f32_16x16x32_bf16
-// and 32-key steps.  Each K/V byte brought into the CU now serves 384 rows
-// instead of 256, and each LDS read 48 rows instead of 32.
+// 384-row prefill for bf16 KV, head_dim 128 ("ping-pong"): one work-group of
+// 8 waves per CU; waves 0-3 (group 0) and 4-7 (group 1) each own 48 query
+// rows per wave (three 16-row blocks) on v_mfma_f32_16x16x32_bf16, in 32-key
+// steps.  In each half-step one group issues its matrix-core work
+// (O += V(t)^T P(t)^T, then S(t+1) = K(t+1) Q^T) while the other turns
+// scores into probabilities on the vector ALUs, so each SIMD always has one
+// wave feeding its matrix core and one wave doing softmax.  (An earlier
+// 256-row design with 32 rows per wave on 32x32x16 MFMAs and 64-key steps
+// brought 1.5x the bytes into the CU per flop and ran at a lower clock.)
 //   Sᵀ = K Qᵀ per (16-key block kb, 16-row block rb): A = K (lane: key c16,
 //   d 32c + 8g..+7, one 16-byte LDS read), B = Qᵀ (lane: row c16, same d, in
 //   registers), D: lane holds row c16, keys 16kb + 4g + r.
@@ -1993,10 +1636,6 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a, int first)
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128) {
-    if (a.tile_rows == kPpTileRows) {
-      hipLaunchKernelGGL((prefill_pp_kernel<BS>), dim3(n), dim3(512), 0, s, a);
-      return hipGetLastError();
-    }
     if (a.tile_rows == kW48TileRows) {
       hipLaunchKernelGGL((prefill_w48_kernel<BS>), dim3(n), dim3(512), 0, s, a);
       return hipGetLastError();

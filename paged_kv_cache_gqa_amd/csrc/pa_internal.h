@@ -132,15 +132,11 @@ struct DequantArgs {
 };
 
 constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
-#ifndef PA_WIDE_TILE
-#define PA_WIDE_TILE 1
-#endif
-constexpr int kPpTileRows = 256;   // query rows per tile of prefill_pp_kernel
 constexpr int kW48TileRows = 384;  // query rows per tile of prefill_w48_kernel
-constexpr int kDmaTileRows = PA_WIDE_TILE ? kW48TileRows : kPpTileRows;  // bf16 KV, d 128
+constexpr int kDmaTileRows = kW48TileRows;  // the LDS-DMA prefill (head_dim 128)
 constexpr int kPrefillRowsMax = 384;
-// keys per item of the LDS-DMA prefill kernels (their block ids are staged in LDS)
-constexpr int kMaxDmaItemKeys = PA_WIDE_TILE ? 131072 : 65536;
+// keys per item of the LDS-DMA prefill kernel (its block ids are staged in LDS)
+constexpr int kMaxDmaItemKeys = 131072;
 constexpr int kMaxDecItemKeys = 32768;  // keys per decode item (block ids staged in LDS)
 constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
