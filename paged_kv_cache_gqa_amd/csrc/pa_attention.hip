@@ -396,25 +396,6 @@ constexpr int kW48TileBytes = 8 * kW48BlockBytes;
 #define PA_W48_STAGES 4
 #endif
 constexpr int kW48Stages = PA_W48_STAGES;
-// PA_W48_BARRIERS: work-group barriers per key step (2: strict alternation of
-// the two groups' phases; 1: one barrier, each group runs both phases back to
-// back).  PA_W48_PRIO: wave priority raised during the matrix-core phase.
-#ifndef PA_W48_BARRIERS
-#define PA_W48_BARRIERS 1
-#endif
-#ifndef PA_W48_PRIO
-#define PA_W48_PRIO 1
-#endif
-// PA_W48_FASTCHK: the per-step test for moving m is one maximum over the
-// lane's 24 scores against the slack, plus a wave-wide flag that every row
-// already has weight (rows without weight take the full test).
-// PA_W48_NEGM: -m held broadcast in registers as the score MFMAs' C operand.
-#ifndef PA_W48_FASTCHK
-#define PA_W48_FASTCHK 1
-#endif
-#ifndef PA_W48_NEGM
-#define PA_W48_NEGM 1
-#endif
 
 template <int BS>
 __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
@@ -536,34 +517,19 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   // o[NDB][rb] is the row sum l: the value product runs one more d-block
   // whose A operand is all ones, so l comes from the matrix cores (over the
   // same bf16 probabilities the output uses) and is rescaled with o.
-#if !PA_W48_NEGM
-  float m[RB];
-#endif
   f32x4 o[NDB + 1][RB];
   f32x4 S[2][RB];
   bf16x8 pb[RB];
-#if PA_W48_NEGM
   f32x4 negm[RB];  // -m[rb] in all four elements; m[rb] itself is not kept
-#endif
   int all_live = 0;  // every row of the wave has weight (wave-uniform)
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
-#if PA_W48_NEGM
     negm[rb] = f32x4{};
-#else
-    m[rb] = 0.f;
-#endif
 #pragma unroll
     for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
   }
 
-  auto cinit = [&](int rb) __attribute__((always_inline)) {
-#if PA_W48_NEGM
-    return negm[rb];
-#else
-    return f32x4{} - m[rb];
-#endif
-  };
+  auto cinit = [&](int rb) __attribute__((always_inline)) { return negm[rb]; };
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
   // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
   auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
@@ -667,11 +633,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
         live = live && (!empty || mx > -INFINITY);
         const float shift = mv ? mx : 0.f;
         const float alpha = fast_exp2(-shift);
-#if PA_W48_NEGM
         negm[rb] -= shift;
-#else
-        m[rb] += shift;
-#endif
 #pragma unroll
         for (int db = 0; db <= NDB; db++) o[db][rb] *= alpha;
 #pragma unroll
@@ -679,7 +641,6 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       }
       all_live = __builtin_amdgcn_readfirstlane(__all(live));
     };
-#if PA_W48_FASTCHK
     float mx = -INFINITY;
 #pragma unroll
     for (int rb = 0; rb < RB; rb++)
@@ -688,19 +649,6 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
 #pragma unroll
         for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
     if (__any(mx > kRescaleSlack) || !all_live) rescale();
-#else
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; rb++) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
-      need |= mx > kRescaleSlack || (o[NDB][rb][0] == 0.f && mx > -INFINITY);
-    }
-    if (__any(need)) rescale();
-#endif
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
@@ -723,14 +671,11 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   // With one barrier per step the groups stay half a step apart: the
   // barrier of step t finds group 0 about to start its matrix-core phase and
   // group 1 its vector phase.
-  auto mid_barrier = [&]() __attribute__((always_inline)) {
-    if constexpr (PA_W48_BARRIERS == 2) wg_barrier();
-  };
   auto prio_hi = [&]() __attribute__((always_inline)) {
-    if constexpr (PA_W48_PRIO) __builtin_amdgcn_s_setprio(PA_W48_PRIO);
+    __builtin_amdgcn_s_setprio(1);
   };
   auto prio_lo = [&]() __attribute__((always_inline)) {
-    if constexpr (PA_W48_PRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Steps before t_full need no causal mask: each group's loop runs in two
   // parts, the mask code only in the second, so the first has no branch.
@@ -741,7 +686,6 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     else softmax(open, t);
   };
   if (grp == 0) {
-    mid_barrier();
     softmax_rt(t_begin);
     int t = t_begin;
     auto body = [&](auto mtag) __attribute__((always_inline)) {
@@ -750,8 +694,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       prio_hi();
       gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
       prio_lo();
-      mid_barrier();
-      issue(t + NST - 1);                                      // phase B: loads, vector ALUs
+        issue(t + NST - 1);                                      // phase B: loads, vector ALUs
       softmax(mtag, t + 1);
     };
     for (const int t_open = min(t_full, t_end) - 1; t < t_open; t++) body(open);
@@ -759,18 +702,15 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     PA_WAIT_VMCNT(2 * (NST - 3));
     wg_barrier();
     gemm(std::false_type{}, stage(t) + TILEB, nullptr);
-    mid_barrier();
     issue(t + NST - 1);
   } else {
-    mid_barrier();
     int t = t_begin;
     auto body = [&](auto mtag) __attribute__((always_inline)) {
       PA_WAIT_VMCNT(2 * (NST - 3));
       wg_barrier();
       issue(t + NST - 1);
       softmax(mtag, t);                                        // phase A: vector ALUs
-      mid_barrier();
-      prio_hi();
+        prio_hi();
       gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
       prio_lo();
     };
@@ -780,7 +720,6 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     wg_barrier();
     issue(t + NST - 1);
     softmax_rt(t);
-    mid_barrier();
     gemm(std::false_type{}, stage(t) + TILEB, nullptr);
   }
   PA_WAIT_VMCNT(0);  // the trailing (empty) step requests complete before exit
@@ -792,11 +731,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     const float lt = o[NDB][rb][0];
     if (tok >= it.nq) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#if PA_W48_NEGM
     const float mrow = -negm[rb][0];
-#else
-    const float mrow = m[rb];
-#endif
     const float lse2 = lt > 0.f ? mrow + __log2f(lt) : -INFINITY;
     if (it.part < 0) {
       const int64_t orow = (int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq;
