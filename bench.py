@@ -247,20 +247,29 @@ def report_decode(pa, torch, spec, dev, steps, warmup, label, kernel=None, traff
     return d
 
 
+def mixed_parts(spec):
+    """(prefill flops, decode flops, decode unique bytes) of a mixed step: the
+    sequences with more than one new token are prefills, the rest decodes;
+    the shared prefix's blocks are counted once."""
+    pre = [i for i, n in enumerate(spec.incr) if n > 1]
+    dec = [i for i, n in enumerate(spec.incr) if n == 1]
+    fl = prefill_flops([spec.hist[i] for i in pre], [spec.incr[i] for i in pre],
+                       spec.num_q_heads, spec.head_dim)
+    dfl = prefill_flops([spec.hist[i] for i in dec], [1] * len(dec), spec.num_q_heads, spec.head_dim)
+    kvb = kv_bytes_per_token(spec)
+    shared = [i for i in dec if i in spec.shared_seqs]
+    uniq = sum(spec.hist[i] + 1 for i in dec) - max(0, len(shared) - 1) * spec.shared_prefix_tokens
+    byts = uniq * kvb + 2 * len(dec) * spec.num_q_heads * spec.head_dim * 2
+    return fl, dfl, byts
+
+
 def report_mixed(pa, torch, spec, dev, steps, warmup, label):
     """One call holding 4 incremental prefills and 48 decodes: the prefill
     part in TFLOP/s over its kernel, the decode part in GB/s over its kernel
     (the shared prefix's blocks counted once)."""
     r = Runner(pa, torch, spec, dev)
     ms, kern = r.timed(steps, warmup)
-    pre = [i for i, n in enumerate(spec.incr) if n > 1]
-    dec = [i for i, n in enumerate(spec.incr) if n == 1]
-    fl = prefill_flops([spec.hist[i] for i in pre], [spec.incr[i] for i in pre],
-                       spec.num_q_heads, spec.head_dim)
-    kvb = kv_bytes_per_token(spec)
-    shared = [i for i in dec if i in spec.shared_seqs]
-    uniq = sum(spec.hist[i] + 1 for i in dec) - max(0, len(shared) - 1) * spec.shared_prefix_tokens
-    byts = uniq * kvb + 2 * len(dec) * spec.num_q_heads * spec.head_dim * 2
+    fl, _, byts = mixed_parts(spec)
     p_ms = kern["prefill"][0] * kern["prefill"][1]
     d_ms = kern["decode"][0] * kern["decode"][1]
     d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
@@ -444,21 +453,26 @@ PROFILED = [("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k", "prefi
             ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k", "prefill_incremental_128k_bytes"),
             ("decode", DECODE_KERNEL, "decode_batch_64x142k", "decode_batch_bytes"),
             ("long_decode", DECODE_FP8_KERNEL, "decode_e4m3_context_1m", "decode_long_e4m3_bytes"),
-            ("kv_append_1m", APPEND_KERNEL, "kv_append_1m_bf16", "kv_append_1m_bytes")]
+            ("kv_append_1m", APPEND_KERNEL, "kv_append_1m_bf16", "kv_append_1m_bytes"),
+            ("mixed", PREFILL_KERNEL, "mixed_step_prefill_part", "prefill_mixed_bytes"),
+            ("mixed", DECODE_KERNEL, "mixed_step_decode_part", "decode_mixed_bytes")]
 
 
 def only_spec(W, name):
     """The workload of bench.py --only NAME."""
     return {"incremental": lambda: W.incremental(), "decode": lambda: W.decode_batch(),
             "incremental_128k": lambda: W.incremental(131_072, 2_700, "incremental_128k"),
-            "long_decode": lambda: W.long_context(1_048_575, 1)}[name]()
+            "long_decode": lambda: W.long_context(1_048_575, 1), "mixed": lambda: W.mixed()}[name]()
 
 
-def algorithmic_work(W, name):
+def algorithmic_work(W, name, kernel=None):
     """(flops, bytes) of one launch of the profiled kernel of bench.py --only NAME."""
     if name == "kv_append_1m":
         return 0, 2 * 1_048_576 * 8 * 128 * 2 * 2 + 1_048_576 * 8
     spec = only_spec(W, name)
+    if name == "mixed":
+        fl, dfl, byts = mixed_parts(spec)
+        return (dfl, byts) if kernel == DECODE_KERNEL else (fl, 0)
     fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
     return fl, decode_bytes(spec) if name in ("decode", "long_decode") else prefill_bytes(spec)
 
@@ -584,7 +598,7 @@ def summarize_design_counters(out, src):
             if not vals:
                 continue
             m = {k: sum(v) / len(v) for k, v in vals.items()}
-            fl, byts = algorithmic_work(W, w)
+            fl, byts = algorithmic_work(W, w, kname)
             fh.write(f"{kname} -- {unit_desc} (bench.py --only {w}), {len(durs)} dispatches\n")
             for k in sorted(m):
                 fh.write(f"  {k:32s} {m[k]:.6g}\n")
@@ -604,7 +618,8 @@ def summarize_design_counters(out, src):
             if dur:
                 if fl:
                     fh.write(f"  algorithmic rate (counter run)   {fl / dur / 1e12:.1f} TFLOP/s\n")
-                fh.write(f"  algorithmic bytes / duration     {byts / dur / 1e9:.1f} GB/s\n")
+                if byts:
+                    fh.write(f"  algorithmic bytes / duration     {byts / dur / 1e9:.1f} GB/s\n")
             fh.write("\n")
         fh.write(f"Kernel sources sha256[:16] = {src}\n")
 
@@ -638,7 +653,8 @@ def main():
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured MFMA and HBM-read ceilings")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m"],
+    ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m",
+                                       "mixed"],
                     help="run one workload (for profiling); prints its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (HBM counter calibration)")
