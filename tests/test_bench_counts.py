@@ -56,3 +56,19 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_mixed_step_split():
+    """The mixed step's parts: prefill flops over the four increments only,
+    decode bytes over the 48 decodes with the 10,000-token shared prefix
+    counted once."""
+    spec = W.mixed()
+    fl, dfl, byts = bench.mixed_parts(spec)
+    pre = [i for i, n in enumerate(spec.incr) if n > 1]
+    dec = [i for i, n in enumerate(spec.incr) if n == 1]
+    assert len(pre) == 4 and len(dec) == 48
+    pairs = sum(spec.incr[i] * spec.hist[i] + spec.incr[i] * (spec.incr[i] + 1) // 2 for i in pre)
+    assert fl == 4 * 128 * 32 * pairs
+    assert dfl == 4 * 128 * 32 * sum(spec.hist[i] + 1 for i in dec)
+    ctx = sum(spec.hist[i] + 1 for i in dec)
+    assert byts == (ctx - 7 * 10_000) * 4096 + 2 * 48 * 32 * 128 * 2
