@@ -47,8 +47,10 @@ def kv_bytes_per_token(spec):
 
 
 def decode_bytes(spec):
-    """Algorithmic HBM bytes of one decode step: every context token's K and V
-    once, plus q, out, the step's appended K/V and the block-table entries read."""
+    """Algorithmic HBM bytes the decode attention moves in one step: every
+    context token's K and V read once (the step's own token included), plus q
+    read, out written and the block-table entries read.  (The append of the
+    step's token is kv_append's traffic, reported on its own.)"""
     ctx = sum(int(h) + int(n) for h, n in zip(spec.hist, spec.incr))
     q = spec.total_q * spec.num_q_heads * spec.head_dim * 2
     nb = sum(-(-(int(h) + int(n)) // spec.block_size) for h, n in zip(spec.hist, spec.incr))

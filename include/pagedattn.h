@@ -201,6 +201,16 @@ PA_API pa_status pa_debug_plan_groups(const int32_t *hist_lens, const int32_t *i
                                       const pa_kv_cache *cache, int32_t *first_out, int32_t cap,
                                       int32_t *num_groups_out);
 
+/* The machine shape the work planner cuts plans for: the current device's
+ * compute units and XCDs (chiplets, each with its own L2), queried once per
+ * device (MI355X: 256 and 8); without a device, the MI355X's shape.  The
+ * planner assumes work-group w of a launch runs on XCD w mod num_xcds. */
+PA_API pa_status pa_device_shape(int32_t *num_cus, int32_t *num_xcds);
+
+/* Test hook for that assumption: enqueues n work-groups on `stream`;
+ * work-group w writes the id of the XCD it ran on to out[w] (device int32[n]). */
+PA_API pa_status pa_debug_xcc_ids(int32_t *out, int32_t n, void *stream);
+
 /* Measurement hooks: the practical ceilings of the two resources the
  * attention kernels are bound by, measured with the same instructions
  * (MI355X: 256 compute units).  Both enqueue one kernel on `stream`; the

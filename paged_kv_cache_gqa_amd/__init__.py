@@ -23,7 +23,8 @@ TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
-           "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read")
+           "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read", "pa_device_shape",
+           "pa_debug_xcc_ids")
 
 
 class pa_kv_cache(C.Structure):
@@ -59,9 +60,11 @@ def _load():
     L.pa_debug_plan_groups.argtypes = [P, P, i32, i32, pc, P, i32, P]
     L.pa_peak_mfma.argtypes = [P, i32, P]
     L.pa_peak_read.argtypes = [P, sz, P, P]
+    L.pa_device_shape.argtypes = [C.POINTER(i32), C.POINTER(i32)]
+    L.pa_debug_xcc_ids.argtypes = [P, i32, P]
     for f in ("kv_append", "paged_attn_forward", "pa_debug_gather", "pa_timing_enable",
               "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
-              "pa_peak_read"):
+              "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -85,15 +88,81 @@ def _check(status):
         raise PagedAttnError(status, lib.pa_last_error().decode())
 
 
+# ---------------------------------------------------------------------------
+# Argument validation.  The library trusts device *contents* (block ids,
+# slots) and sees only raw pointers, so a tensor of the wrong dtype, device,
+# layout or shape would be reinterpreted silently and could make the GPU read
+# out of bounds.  Every tensor argument is checked here before the call;
+# shapes and dtypes first, the device last (so the checks can be exercised
+# without a GPU).  These are checks only: no value is computed or converted.
+
+def _bad(msg):
+    raise PagedAttnError(PA_ERR_BAD_SHAPE, msg)
+
+
+def _tensor(t, name, dtypes, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        _bad(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        _bad(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(a) != int(w)
+                                        for a, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            _bad(f"{name} has shape {list(t.shape)}, expected {want}")
+    if not t.is_contiguous():
+        _bad(f"{name} must be contiguous")
+    return (t, name)
+
+
+def _on_device(checked, device=None):
+    """Second pass over the (tensor, name) pairs _tensor accepted: each must
+    live on the GPU (the cache's device when that is known)."""
+    for t, name in checked:
+        if not t.is_cuda:
+            _bad(f"{name} must be a GPU tensor (got device {t.device})")
+        if device is not None and t.device != device:
+            _bad(f"{name} is on {t.device}, the cache on {device}")
+
+
+def _bf16():
+    import torch
+    return (torch.bfloat16,)
+
+
+def _code_dtypes():
+    import torch
+    return (torch.uint8, torch.float8_e4m3fn)
+
+
 def make_cache(k_cache, v_cache, k_scale=None, v_scale=None) -> pa_kv_cache:
     """Describe caches [num_blocks, num_kv_heads, block_size, head_dim]
-    (bf16, or uint8 E4M3 codes with fp32 [num_blocks, num_kv_heads] scales)."""
-    nb, hkv, bs, d = k_cache.shape
-    fp8 = k_cache.element_size() == 1
-    return pa_kv_cache(k_cache.data_ptr(), v_cache.data_ptr(),
-                       None if k_scale is None else k_scale.data_ptr(),
-                       None if v_scale is None else v_scale.data_ptr(),
-                       nb, hkv, bs, d, PA_KV_FP8_E4M3 if fp8 else PA_KV_BF16)
+    (bf16, or E4M3 codes as uint8 / float8_e4m3fn with fp32
+    [num_blocks, num_kv_heads] scales).  The tensors must outlive every call
+    that uses the returned descriptor."""
+    import torch
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        _bad("k_cache must be a 4-D tensor [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, bs, d = (int(x) for x in k_cache.shape)
+    fp8 = k_cache.dtype in _code_dtypes()
+    dtypes = _code_dtypes() if fp8 else _bf16()
+    ok = [_tensor(k_cache, "k_cache", dtypes),
+          _tensor(v_cache, "v_cache", (k_cache.dtype,), (nb, hkv, bs, d))]
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise PagedAttnError(PA_ERR_NULL_ARG, "an E4M3 cache needs k_scale and v_scale")
+        ok += [_tensor(k_scale, "k_scale", (torch.float32,), (nb, hkv)),
+               _tensor(v_scale, "v_scale", (torch.float32,), (nb, hkv))]
+    elif k_scale is not None or v_scale is not None:
+        _bad("a bf16 cache takes no scales")
+    _on_device(ok, k_cache.device)
+    c = pa_kv_cache(k_cache.data_ptr(), v_cache.data_ptr(),
+                    None if k_scale is None else k_scale.data_ptr(),
+                    None if v_scale is None else v_scale.data_ptr(),
+                    nb, hkv, bs, d, PA_KV_FP8_E4M3 if fp8 else PA_KV_BF16)
+    c.device = k_cache.device
+    return c
 
 
 def _host_i32(a):
@@ -102,12 +171,21 @@ def _host_i32(a):
 
 def kv_append(cache: pa_kv_cache, k_new, v_new, slot_mapping, stream=None):
     """Scatter new K/V rows [T, Hkv, d] (bf16) into the slots slot_mapping [T] (int64)."""
-    _check(lib.kv_append(C.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
-                         int(slot_mapping.shape[0]), _stream_ptr(stream)))
+    import torch
+    dev = getattr(cache, "device", None)
+    ok = [_tensor(slot_mapping, "slot_mapping", (torch.int64,), (None,))]
+    T = int(slot_mapping.shape[0])
+    shape = (T, cache.num_kv_heads, cache.head_dim)
+    ok += [_tensor(k_new, "k_new", _bf16(), shape), _tensor(v_new, "v_new", _bf16(), shape)]
+    _on_device(ok, dev)
+    _check(lib.kv_append(C.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+                         _stream_ptr(stream)))
 
 
 def pa_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache) -> int:
     h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    if h.shape != n.shape or h.ndim != 1:
+        _bad("hist_lens and incr_lens must be 1-D of equal length")
     r = lib.pa_workspace_size(h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p),
                               len(h), num_q_heads, C.byref(cache))
     if r == 0:
@@ -118,15 +196,44 @@ def pa_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache) -> 
 def paged_attn_forward(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale, out,
                        workspace, lse_out=None, stream=None):
     """Attention of q [total_q, Hq, d] over the paged cache; writes out (and lse_out)."""
+    import torch
     h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    if h.shape != n.shape or h.ndim != 1:
+        _bad("hist_lens and incr_lens must be 1-D of equal length")
+    dev = getattr(cache, "device", None)
+    total_q = int(n.astype(np.int64).sum())
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        _bad("q must be a 3-D tensor [total_q, num_q_heads, head_dim]")
+    hq = int(q.shape[1])
+    ok = [_tensor(q, "q", _bf16(), (total_q, hq, cache.head_dim)),
+          _tensor(out, "out", _bf16(), (total_q, hq, cache.head_dim))]
+    if lse_out is not None:
+        ok.append(_tensor(lse_out, "lse_out", (torch.float32,), (total_q, hq)))
+    ok.append(_tensor(block_tables, "block_tables", (torch.int32,), (None, None)))
+    if int(block_tables.shape[0]) < len(h):
+        _bad(f"block_tables has {int(block_tables.shape[0])} rows for {len(h)} sequences")
+    if not isinstance(workspace, torch.Tensor):
+        _bad("workspace must be a torch.Tensor")
+    ok.append(_tensor(workspace, "workspace", (workspace.dtype,)))
+    _on_device(ok, dev)
     _check(lib.paged_attn_forward(
         _ptr(q), C.byref(cache), _ptr(block_tables), int(block_tables.shape[1]),
-        h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), int(q.shape[1]),
+        h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq,
         float(scale), _ptr(out), _ptr(lse_out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _stream_ptr(stream)))
 
 
 def pa_debug_gather(cache: pa_kv_cache, block_table_row, ctx, k_out, v_out, stream=None):
+    """Raw gather of one sequence's first ctx tokens through a table row (test hook)."""
+    import torch
+    dev = getattr(cache, "device", None)
+    ok = [_tensor(block_table_row, "block_table_row", (torch.int32,), (None,))]
+    if int(block_table_row.shape[0]) * cache.block_size < int(ctx):
+        _bad(f"block_table_row covers {int(block_table_row.shape[0]) * cache.block_size} tokens, ctx {ctx}")
+    dt = _code_dtypes() if cache.dtype == PA_KV_FP8_E4M3 else _bf16()
+    shape = (int(ctx), cache.num_kv_heads, cache.head_dim)
+    ok += [_tensor(k_out, "k_out", dt, shape), _tensor(v_out, "v_out", dt, shape)]
+    _on_device(ok, dev)
     _check(lib.pa_debug_gather(C.byref(cache), _ptr(block_table_row), int(ctx), _ptr(k_out),
                                _ptr(v_out), _stream_ptr(stream)))
 
@@ -149,6 +256,20 @@ def pa_peak_read(buf, out, stream=None):
     """Enqueue a streaming read of the device buffer buf (out: int32 [PEAK_READ_THREADS])."""
     _check(lib.pa_peak_read(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(out),
                             _stream_ptr(stream)))
+
+
+def pa_device_shape():
+    """(compute units, XCDs) the planner cuts plans for on the current device."""
+    cus, xcds = C.c_int32(), C.c_int32()
+    _check(lib.pa_device_shape(C.byref(cus), C.byref(xcds)))
+    return cus.value, xcds.value
+
+
+def pa_debug_xcc_ids(out, stream=None):
+    """Enqueue out.numel() work-groups, each writing the XCD it ran on (out: int32, GPU)."""
+    import torch
+    _on_device([_tensor(out, "out", (torch.int32,), (None,))])
+    _check(lib.pa_debug_xcc_ids(_ptr(out), int(out.numel()), _stream_ptr(stream)))
 
 
 def pa_timing_enable(on: bool):

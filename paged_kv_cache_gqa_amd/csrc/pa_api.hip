@@ -76,13 +76,50 @@ pa_status check_cache(const pa_kv_cache *c) {
 // cut into 128-row prefill tiles.  Key ranges are split so that there are
 // enough similar-sized items to fill every compute unit; split items write
 // partials merged by LSE ([Agentic] §4.3.3).
-constexpr int kNumCUs = 256;
 #ifndef PA_DEC_ITEMS_PER_CU
 #define PA_DEC_ITEMS_PER_CU 4
 #endif
-constexpr int kDecodeTargetItems = PA_DEC_ITEMS_PER_CU * kNumCUs;
+constexpr int kDecodeItemsPerCU = PA_DEC_ITEMS_PER_CU;
 constexpr int kDecodeMinChunk = 2048;
-constexpr int kPrefillTargetItems = 8 * kNumCUs;
+constexpr int kPrefillItemsPerCU = 8;
+
+// The machine the plan is cut for: compute units and XCDs (chiplets, each
+// with its own L2) of the current device, queried once per device.  Without a
+// device (the host-only planning hooks on a machine with no GPU) the MI355X's
+// 256 CUs in 8 XCDs are assumed.  Work-group ids are dispatched round-robin
+// over the XCDs (work-group w runs on XCD w mod num_xcds); pa_debug_xcc_ids
+// lets a test check that on the GPU.
+struct MachineShape {
+  int32_t cus = 256;
+  int32_t xcds = 8;
+};
+
+MachineShape machine_shape() {
+  static std::mutex mu;
+  static std::vector<std::pair<int, MachineShape>> known;
+  static bool no_device = false;
+  std::lock_guard<std::mutex> lk(mu);
+  if (no_device) return MachineShape{};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    no_device = true;
+    return MachineShape{};
+  }
+  for (auto &k : known)
+    if (k.first == dev) return k.second;
+  MachineShape m;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) m.cus = v;
+  v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0 && m.cus % v == 0)
+    m.xcds = v;
+  else
+    m.xcds = 1;
+  (void)hipGetLastError();
+  known.push_back({dev, m});
+  return m;
+}
 constexpr int kPrefillMinChunk = 4096;
 constexpr int kMinGroupKeyTiles = 16;  // persistent launch: at least 1024 keys per work-group
 
@@ -160,7 +197,8 @@ constexpr int kGroupPieces = PA_GROUP_PIECES;
 #endif
 constexpr bool kPlanLpt = PA_PLAN_LPT;
 
-void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, Plan &P) {
+void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, const MachineShape &M,
+                     Plan &P) {
   std::vector<int32_t> pre;  // prefill tiles
   int32_t max_steps = 0;
   int64_t W = 0;
@@ -172,7 +210,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
     W += (int64_t)steps * hkv;
   }
   if (W == 0) return;
-  const int32_t nwg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kNumCUs, W / kMinGroupKeyTiles));
+  const int32_t nwg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(M.cus, W / kMinGroupKeyTiles));
   // chunk length (in steps) so that a work-group's range spans about
   // kGroupPieces (tile, chunk) pieces
   const int64_t units = (int64_t)pre.size() * hkv;
@@ -194,18 +232,18 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   // work-groups then start tiles of nearly equal length at key 0 together,
   // round after round, and share K/V in L2; no tile is split (no partials)
   // unless it exceeds the item cap.
-  constexpr int kXcds = 8;
-  const int32_t per_xcd = nwg / kXcds;
-  const bool lpt = kPlanLpt && nwg % kXcds == 0 && hkv % kXcds == 0 &&
-                   (int64_t)pre.size() * (hkv / kXcds) >= 8 * per_xcd;
+  const int32_t xcds = M.xcds;
+  const int32_t per_xcd = nwg / xcds;
+  const bool lpt = kPlanLpt && nwg % xcds == 0 && hkv % xcds == 0 &&
+                   (int64_t)pre.size() * (hkv / xcds) >= 8 * per_xcd;
   if (lpt) {
     std::vector<int32_t> order(pre.size());
     for (size_t k = 0; k < pre.size(); k++) order[k] = (int32_t)k;
     auto steps_of = [&](int32_t k) { return (int32_t)cdiv64(tiles[pre[k]].keys, kKeyTile); };
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return steps_of(x) > steps_of(y); });
-    for (int32_t x = 0; x < kXcds; x++) {
+    for (int32_t x = 0; x < xcds; x++) {
       std::vector<int64_t> load(per_xcd, 0);
-      for (int32_t kvh = x; kvh < hkv; kvh += kXcds)
+      for (int32_t kvh = x; kvh < hkv; kvh += xcds)
         for (int32_t k : order) {
           int32_t j = 0;
           for (int32_t q = 1; q < per_xcd; q++)
@@ -272,7 +310,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   }
   P.wg_first.assign(nwg + 1, 0);
   for (int32_t w = 0; w < nwg; w++) {
-    const int32_t rr = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;
+    const int32_t rr = nwg % xcds == 0 ? (w % xcds) * (nwg / xcds) + w / xcds : w;
     P.wg_first[w] = (int32_t)P.prefill.size();
     P.prefill.insert(P.prefill.end(), by_range[rr].begin(), by_range[rr].end());
   }
@@ -281,6 +319,9 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
 
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
                int32_t group, int32_t d, int32_t tile_rows, Plan &P, int32_t dq_bs = 0) {
+  const MachineShape M = machine_shape();
+  const int64_t decode_target_items = (int64_t)kDecodeItemsPerCU * M.cus;
+  const int64_t prefill_target_items = (int64_t)kPrefillItemsPerCU * M.cus;
   const int32_t dec_tokens = kDecodeRows / group;  // >= 1 for group <= 16
   const int32_t pre_tokens = tile_rows / group;
   std::vector<Tile> tiles;
@@ -309,13 +350,13 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
     }
   }
   const int64_t dchunk = std::min<int64_t>(
-      kMaxDecItemKeys, std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), kDecodeTargetItems)));
+      kMaxDecItemKeys, std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), decode_target_items)));
   int64_t pchunk = INT32_MAX;
-  if (np0 > 0 && np0 < kPrefillTargetItems)
-    pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, kPrefillTargetItems));
+  if (np0 > 0 && np0 < prefill_target_items)
+    pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, prefill_target_items));
 
   const bool persistent = tile_rows == kDmaTileRows;
-  if (persistent) plan_persistent(tiles, hkv, tile_rows, P);
+  if (persistent) plan_persistent(tiles, hkv, tile_rows, M, P);
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
   for (const Tile &t : tiles) {
@@ -759,6 +800,22 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
     e = timed(3, s, [&] { return launch_merge(m, n_few, n_many, many_rows, s); });
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
+  return PA_OK;
+}
+
+pa_status pa_device_shape(int32_t *num_cus, int32_t *num_xcds) {
+  if (!num_cus || !num_xcds) return fail(PA_ERR_NULL_ARG, "num_cus/num_xcds is NULL");
+  const MachineShape m = machine_shape();
+  *num_cus = m.cus;
+  *num_xcds = m.xcds;
+  return PA_OK;
+}
+
+pa_status pa_debug_xcc_ids(int32_t *out, int32_t n, void *stream) {
+  if (!out) return fail(PA_ERR_NULL_ARG, "out is NULL");
+  if (n < 1) return fail(PA_ERR_BAD_SHAPE, "n %d < 1", n);
+  hipError_t e = launch_xcc_ids(out, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "xcc id launch");
   return PA_OK;
 }
 

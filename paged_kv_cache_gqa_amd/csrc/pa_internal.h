@@ -155,6 +155,7 @@ constexpr int kPeakReadGroups = 256;   // streaming read: one 4-wave work-group 
 hipError_t launch_peak_mfma(float *out, int iters, hipStream_t s);
 hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+hipError_t launch_xcc_ids(int32_t *out, int n, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
 hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s);
 

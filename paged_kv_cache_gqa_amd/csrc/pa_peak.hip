@@ -97,4 +97,17 @@ hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *out, hipSt
   return hipGetLastError();
 }
 
+// Which XCD runs each work-group: work-group w writes the XCC id its waves
+// read from the hardware register (one 64-thread work-group per id).
+__global__ __launch_bounds__(64) void xcc_ids_kernel(int32_t *out, int n) {
+  int xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  if (threadIdx.x == 0 && (int)blockIdx.x < n) out[blockIdx.x] = xcc & 0xF;
+}
+
+hipError_t launch_xcc_ids(int32_t *out, int n, hipStream_t s) {
+  hipLaunchKernelGGL(xcc_ids_kernel, dim3(n), dim3(64), 0, s, out, n);
+  return hipGetLastError();
+}
+
 }  // namespace pa

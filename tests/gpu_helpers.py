@@ -7,9 +7,7 @@ import oracle
 import workloads as W
 from tests.helpers import bits16, host_caches
 
-# parity bars: max abs / mean abs error against the fp64 oracle
-TOL_BF16 = (2e-2, 2e-3)
-TOL_FP8 = (6e-2, 6e-3)
+from tests.parity import assert_lse, assert_parity  # noqa: F401  (the bars)
 
 
 def gpu_caches(batch, host=None):
@@ -49,19 +47,3 @@ def forward(pa, batch, c, want_lse=False, stream=None, q=None, hist=None, incr=N
                      device=dev) if want_lse else None
     pa.paged_attn_forward(q, c, bt, hist, incr, spec.scale, out, ws, lse_out=lse, stream=stream)
     return out, lse
-
-
-def errors(out_gpu, ref):
-    got = out_gpu.detach().float().cpu().numpy().astype(np.float64)
-    diff = np.abs(got - ref)
-    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
-    return float(np.nanmax(diff)) if diff.size else 0.0, float(np.mean(diff)) if diff.size else 0.0, float(rel), bool(np.isnan(got).any())
-
-
-def assert_parity(out_gpu, ref, fp8=False, what=""):
-    mx, mean, rel, has_nan = errors(out_gpu, ref)
-    tmax, tmean = TOL_FP8 if fp8 else TOL_BF16
-    print(f"[parity] {what}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_fro={rel:.3e}", flush=True)
-    assert not has_nan, f"{what}: NaN in output"
-    assert mx <= tmax and mean <= tmean, (what, mx, mean, rel)
-    return mx, mean, rel

@@ -48,3 +48,56 @@ def bf16_bits_of(x: np.ndarray) -> np.ndarray:
 
 def bf16_values(bits: np.ndarray) -> np.ndarray:
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+_E4M3_LUT = None
+
+
+def key_values(caches, bt_row, ctx):
+    """Values [ctx, hkv, d] (fp64) of one sequence's keys from host caches,
+    through the oracle's gather and its codecs (test-side bound computations)."""
+    global _E4M3_LUT
+    kc, _, ks, _, dt = caches
+    raw = oracle.gather(kc, bt_row, ctx)
+    if dt == oracle.KV_BF16:
+        return bf16_values(raw)
+    if _E4M3_LUT is None:
+        _E4M3_LUT = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    bs = kc.shape[2]
+    blk = bt_row[np.arange(ctx) // bs]
+    return _E4M3_LUT[raw] * ks[blk][:, :, None].astype(np.float64)
+
+
+def row_paths(batch):
+    """Per q row, the kernel family that computes it: 'w48' (the 384-row
+    prefill, head dim 128: bf16-rounded scaled query) or 'exact' (decode
+    kernels and the head-dim-64 prefill: exact query, fp32 probability sums)."""
+    spec = batch.spec
+    G = spec.num_q_heads // spec.num_kv_heads
+    out = []
+    for s in range(spec.num_seqs):
+        n = int(batch.incr[s])
+        decode_class = n <= 16 // G
+        out += ["w48" if (spec.head_dim == 128 and not decode_class) else "exact"] * n
+    return out
+
+
+def lse_bounds(batch, caches):
+    """Per (q row, head) LSE bound [total_q, hq] for the row's kernel family."""
+    from tests.parity import LSE_EXACT, w48_lse_bound
+    spec = batch.spec
+    G = spec.num_q_heads // spec.num_kv_heads
+    fp8 = spec.kv_dtype == "e4m3"
+    paths = row_paths(batch)
+    bound = np.full((spec.total_q, spec.num_q_heads), LSE_EXACT)
+    q = bf16_values(bits16(batch.q))
+    r0 = 0
+    for s in range(spec.num_seqs):
+        n = int(batch.incr[s])
+        if n and paths[r0] == "w48":
+            ctx = int(batch.hist[s]) + n
+            keys = key_values(caches, batch.block_tables[s], ctx)
+            for h in range(spec.num_q_heads):
+                bound[r0:r0 + n, h] = w48_lse_bound(q[r0:r0 + n, h], keys[:, h // G], spec.scale, fp8)
+        r0 += n
+    return bound

@@ -282,3 +282,69 @@ def test_measurement_hooks_reject_bad_arguments(palib):
     assert pa.lib.pa_peak_read(FAKE, 4096 + 16, FAKE, None) == pa.PA_ERR_BAD_SHAPE
     assert pa.lib.pa_peak_read(FAKE, 0, FAKE, None) == pa.PA_ERR_BAD_SHAPE
     assert "4096" in pa.pa_last_error()
+
+
+# ---------------------------------------------------------------------------
+# The binding's own checks: a tensor of the wrong dtype, shape, layout or
+# device is refused before the library sees its pointer.  (Dtype, shape and
+# layout are checked before the device, so CPU tensors reach every check.)
+def _expect_bad(pa, fn, what):
+    with pytest.raises(pa.PagedAttnError) as e:
+        fn()
+    assert what in str(e.value), str(e.value)
+
+
+def test_binding_rejects_bad_tensors(palib):
+    import torch
+    pa = palib
+    bf, i32, i64 = torch.bfloat16, torch.int32, torch.int64
+    kc = torch.zeros((4, 2, 16, 64), dtype=bf)
+    # caches
+    _expect_bad(pa, lambda: pa.make_cache(kc.float(), kc.float()), "dtype")
+    _expect_bad(pa, lambda: pa.make_cache(kc, kc[:3]), "shape")
+    _expect_bad(pa, lambda: pa.make_cache(kc, kc.to(torch.uint8)), "dtype")
+    _expect_bad(pa, lambda: pa.make_cache(kc, kc), "GPU tensor")
+    _expect_bad(pa, lambda: pa.make_cache(kc.transpose(2, 3).contiguous().transpose(2, 3), kc),
+                "contiguous")
+    c8 = torch.zeros((4, 2, 16, 64), dtype=torch.uint8)
+    with pytest.raises(pa.PagedAttnError):
+        pa.make_cache(c8, c8)  # E4M3 without scales
+    _expect_bad(pa, lambda: pa.make_cache(c8, c8, torch.ones(4, 3), torch.ones(4, 2)), "shape")
+    _expect_bad(pa, lambda: pa.make_cache(c8, c8, torch.ones(4, 2, dtype=torch.float64),
+                                          torch.ones(4, 2)), "dtype")
+    _expect_bad(pa, lambda: pa.make_cache(kc, kc, torch.ones(4, 2), torch.ones(4, 2)), "no scales")
+    # a descriptor for the calls below (raw fields: never dereferenced)
+    c = cache(pa, num_blocks=4, num_kv_heads=2, block_size=16, head_dim=64)
+    k_new = torch.zeros((3, 2, 64), dtype=bf)
+    slots = torch.zeros(3, dtype=i64)
+    _expect_bad(pa, lambda: pa.kv_append(c, k_new, k_new, slots.to(i32)), "dtype")
+    _expect_bad(pa, lambda: pa.kv_append(c, k_new, k_new, torch.zeros(4, dtype=i64)), "shape")
+    _expect_bad(pa, lambda: pa.kv_append(c, k_new[:, :1], k_new, slots), "shape")
+    _expect_bad(pa, lambda: pa.kv_append(c, k_new, k_new.float(), slots), "dtype")
+    _expect_bad(pa, lambda: pa.kv_append(c, k_new, k_new, slots), "GPU tensor")
+    # forward: q rows must equal sum(incr); out/lse shapes follow q; tables int32 with a row
+    # per sequence
+    q = torch.zeros((5, 8, 64), dtype=bf)
+    out = torch.zeros_like(q)
+    bt = torch.zeros((2, 4), dtype=i32)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    call = lambda **kw: pa.paged_attn_forward(**{**dict(q=q, cache=c, block_tables=bt,
+                                                        hist_lens=[10, 3], incr_lens=[4, 1],
+                                                        scale=0.125, out=out, workspace=ws), **kw})
+    _expect_bad(pa, lambda: call(incr_lens=[4, 2]), "shape")
+    _expect_bad(pa, lambda: call(hist_lens=[10]), "equal length")
+    _expect_bad(pa, lambda: call(q=q.float()), "dtype")
+    _expect_bad(pa, lambda: call(q=torch.zeros((5, 8, 128), dtype=bf)), "shape")
+    _expect_bad(pa, lambda: call(out=torch.zeros((5, 4, 64), dtype=bf)), "shape")
+    _expect_bad(pa, lambda: call(lse_out=torch.zeros((5, 8), dtype=torch.float64)), "dtype")
+    _expect_bad(pa, lambda: call(block_tables=bt.to(i64)), "dtype")
+    _expect_bad(pa, lambda: call(block_tables=bt[:1]), "rows")
+    _expect_bad(pa, lambda: call(block_tables=bt.t()), "contiguous")
+    _expect_bad(pa, lambda: call(workspace=None), "workspace")
+    _expect_bad(pa, lambda: call(), "GPU tensor")
+    _expect_bad(pa, lambda: pa.pa_debug_gather(c, torch.zeros(2, dtype=i32), 40,
+                                               torch.zeros((40, 2, 64), dtype=bf),
+                                               torch.zeros((40, 2, 64), dtype=bf)), "covers")
+    _expect_bad(pa, lambda: pa.pa_debug_gather(c, torch.zeros(4, dtype=i32), 40,
+                                               torch.zeros((40, 2, 32), dtype=bf),
+                                               torch.zeros((40, 2, 64), dtype=bf)), "shape")

@@ -87,57 +87,114 @@ def gpu_full_step(palib, b, host_codes=None):
     return out, c, caches
 
 
-def sample_rows(n, tile_tokens, rng, k=10):
-    rows = {0, n - 1, min(n - 1, tile_tokens - 1), min(n - 1, tile_tokens)}
+def plan_tiles(palib, spec):
+    """(first row, tokens) of every prefill tile the library's planner makes
+    for this step, from its work list (pa_debug_plan): the tile height is the
+    kernel's, so boundary rows are sampled where tiles really meet."""
+    fp8 = spec.kv_dtype == "e4m3"
+    c = palib.pa_kv_cache(0x1000, 0x1000, 0x1000 if fp8 else None, 0x1000 if fp8 else None, 1,
+                          spec.num_kv_heads, spec.block_size, spec.head_dim,
+                          palib.PA_KV_FP8_E4M3 if fp8 else palib.PA_KV_BF16)
+    items, counts = palib.pa_debug_plan(spec.hist, spec.incr, spec.num_q_heads, c)
+    pre = items[:counts[0]]
+    return sorted({(int(r), int(n)) for r, n in zip(pre[:, 2], pre[:, 4])})
+
+
+def tile_boundary_rows(tiles, seq_row0, n, rng, k=8):
+    """Local rows of one sequence's increment: the first and last row of its
+    first, middle and last tiles and of the tiles around them, plus k random rows."""
+    mine = [(r - seq_row0, t) for r, t in tiles if seq_row0 <= r < seq_row0 + n]
+    rows = {0, n - 1}
+    for i in sorted({0, 1, len(mine) // 2, len(mine) - 2, len(mine) - 1}):
+        if 0 <= i < len(mine):
+            r, t = mine[i]
+            rows |= {r, r + t - 1}
     rows |= set(int(x) for x in rng.integers(0, n, size=k))
     return sorted(rows)
 
 
-@pytest.mark.parametrize("spec", [W.incremental(), W.initial(),
-                                  W.incremental(131_072, 2_700, "incremental_128k")],
-                         ids=["incremental_45.7k_to_48.4k", "initial_45.7k", "incremental_128k"])
-def test_single_session_prefill(palib, spec):
-    print(f"[case] {spec.name} hist={spec.hist} incr={spec.incr}", flush=True)
+def local_needles(b, rows):
+    """(index into `rows`, head) of the batch's needles among the sampled rows."""
+    at = {r: i for i, r in enumerate(rows)}
+    return [(at[r], h) for r, h, _, _ in b.needles if r in at]
+
+
+PREFILL = [W.incremental(), W.initial(), W.incremental(131_072, 2_700, "incremental_128k")]
+
+
+@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
+@pytest.mark.parametrize("spec", PREFILL, ids=["incremental_45.7k_to_48.4k", "initial_45.7k",
+                                               "incremental_128k"])
+def test_single_session_prefill(palib, spec, needled):
+    tiles = plan_tiles(palib, spec)
+    rows = tile_boundary_rows(tiles, 0, spec.incr[0], np.random.default_rng(1))
+    if needled:
+        if spec.hist[0] == 0:
+            pytest.skip("no history to hold a needle")
+        spec = W.with_needles(spec, needles=[(0, r) for r in rows[::2]])
+    print(f"[case] {spec.name} hist={spec.hist} incr={spec.incr} needled={needled} "
+          f"tiles={len(tiles)} rows={rows}", flush=True)
     b = W.make_batch(spec, DEV)
     sub = compact_subset(b, [0])
     out, _, _ = gpu_full_step(palib, b)
-    rows = sample_rows(spec.incr[0], 128 // (spec.num_q_heads // spec.num_kv_heads),
-                       np.random.default_rng(1))
     ref, _ = oracle_on_subset(sub, spec, rows)
-    assert_parity(out[rows], ref, False, spec.name)
+    assert_parity(out[rows], ref, False, spec.name, needles=local_needles(b, rows))
 
 
-def test_decode_batch(palib):
+@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
+def test_decode_batch(palib, needled):
     spec = W.decode_batch()
-    print(f"[case] decode_batch sessions=64 sum_ctx={sum(spec.hist) + 64}", flush=True)
-    b = W.make_batch(spec, DEV)
     ctx = np.array(spec.hist) + 1
     seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 7, 33, 50})
+    if needled:
+        spec = W.with_needles(spec, needles=[(s, 0) for s in seqs])
+    print(f"[case] decode_batch sessions=64 sum_ctx={sum(spec.hist) + 64} needled={needled}", flush=True)
+    b = W.make_batch(spec, DEV)
     sub = compact_subset(b, seqs)
     out, _, _ = gpu_full_step(palib, b)
     ref, _ = oracle_on_subset(sub, spec, list(range(len(seqs))))
-    assert_parity(out[torch.as_tensor(sub["rows"], device=DEV)], ref, False, "decode_batch")
+    assert_parity(out[torch.as_tensor(sub["rows"], device=DEV)], ref, False, "decode_batch",
+                  needles=local_needles(b, list(sub["rows"])))
 
 
-def test_mixed_step_with_shared_prefix(palib):
+@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
+def test_mixed_step_with_shared_prefix(palib, needled):
     spec = W.mixed()
-    print(f"[case] mixed incr={spec.incr[:4]}", flush=True)
-    b = W.make_batch(spec, DEV)
     seqs = [0, 3, 4, 5, 11, 12, 51]
+    n0, n3 = spec.incr[0], spec.incr[3]
+    tiles = plan_tiles(palib, spec)
+    rs = np.random.default_rng(2)
+    loc0 = tile_boundary_rows(tiles, 0, n0, rs, k=3)
+    row3 = int(np.sum(spec.incr[:3]))
+    loc3 = tile_boundary_rows(tiles, row3, n3, rs, k=3)
+    if needled:
+        spec = W.with_needles(spec, needles=[(0, loc0[0]), (0, loc0[-1]), (3, loc3[len(loc3) // 2])]
+                              + [(s, 0) for s in (4, 5, 11, 12, 51)])
+    print(f"[case] mixed incr={spec.incr[:4]} needled={needled}", flush=True)
+    b = W.make_batch(spec, DEV)
     sub = compact_subset(b, seqs)
     out, _, _ = gpu_full_step(palib, b)
-    n0, n3 = spec.incr[0], spec.incr[3]
-    local = [0, n0 // 2, n0 - 1, n0, n0 + n3 - 1] + list(range(n0 + n3, n0 + n3 + 5))
+    local = loc0 + [n0 + r for r in loc3] + list(range(n0 + n3, n0 + n3 + 5))
     ref, _ = oracle_on_subset(sub, spec, local)
-    assert_parity(out[torch.as_tensor(sub["rows"][local], device=DEV)], ref, False, "mixed")
+    grows = [int(sub["rows"][i]) for i in local]
+    assert_parity(out[torch.as_tensor(grows, device=DEV)], ref, False, "mixed",
+                  needles=local_needles(b, grows))
 
 
-def test_long_context_fp8(palib):
+@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
+def test_long_context_fp8(palib, needled):
     """1M-token history in E4M3 (block 64): the incremental prefill of 4,096
     tokens, then 256 decode steps (append one token, attend); sampled rows of
-    the prefill and the first and last decode steps are checked."""
+    the prefill (tile boundaries from the plan) and the first and last decode
+    steps are checked.  The needled variant plants needles for sampled
+    prefill rows and for both checked decode steps."""
     spec = W.long_context()
-    print("[case] long_context hist=1044480 incr=4096 e4m3", flush=True)
+    tiles = plan_tiles(palib, spec)
+    rows = tile_boundary_rows(tiles, 0, spec.incr[0], np.random.default_rng(3), k=2)
+    checked = {1, 256}
+    if needled:
+        spec = W.with_needles(spec, needles=[(0, r) for r in rows[::2]], decode_steps=sorted(checked))
+    print(f"[case] long_context hist=1044480 incr=4096 e4m3 needled={needled} rows={rows}", flush=True)
     b = W.make_batch(spec, DEV)
     kh, vh = bits16(b.k_pool), bits16(b.v_pool)
     ks, vs = b.k_scale.cpu().numpy(), b.v_scale.cpu().numpy()
@@ -151,15 +208,13 @@ def test_long_context_fp8(palib):
     # GPU cache after the quantising append equals the oracle's, byte for byte
     assert torch.equal(caches[0].cpu(), torch.from_numpy(kc))
     assert torch.equal(caches[1].cpu(), torch.from_numpy(vc))
-    rows = [0, 1, 2047, 4095]
     t = time.time()
     ref, _ = oracle.attention(bits16(b.q), kc, vc, ks, vs, oracle.KV_E4M3, b.block_tables, b.hist,
                               b.incr, 32, spec.scale, rows=rows)
     print(f"[oracle] prefill rows in {time.time() - t:.1f}s", flush=True)
-    assert_parity(out[rows], ref, True, "long_context prefill")
+    assert_parity(out[rows], ref, True, "long_context prefill", needles=local_needles(b, rows))
     # decode steps
     first = 1_048_576
-    checked = {1, 256}
     for step in range(1, 257):
         q, k1, v1 = W.decode_step_tokens(spec, step, DEV)
         pos = first + step - 1
@@ -173,7 +228,8 @@ def test_long_context_fp8(palib):
                              slot.cpu().numpy())
             refd, _ = oracle.attention(bits16(q), kc, vc, ks, vs, oracle.KV_E4M3, b.block_tables,
                                        [pos], [1], 32, spec.scale)
-            assert_parity(outd, refd, True, f"long_context decode step {step}")
+            nd = [(0, b.decode_needles[step][0])] if step in b.decode_needles else []
+            assert_parity(outd, refd, True, f"long_context decode step {step}", needles=nd)
         else:
             # keep the oracle's cache in step with the GPU's
             oracle.kv_append(kc, vc, ks, vs, oracle.KV_E4M3, bits16(k1), bits16(v1),

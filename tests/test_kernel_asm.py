@@ -5,8 +5,15 @@ the hazards of their operands.  The ISA requires 5 wait states between a
 VALU write of an SGPR (v_readfirstlane) and a vector-memory instruction that
 reads it, and 1 wait state between a scalar write of M0 and a buffer load
 that writes LDS.  This test compiles the kernels to assembly and checks every
-such load.  It also checks that no kernel spills to scratch and that no
-packed fp32 VALU instruction was generated.
+such load: the instruction right before it must be the asm's own s_nop of at
+least 4 (5 wait states), whatever the compiler put before the asm block, and
+the distances are measured as well.  (A microbenchmark that issued these
+loads without the padding made the GPU fault: the compiler had placed the
+v_readfirstlane that writes the descriptor's base word directly before the
+load, which then read a stale base address.)  It also checks that the
+key-step loops run without scratch spills (the 384-row kernel may spill a few
+per-item values outside them) and that no packed fp32 VALU instruction was
+generated.
 """
 import os
 import re
@@ -68,6 +75,8 @@ def test_lds_dma_hazards_padded(attention_asm):
             if not (line.startswith("buffer_load") and " lds" in line):
                 continue
             checked += 1
+            prev = lines[k - 1].split()
+            assert prev[0] == "s_nop" and int(prev[1], 0) >= 4, f"{name}: unpadded LDS load: {line}"
             rsrc = _sgprs(line.split(None, 1)[1].split(",")[1].strip())
             assert rsrc, line
             dist, m0_done, sgpr_done = 0, False, False

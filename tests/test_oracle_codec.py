@@ -99,3 +99,46 @@ def test_division_is_ieee_binary32(scale):
         ref = xs / s
     got = np.array([oracle.div_f32(x, s) for x in xs], dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _random_pool(rng, nb, hkv, bs, d, nan_frac=0.05):
+    vals = (rng.standard_normal((nb, hkv, bs, d)) * rng.choice([1e-3, 0.3, 2.0, 50.0], size=(nb, hkv, 1, 1)))
+    bits = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bits = bits.copy()
+    bits.reshape(-1)[rng.random(bits.size) < nan_frac] = 0x7FC0  # poisoned slots
+    return bits
+
+
+def test_quantize_pool_vs_torch_cast_and_kv_append():
+    """orc_e4m3_quantize_pool (the quantised history both sides start from):
+    every element equals torch's float8_e4m3fn cast of the fp32 quotient
+    x / scale[block, head] (the scale of its own block and head, with scales of
+    the amax / 448 form plus a few arbitrary ones), NaN slots give a NaN code,
+    and the whole pool equals writing every token through the oracle's
+    kv_append into an empty E4M3 cache."""
+    rng = np.random.default_rng(21)
+    nb, hkv, bs, d = 13, 3, 16, 64
+    bits = _random_pool(rng, nb, hkv, bs, d)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float()
+    amax = torch.nan_to_num(x, nan=0.0).abs().amax(dim=(2, 3))
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    sc[0, 1] = 0.37  # scales not tied to the content: saturating and tiny codes
+    sc[5, 2] = 3.1e-5
+    scn = sc.numpy().astype(np.float32)
+    got = oracle.quantize_pool(bits, scn)
+    q = x / sc[:, :, None, None]
+    fin = torch.isfinite(q) & (q.abs() <= 448.0)
+    ref = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    fin = fin.numpy()
+    assert np.array_equal(got[fin], ref[fin])
+    nan = torch.isnan(x).numpy()
+    assert np.all((got[nan] & 0x7F) == 0x7F)
+    big = ~fin & ~nan  # quotients beyond 448 saturate
+    assert big.any() and np.all((got[big] & 0x7F) == 0x7E)
+    # the same bytes through kv_append, one token (all heads) per slot
+    cache_k = np.zeros((nb, hkv, bs, d), np.uint8)
+    cache_v = np.zeros_like(cache_k)
+    tok = bits.transpose(0, 2, 1, 3).reshape(nb * bs, hkv, d)  # [slot][head][d]
+    slots = np.arange(nb * bs, dtype=np.int64)
+    oracle.kv_append(cache_k, cache_v, scn, scn, oracle.KV_E4M3, tok, tok, slots)
+    assert np.array_equal(cache_k, got) and np.array_equal(cache_v, got)

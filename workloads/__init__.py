@@ -20,18 +20,27 @@ cited in full):
     between running (decode) and newly admitted (prefill) requests.
 
 Random streams: numpy PCG64 seeded by SeedSequence([cfg, stream, ...]) for
-lengths (stream 0) and block placement (stream 1); torch generators seeded from
-the same SeedSequence family for q (2), k (3), v (4) and decode-step tokens (5).
+lengths (stream 0), block placement (stream 1) and needle placement (6); torch
+generators seeded from the same SeedSequence family for q (2), k (3), v (4) and
+decode-step tokens (5).
+
 K/V history values are drawn per sequence in logical order and then placed, so
 two batches that differ only in placement hold identical logical content.
 Every pool slot that holds no history token (spare blocks, tail slots, the
 slots the step's new tokens will fill) is poisoned with NaN.
+
+Needles (parity inputs only): a chosen (query row, head) gets one history key
+equal to twice its own query vector (exact in bf16), at a seeded history
+position.  Its logit, scale * 2 |q|^2 ~ 22.6 at d 128, outweighs the other keys'
+N(0, 1) logits even over a million keys, so that row's output is close to the
+needle's value vector (|o| ~ 1 instead of ~ sqrt(e / n)): an output computed
+from the wrong blocks, or not at all, is then far outside any tolerance.
 """
 from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 import torch
@@ -54,16 +63,18 @@ def _torch_gen(device, *key) -> torch.Generator:
     return g
 
 
-def randn_bf16(shape, device, *key, chunk_elems: int = 1 << 26) -> torch.Tensor:
-    """N(0,1) fp32 draws rounded to bf16 (round-to-nearest-even), chunked."""
+def randn_bf16(shape, device, *key, chunk_elems: int = 1 << 26, std: float = 1.0) -> torch.Tensor:
+    """N(0, std^2) fp32 draws rounded to bf16 (round-to-nearest-even), chunked."""
     g = _torch_gen(device, *key)
     out = torch.empty(shape, dtype=torch.bfloat16, device=device)
     flat = out.view(-1)
     n = flat.numel()
     for s in range(0, n, chunk_elems):
         e = min(n, s + chunk_elems)
-        flat[s:e] = torch.randn(e - s, generator=g, device=device, dtype=torch.float32).to(
-            torch.bfloat16)
+        x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        flat[s:e] = x.to(torch.bfloat16)
     return out
 
 
@@ -86,6 +97,9 @@ class Spec:
     pool_blocks: Optional[int] = None  # force an exact pool size (C1: 18 blocks)
     extra_blocks_per_seq: int = 0    # table capacity beyond the current context
     scale_tokens: Optional[List[int]] = None  # e4m3: scales cover content up to this length
+    q_std: float = 1.0               # standard deviation of q (logit std ~ q_std)
+    needles: List[Tuple[int, int]] = field(default_factory=list)  # (seq, row of its increment)
+    decode_needle_steps: List[int] = field(default_factory=list)  # single-session decode steps
 
     @property
     def num_seqs(self):
@@ -115,6 +129,10 @@ class Batch:
     v_pool: torch.Tensor
     k_scale: Optional[torch.Tensor] = None   # fp32 [nb, Hkv] (e4m3 only)
     v_scale: Optional[torch.Tensor] = None
+    # planted needles: (global q row, q head, seq, history position); decode-step
+    # needles: {step: (q head, history position)}
+    needles: List[Tuple[int, int, int, int]] = field(default_factory=list)
+    decode_needles: dict = field(default_factory=dict)
 
     @property
     def max_blocks(self):
@@ -193,7 +211,7 @@ def make_batch(spec: Spec, device="cpu") -> Batch:
     fill_history(k_pool, 3)
     fill_history(v_pool, 4)
 
-    q = randn_bf16((total_q, hq, d), device, spec.cfg, 2)
+    q = randn_bf16((total_q, hq, d), device, spec.cfg, 2, std=spec.q_std)
     k_new = randn_bf16((total_q, hkv, d), device, spec.cfg, 3, 2)
     v_new = randn_bf16((total_q, hkv, d), device, spec.cfg, 4, 2)
 
@@ -206,9 +224,53 @@ def make_batch(spec: Spec, device="cpu") -> Batch:
     slot_mapping = torch.as_tensor(slots, device=device)
 
     b = Batch(spec, bt, pool, hist, incr, slot_mapping, q, k_new, v_new, k_pool, v_pool)
+    if spec.needles or spec.decode_needle_steps:
+        _plant_needles(b)
     if spec.kv_dtype == "e4m3":
         b.k_scale, b.v_scale = _amax_scales(b, scale_ctx)
     return b
+
+
+def _plant_needles(b: Batch):
+    """Set one seeded history key per needle to 2 x the needled query vector
+    (a power-of-two multiple: exact in bf16).  Positions are distinct."""
+    spec = b.spec
+    bs, G = spec.block_size, spec.num_q_heads // spec.num_kv_heads
+    rng = _np_rng(spec.cfg, 6, spec.perm_seed)
+    rowstart = np.concatenate([[0], np.cumsum(b.incr.astype(np.int64))])
+    used = set()
+
+    def plant(seq, qvec_heads, what):
+        h = int(rng.integers(0, spec.num_q_heads))
+        hist = int(b.hist[seq])
+        assert hist > 0, f"needle {what} needs a history"
+        while True:
+            j = int(rng.integers(0, hist))
+            if (seq, j) not in used:
+                break
+        used.add((seq, j))
+        phys = int(b.block_tables[seq, j // bs])
+        key = (2 * qvec_heads[h].float()).to(torch.bfloat16)
+        b.k_pool[phys, h // G, j % bs, :] = key
+        return h, j
+
+    for seq, i in spec.needles:
+        assert 0 <= i < int(b.incr[seq])
+        row = int(rowstart[seq]) + i
+        h, j = plant(seq, b.q[row], f"({seq}, {i})")
+        b.needles.append((row, h, seq, j))
+    for step in spec.decode_needle_steps:
+        q, _, _ = decode_step_tokens(spec, step, b.q.device)
+        b.decode_needles[step] = plant(0, q[0], f"step {step}")
+
+
+def with_needles(spec: Spec, needles=(), decode_steps=(), q_std: float = None) -> Spec:
+    """A copy of `spec` with planted needles (parity inputs)."""
+    import dataclasses
+    kw = dict(needles=list(needles), decode_needle_steps=list(decode_steps))
+    if q_std is not None:
+        kw["q_std"] = q_std
+    return dataclasses.replace(spec, **kw)
 
 
 def decode_step_tokens(spec: Spec, step: int, device="cpu"):
