@@ -416,8 +416,9 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   const int grp = wave >> 2;
   const int c16 = lane & 15, g = lane >> 4;
 
-  // Q is held pre-multiplied by scale * log2(e) (rounded to bf16), so the
-  // score MFMAs produce base-2 exponents directly.
+  // Q as stored (bf16, exact): the score MFMAs produce raw q.k, and one fused
+  // multiply-add per score applies scale * log2(e) and the row's reference
+  // exponent in fp32.
   bf16x8 qf[RB][NCQ];
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
@@ -429,9 +430,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
 #pragma unroll
     for (int c = 0; c < NCQ; c++) {
       uint4 v = act ? gload16(qrow + (32 * c + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
-      const bf16x8 q = as_bf16x8(v);
-#pragma unroll
-      for (int e = 0; e < 8; e++) qf[rb][c][e] = (__bf16)((float)q[e] * scale_log2);
+      qf[rb][c] = as_bf16x8(v);
     }
   }
 
@@ -510,8 +509,8 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
   };
 
-  // m[rb]: the row's reference exponent (base 2).  The score MFMAs start
-  // from -m, so they yield s - m and a probability is one exp2; m moves up
+  // m[rb]: the row's reference exponent (base 2).  A score's exponent is
+  // fma(q.k, scale * log2 e, -m), so a probability is one exp2; m moves up
   // only when a step's maximum exceeds it by kRescaleSlack, and while the
   // row has no weight yet it follows the maximum.
   // o[NDB][rb] is the row sum l: the value product runs one more d-block
@@ -520,16 +519,16 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   f32x4 o[NDB + 1][RB];
   f32x4 S[2][RB];
   bf16x8 pb[RB];
-  f32x4 negm[RB];  // -m[rb] in all four elements; m[rb] itself is not kept
+  float negm[RB];  // -m[rb]; m[rb] itself is not kept
   int all_live = 0;  // every row of the wave has weight (wave-uniform)
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
-    negm[rb] = f32x4{};
+    negm[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
   }
 
-  auto cinit = [&](int rb) __attribute__((always_inline)) { return negm[rb]; };
+  auto cinit = [&](int) __attribute__((always_inline)) { return f32x4{}; };
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
   // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
   auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
@@ -603,6 +602,12 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       }
   };
   auto softmax = [&](auto masked_tag, int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) S[kb][rb][r] = __builtin_fmaf(S[kb][rb][r], scale_log2, negm[rb]);
     if constexpr (decltype(masked_tag)::value) {
       const int key0 = t * kW48Step + 4 * g;
 #pragma unroll
@@ -731,7 +736,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     const float lt = o[NDB][rb][0];
     if (tok >= it.nq) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float mrow = -negm[rb][0];
+    const float mrow = -negm[rb];
     const float lse2 = lt > 0.f ? mrow + __log2f(lt) : -INFINITY;
     if (it.part < 0) {
       const int64_t orow = (int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq;

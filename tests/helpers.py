@@ -70,8 +70,8 @@ def key_values(caches, bt_row, ctx):
 
 def row_paths(batch):
     """Per q row, the kernel family that computes it: 'w48' (the 384-row
-    prefill, head dim 128: bf16-rounded scaled query) or 'exact' (decode
-    kernels and the head-dim-64 prefill: exact query, fp32 probability sums)."""
+    prefill, head dim 128: l summed from bf16-rounded probabilities) or
+    'exact' (decode kernels and the head-dim-64 prefill: fp32 probability sums)."""
     spec = batch.spec
     G = spec.num_q_heads // spec.num_kv_heads
     out = []
@@ -95,9 +95,12 @@ def lse_bounds(batch, caches):
     for s in range(spec.num_seqs):
         n = int(batch.incr[s])
         if n and paths[r0] == "w48":
-            ctx = int(batch.hist[s]) + n
-            keys = key_values(caches, batch.block_tables[s], ctx)
-            for h in range(spec.num_q_heads):
-                bound[r0:r0 + n, h] = w48_lse_bound(q[r0:r0 + n, h], keys[:, h // G], spec.scale, fp8)
+            if not fp8:
+                bound[r0:r0 + n] = w48_lse_bound(q[r0:r0 + 1, 0], None, spec.scale, False)[0]
+            else:
+                ctx = int(batch.hist[s]) + n
+                keys = key_values(caches, batch.block_tables[s], ctx)
+                for h in range(spec.num_q_heads):
+                    bound[r0:r0 + n, h] = w48_lse_bound(q[r0:r0 + n, h], keys[:, h // G], spec.scale, True)
         r0 += n
     return bound

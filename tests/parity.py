@@ -12,17 +12,18 @@ error near 1.  The bf16 arithmetic itself gives about 2.4e-3 (the bf16
 rounding of the output and of the probabilities, each about 1.6e-3 RMS
 relative, plus the logit error of a bf16-rounded query).
 
-LSE (natural log): paths that keep the query exact and sum fp32 probabilities
-(the decode kernels, the head-dim-64 prefill) are held to max 2e-3.  The
-384-row prefill (head dim 128) holds q * scale * log2(e) rounded to bf16 and
-sums bf16-rounded probabilities (and, for E4M3 KV, reads keys rounded to
-bf16); its a-priori bound for a row r and head h is
+LSE (natural log): paths that sum fp32 probabilities (the decode kernels,
+the head-dim-64 prefill) are held to max 2e-3.  The 384-row prefill (head dim
+128) sums the bf16-rounded probabilities its value product uses (l from the
+matrix cores), and for E4M3 KV it reads keys rounded to bf16
+(code * scale); its a-priori bound for a row r and head h is
     2^-8 * (1 + k * scale * max_j sum_e |q_re| |k_je|) + 1e-4,
-k = 1 for bf16 KV and 2 for E4M3 KV: bf16 rounding moves each rounded factor
-by at most 2^-8 of itself, so each logit by at most 2^-8 * scale * sum_e
-|q_e k_e| per rounded operand, and the log of a sum of exponentials moves by
-at most the largest move of its terms; the bf16 probabilities move l by at
-most 2^-8 relative.  Every path is also held to mean 2e-3.
+k = 0 for bf16 KV (the query and keys enter the score exactly) and 1 for
+E4M3 KV: bf16 rounding moves each probability, and each rounded key element,
+by at most 2^-8 of itself, so l by at most 2^-8 relative and each logit by at
+most 2^-8 * scale * sum_e |q_e k_e|, and the log of a sum of exponentials
+moves by at most the largest move of its terms.  Every path is also held to
+mean 2e-3.
 """
 import numpy as np
 
@@ -68,11 +69,12 @@ def assert_parity(out_gpu, ref, fp8=False, what="", needles=()):
     return mx, mean, rel_plain, rel_needle
 
 
-def w48_lse_bound(q_rows, keys, scale, fp8):
+def w48_lse_bound(q_rows, keys, scale, rounded_keys):
     """A-priori LSE bound of the 384-row prefill for q_rows [R, d] of one head
     against that head's KV-head keys [n, d] (values, fp64)."""
-    m = np.abs(q_rows) @ np.abs(keys).T
-    return 2.0 ** -8 * (1.0 + (2.0 if fp8 else 1.0) * scale * m.max(axis=1)) + 1e-4
+    k = 1.0 if rounded_keys else 0.0
+    m = np.abs(q_rows) @ np.abs(keys).T if rounded_keys else np.zeros((len(q_rows), 1))
+    return 2.0 ** -8 * (1.0 + k * scale * m.max(axis=1)) + 1e-4
 
 
 def assert_lse(lse_gpu, ref_lse, bound, what=""):
