@@ -75,7 +75,9 @@ typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
  *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim],
  *                     bf16 (2 bytes) or E4M3 codes (1 byte) per element.
  *   k_scale, v_scale  fp32 [num_blocks][num_kv_heads]; stored value =
- *                     decode(code) * scale.  NULL iff dtype == PA_KV_BF16.
+ *                     decode(code) * scale; every scale a block in use has is
+ *                     a positive, finite, normal fp32 number.  NULL iff
+ *                     dtype == PA_KV_BF16.
  * ([V41] "SWA 有界重放" and the kernels section keep KV in FP8 to cut its
  * footprint.) */
 typedef struct {
@@ -135,14 +137,18 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  *   lse_out       optional fp32 [total_q][num_q_heads]: ln(sum_j exp(scale *
  *                 q.k_j)) over the keys the row sees; NULL to skip.
  *   workspace     device scratch of at least pa_workspace_size(...) bytes,
- *                 256-byte aligned; contents need no initialisation.  With an
- *                 E4M3 cache of head_dim 128 it also holds a bf16 copy of the
- *                 context of every sequence with more than 16/G new tokens
- *                 (4 KB per token for 8 KV heads), which the prefill reads.
+ *                 256-byte aligned; contents need no initialisation.  It
+ *                 holds the work list and the fp32 partial results of key
+ *                 ranges split across work-groups; its size depends on the
+ *                 number of tiles and of compute units, not on context
+ *                 length (for the prefill: at most one 384-row partial per
+ *                 (tile, KV head) and work-group boundary).
  * Row i of sequence s is at position p = hist[s] + i, and
  *   out[row][h] = sum_{j<=p} softmax_j(scale * q[row][h] . K[j][h/G]) V[j][h/G].
  * With an E4M3 cache, K[j] and V[j] are code * scale of their (block, head);
- * decode uses that product in fp32, prefill rounds it to bf16 (nearest-even).
+ * the codes widen to bf16 exactly and the scales act in fp32 (the key scale
+ * on the score, the value scale on the probability before it is rounded to
+ * bf16 for the value product), in prefill and decode alike.
  * Neither q nor the caches are written.
  */
 PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
@@ -172,7 +178,7 @@ PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_
  * records HIP events on the call's stream around the kernel; the durations
  * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
  * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention,
- * 3 = LSE merge, 4 = bf16 copy of E4M3 context for prefill, the summed
+ * 3 = LSE merge, 4 = unused (kept for numbering), the summed
  * milliseconds and launch count since the last reset (it synchronises on the
  * recorded events), then resets that kind. */
 PA_API pa_status pa_timing_enable(int enable);
@@ -190,8 +196,8 @@ PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_len
                                int32_t *items_out, int32_t items_cap, int32_t *counts_out);
 
 /* Test hook for the persistent prefill launch: when the plan for these HOST
- * lengths runs the persistent 384-row kernel (head_dim 128: bf16 KV, or the
- * bf16 copy of E4M3 KV) with one work-group per balanced range of work, *num_groups_out receives the number
+ * lengths runs the persistent 384-row kernel (head_dim 128, bf16 or E4M3 KV)
+ * with one work-group per balanced range of work, *num_groups_out receives the number
  * of work-groups n and first_out[0..n] the offsets into the prefill items
  * (as listed by pa_debug_plan) where each work-group's items begin, with
  * first_out[n] = the number of prefill items.  n = 0 (nothing written) for

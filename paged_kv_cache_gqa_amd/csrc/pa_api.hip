@@ -129,15 +129,8 @@ struct Plan {
   std::vector<int32_t> wg_first;  // persistent prefill launch: items of work-group w are
                                   // prefill[wg_first[w] .. wg_first[w+1]); empty otherwise
   int64_t n_part_prefill = 0, n_part_decode = 0;
-  // E4M3 caches with prefill work: bf16 copies of the prefilled sequences'
-  // context (dq items), read by the bf16 prefill kernels through compact
-  // block tables [num_seqs][dq_mb]
-  std::vector<DqItem> dq;
-  int64_t dq_blocks = 0;
-  int32_t dq_mb = 0;
-  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, off_dq = 0, plan_bytes = 0;
-  size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0;
-  size_t off_dq_bt = 0, off_dq_k = 0, off_dq_v = 0, total = 0;
+  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, plan_bytes = 0;
+  size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -160,16 +153,11 @@ void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out)
   }
 }
 
-// Query rows per prefill tile: the LDS-DMA kernel (head_dim 128; E4M3
-// context goes through a bf16 copy) takes 384, the register-staged kernel
-// (head_dim 64) 128.
+// Query rows per prefill tile: the LDS-DMA kernel (head_dim 128, bf16 or
+// E4M3 KV) takes 384, the register-staged kernel (head_dim 64) 128.
 int32_t prefill_tile_rows(const pa_kv_cache *c) {
   return c->head_dim == 128 ? kDmaTileRows : kRegTileRows;
 }
-bool prefill_dequant(const pa_kv_cache *c) {
-  return c->dtype == PA_KV_FP8_E4M3 && c->head_dim == 128;
-}
-constexpr int32_t kDqBlocksPerGroup = 16;  // cache blocks per work-group of the bf16 copy
 
 // Persistent split for the LDS-DMA prefill kernels.  The prefill work -- every tile
 // times every KV head, measured in 64-key steps -- is laid out KV-head-major,
@@ -222,7 +210,6 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   };
   std::vector<Piece> pieces;
   auto bound = [&](int64_t r) { return W * r / nwg; };  // first step of range r
-  constexpr int32_t kMaxSegSteps = kMaxDmaItemKeys / kKeyTile;
   int64_t pos = 0;
   int32_t r = 0;
   // Many tiles per KV head (an initial prefill: tiles of every length up to
@@ -230,8 +217,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   // the least loaded range of the XCD that holds the head (greedy LPT: the
   // loads end within the shortest tiles' length of each other).  The XCD's
   // work-groups then start tiles of nearly equal length at key 0 together,
-  // round after round, and share K/V in L2; no tile is split (no partials)
-  // unless it exceeds the item cap.
+  // round after round, and share K/V in L2; no tile is split (no partials).
   const int32_t xcds = M.xcds;
   const int32_t per_xcd = nwg / xcds;
   const bool lpt = kPlanLpt && nwg % xcds == 0 && hkv % xcds == 0 &&
@@ -249,11 +235,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
           for (int32_t q = 1; q < per_xcd; q++)
             if (load[q] < load[j]) j = q;
           const int32_t steps = steps_of(k);
-          for (int32_t lo = 0; lo < steps;) {
-            const int32_t hi = std::min(steps, lo + kMaxSegSteps);
-            pieces.push_back({kvh * (int32_t)pre.size() + k, lo, hi, x * per_xcd + j});
-            lo = hi;
-          }
+          pieces.push_back({kvh * (int32_t)pre.size() + k, 0, steps, x * per_xcd + j});
           load[j] += steps;
         }
     }
@@ -266,14 +248,16 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
         const int32_t c1 = std::min(steps, c0 + C);
         for (int32_t lo = c0; lo < c1;) {
           while (bound(r + 1) <= pos) r++;
-          const int32_t hi = (int32_t)std::min<int64_t>({(int64_t)c1, lo + bound(r + 1) - pos,
-                                                         (int64_t)lo + kMaxSegSteps});
+          const int32_t hi = (int32_t)std::min<int64_t>((int64_t)c1, lo + bound(r + 1) - pos);
           pieces.push_back({kvh * (int32_t)pre.size() + (int32_t)k, lo, hi, r});
           pos += hi - lo;
           lo = hi;
         }
       }
-  // partial slots: consecutive per (tile, head) unit, in key order
+  // partial slots: consecutive per (tile, head) unit, in key order.  A piece
+  // is never cut for length: the kernel walks any key range in windows whose
+  // block ids it restages, so a (tile, head) needs a partial slot per range
+  // it spans -- at most units + work-groups slots, whatever the context.
   std::vector<int32_t> count(units, 0), part0(units, -1), seen(units, 0);
   for (const Piece &pc : pieces) count[pc.unit]++;
   for (int64_t u = 0; u < units; u++) {
@@ -290,24 +274,11 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
     by_range[pc.range].push_back({t.seq, pc.unit / (int32_t)pre.size(), t.row0, t.pos0, t.nq,
                                   pc.lo * kKeyTile, std::min(t.keys, pc.hi * kKeyTile), part});
   }
-  // Within a range, runs of pieces that start at a chunk boundary come first
-  // (a run: consecutive pieces of one (tile, head) continuing each other,
-  // which the item length cap splits a chunk into), in key order: every
-  // work-group then starts at the start of a chunk at the same moment, and
-  // the work-groups on one chunk walk it in step.
-  for (auto &v : by_range) {
-    std::vector<char> aligned(v.size(), 0);
-    for (size_t i = 0; i < v.size(); i++) {
-      const Item &x = v[i];
-      const bool cont = i > 0 && v[i - 1].kvh == x.kvh && v[i - 1].row0 == x.row0 &&
-                        v[i - 1].kv_hi == x.kv_lo;
-      aligned[i] = x.kv_lo % (C * kKeyTile) == 0 || (cont && aligned[i - 1]);
-    }
-    std::vector<Item> first, rest;
-    for (size_t i = 0; i < v.size(); i++) (aligned[i] ? first : rest).push_back(v[i]);
-    first.insert(first.end(), rest.begin(), rest.end());
-    v.swap(first);
-  }
+  // Within a range, pieces that start at a chunk boundary come first, in key
+  // order: every work-group then starts at the start of a chunk at the same
+  // moment, and the work-groups on one chunk walk it in step.
+  for (auto &v : by_range)
+    std::stable_partition(v.begin(), v.end(), [&](const Item &x) { return x.kv_lo % (C * kKeyTile) == 0; });
   P.wg_first.assign(nwg + 1, 0);
   for (int32_t w = 0; w < nwg; w++) {
     const int32_t rr = nwg % xcds == 0 ? (w % xcds) * (nwg / xcds) + w / xcds : w;
@@ -317,8 +288,9 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   P.wg_first[nwg] = (int32_t)P.prefill.size();
 }
 
-void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hkv,
-               int32_t group, int32_t d, int32_t tile_rows, Plan &P, int32_t dq_bs = 0) {
+void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const pa_kv_cache *c,
+               int32_t group, Plan &P) {
+  const int32_t hkv = c->num_kv_heads, d = c->head_dim, tile_rows = prefill_tile_rows(c);
   const MachineShape M = machine_shape();
   const int64_t decode_target_items = (int64_t)kDecodeItemsPerCU * M.cus;
   const int64_t prefill_target_items = (int64_t)kPrefillItemsPerCU * M.cus;
@@ -356,7 +328,8 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, prefill_target_items));
 
   const bool persistent = tile_rows == kDmaTileRows;
-  if (persistent) plan_persistent(tiles, hkv, tile_rows, M, P);
+  if (persistent)
+    plan_persistent(tiles, hkv, tile_rows, M, P);
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
   for (const Tile &t : tiles) {
@@ -396,19 +369,6 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
       if (i < pre_by_head[k].size()) P.prefill.push_back(pre_by_head[k][i]);
   std::stable_sort(P.decode.begin(), P.decode.end(), longer);
 
-  if (dq_bs > 0) {  // bf16 copies of the context of every sequence with prefill tiles
-    int32_t last = -1;
-    for (const Tile &t : tiles) {
-      if (t.decode || t.seq == last) continue;
-      last = t.seq;
-      const int32_t nblk = (int32_t)cdiv64((int64_t)hist[t.seq] + incr[t.seq], dq_bs);
-      for (int32_t j = 0; j < nblk; j += kDqBlocksPerGroup)
-        P.dq.push_back({t.seq, j, std::min(nblk, j + kDqBlocksPerGroup), (int32_t)P.dq_blocks});
-      P.dq_blocks += nblk;
-      P.dq_mb = std::max(P.dq_mb, nblk);
-    }
-  }
-
   // merges with many parts last (they take the one-row-per-work-group kernel)
   std::stable_partition(P.merges.begin(), P.merges.end(),
                         [](const Merge &m) { return m.nparts <= kMergeSerialParts; });
@@ -422,8 +382,6 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + P.merges.size() * sizeof(Merge));
   P.off_wg = off;
   off = align256(off + P.wg_first.size() * sizeof(int32_t));
-  P.off_dq = off;
-  off = align256(off + P.dq.size() * sizeof(DqItem));
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -433,15 +391,6 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32
   off = align256(off + (size_t)P.n_part_decode * kDecodeRows * d * sizeof(float));
   P.off_pl_dec = off;
   off = align256(off + (size_t)P.n_part_decode * kDecodeRows * sizeof(float));
-  if (!P.dq.empty()) {
-    P.off_dq_bt = off;
-    off = align256(off + (size_t)num_seqs * P.dq_mb * sizeof(int32_t));
-    const size_t cache_bytes = (size_t)P.dq_blocks * hkv * dq_bs * d * 2;
-    P.off_dq_k = off;
-    off = align256(off + cache_bytes);
-    P.off_dq_v = off;
-    off = align256(off + cache_bytes);
-  }
   P.total = off;
 }
 
@@ -664,9 +613,7 @@ size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int
   if (check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, 0, false, &total_q))
     return 0;
   Plan P;
-  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P,
-            prefill_dequant(cache) ? cache->block_size : 0);
+  make_plan(hist_lens, incr_lens, num_seqs, cache, num_q_heads / cache->num_kv_heads, P);
   return std::max<size_t>(P.total, 256);
 }
 
@@ -690,8 +637,7 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
-  const bool dq = prefill_dequant(cache);
-  make_plan(hist_lens, incr_lens, num_seqs, hkv, group, d, tile_rows, P, dq ? cache->block_size : 0);
+  make_plan(hist_lens, incr_lens, num_seqs, cache, group, P);
   if (!workspace) return fail(PA_ERR_NULL_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(PA_ERR_BAD_SHAPE, "workspace not 256-byte aligned");
   if (workspace_bytes < P.total)
@@ -704,7 +650,6 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   if (!P.merges.empty()) memcpy(host.data() + P.off_merges, P.merges.data(), P.merges.size() * sizeof(Merge));
   if (!P.wg_first.empty())
     memcpy(host.data() + P.off_wg, P.wg_first.data(), P.wg_first.size() * sizeof(int32_t));
-  if (!P.dq.empty()) memcpy(host.data() + P.off_dq, P.dq.data(), P.dq.size() * sizeof(DqItem));
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   st = stage_copy(host.data(), P.plan_bytes, ws, s);
@@ -732,41 +677,12 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   hipError_t e;
   if (!P.prefill.empty()) {
     AttnArgs ap = a;
-    bool pre_fp8 = fp8;
-    if (!P.dq.empty()) {
-      // E4M3 context -> bf16 copy; the prefill reads the copy through
-      // compact block tables (block j of sequence s at compact block base + j)
-      DequantArgs da{};
-      da.k = cache->k_cache;
-      da.v = cache->v_cache;
-      da.ks = cache->k_scale;
-      da.vs = cache->v_scale;
-      da.bt = block_tables;
-      da.max_blocks = max_blocks_per_seq;
-      da.hkv = hkv;
-      da.bs = bs;
-      da.d = d;
-      da.items = (const DqItem *)(ws + P.off_dq);
-      da.k_out = ws + P.off_dq_k;
-      da.v_out = ws + P.off_dq_v;
-      da.bt_out = (int32_t *)(ws + P.off_dq_bt);
-      da.mb_out = P.dq_mb;
-      e = timed(4, s, [&] { return launch_dequant(da, (int)P.dq.size(), s); });
-      if (e != hipSuccess) return hip_fail(e, "E4M3 context copy launch");
-      ap.c.k = da.k_out;
-      ap.c.v = da.v_out;
-      ap.c.ks = ap.c.vs = nullptr;
-      ap.c.num_blocks = (int32_t)P.dq_blocks;
-      ap.bt = da.bt_out;
-      ap.max_blocks = P.dq_mb;
-      pre_fp8 = false;
-    }
     ap.items = (const Item *)(ws + P.off_prefill);
     ap.part_o = (float *)(ws + P.off_po_pre);
     ap.part_lse = (float *)(ws + P.off_pl_pre);
     ap.wg_first = P.wg_first.empty() ? nullptr : (const int32_t *)(ws + P.off_wg);
     const int n = P.wg_first.empty() ? (int)P.prefill.size() : (int)P.wg_first.size() - 1;
-    e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, pre_fp8, s); });
+    e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fp8, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
   if (!P.decode.empty()) {
@@ -869,8 +785,7 @@ pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens, int3
   if (st) return st;
   if (!counts_out || (items_cap > 0 && !items_out)) return fail(PA_ERR_NULL_ARG, "output is NULL");
   Plan P;
-  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
+  make_plan(hist_lens, incr_lens, num_seqs, cache, num_q_heads / cache->num_kv_heads, P);
   counts_out[0] = (int32_t)P.prefill.size();
   counts_out[1] = (int32_t)P.decode.size();
   counts_out[2] = (int32_t)P.merges.size();
@@ -894,8 +809,7 @@ pa_status pa_debug_plan_groups(const int32_t *hist_lens, const int32_t *incr_len
   if (st) return st;
   if (!num_groups_out || (cap > 0 && !first_out)) return fail(PA_ERR_NULL_ARG, "output is NULL");
   Plan P;
-  make_plan(hist_lens, incr_lens, num_seqs, cache->num_kv_heads,
-            num_q_heads / cache->num_kv_heads, cache->head_dim, prefill_tile_rows(cache), P);
+  make_plan(hist_lens, incr_lens, num_seqs, cache, num_q_heads / cache->num_kv_heads, P);
   const int32_t n = P.wg_first.empty() ? 0 : (int32_t)P.wg_first.size() - 1;
   *num_groups_out = n;
   if (n == 0) return PA_OK;

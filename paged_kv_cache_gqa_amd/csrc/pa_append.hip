@@ -61,64 +61,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-// bf16 copy of E4M3 context for the prefill kernels: value = bf16(code *
-// scale), the product rounded in fp32, then to bf16, both nearest-even (every
-// code is exact in fp32).  A work-group converts blocks j0 .. j1-1 of one
-// sequence for all KV heads, 16 codes per thread and step, and writes the
-// compact block table entries of those blocks.
-__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
-  const DqItem it = a.items[blockIdx.x];
-  const int tid = threadIdx.x;
-  const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks;
-  for (int j = it.j0 + tid; j < it.j1; j += 256) a.bt_out[(int64_t)it.seq * a.mb_out + j] = it.base + j;
-  const int cpb = a.bs * a.d / 16;  // 16-byte chunks of codes per (block, head)
-  const int64_t total = (int64_t)(it.j1 - it.j0) * a.hkv * cpb;
-  constexpr int U = 4;  // chunks per thread whose loads are in flight together
-  for (int64_t c0 = tid; c0 < total; c0 += U * 256) {
-    uint4 w[U][2];
-    int64_t src[U], dst[U];
-    float sc[U][2];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int64_t c = min(c0 + u * 256, total - 1);  // a repeat of the last chunk is harmless
-      const int ch = (int)(c % cpb);
-      const int64_t jh = c / cpb;
-      const int h = (int)(jh % a.hkv);
-      const int j = it.j0 + (int)(jh / a.hkv);
-      const int64_t blk = btr[j];
-      src[u] = (blk * a.hkv + h) * a.bs * a.d + ch * 16;
-      dst[u] = ((int64_t)(it.base + j) * a.hkv + h) * a.bs * a.d + ch * 16;
-      sc[u][0] = a.ks[blk * a.hkv + h];
-      sc[u][1] = a.vs[blk * a.hkv + h];
-      w[u][0] = gload16_nt((const unsigned char *)a.k + src[u]);
-      w[u][1] = gload16_nt((const unsigned char *)a.v + src[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-#pragma unroll
-      for (int kv = 0; kv < 2; kv++) {
-        const uint32_t wd[4] = {w[u][kv].x, w[u][kv].y, w[u][kv].z, w[u][kv].w};
-        const float scale = sc[u][kv];
-        uint32_t o[8];
-        auto pack = [&](float x, float y) {
-          const __bf16 lo = (__bf16)(x * scale), hi = (__bf16)(y * scale);
-          return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        };
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const auto f_lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);  // codes 4i, 4i+1
-          const auto f_hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);   // codes 4i+2, 4i+3
-          o[2 * i] = pack(f_lo[0], f_lo[1]);
-          o[2 * i + 1] = pack(f_hi[0], f_hi[1]);
-        }
-        unsigned char *dp = (unsigned char *)(kv ? a.v_out : a.k_out) + dst[u] * 2;
-        *(uint4 *)dp = make_uint4(o[0], o[1], o[2], o[3]);
-        *(uint4 *)(dp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  }
-}
-
 // Work-list copy from a pinned host buffer into the workspace (bytes is a
 // multiple of 16, both addresses 16-byte aligned).
 __global__ __launch_bounds__(256) void stage_kernel(const uint4 *src, uint4 *dst, int64_t n16) {
@@ -135,11 +77,7 @@ hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dequant_kernel, dim3(n_items), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
+
 
 // Raw gather of one sequence through its block-table row ([V1Sched]
 // "Scheduler.schedule — 记账与状态": a request's KV lives in the blocks its

@@ -24,8 +24,8 @@
 //
 // Kernels, in file order:
 //   prefill_kernel<D, BS, FP8>     register-staged, 128-row tiles (head_dim 64)
-//   prefill_w48_kernel<BS>         persistent 384-row LDS-DMA prefill (head_dim 128; E4M3
-//                                  through its bf16 copy)
+//   prefill_w48_kernel<BS, FP8>    persistent 384-row LDS-DMA prefill (head_dim 128; bf16
+//                                  and E4M3 KV)
 //   decode_kernel<D, BS, FP8>      register-staged decode (head_dim 64)
 //   decode_dma_kernel<BS, NW, NST>, decode_dma_fp8_kernel<BS, NW, NST>
 //                                  LDS-DMA decode, bf16 and E4M3 (head_dim 128)
@@ -367,15 +367,15 @@ __device__ __forceinline__ void wg_barrier() {
 
 
 // =============================================================================
-// 384-row prefill for bf16 KV, head_dim 128 ("ping-pong"): one work-group of
-// 8 waves per CU; waves 0-3 (group 0) and 4-7 (group 1) each own 48 query
-// rows per wave (three 16-row blocks) on v_mfma_f32_16x16x32_bf16, in 32-key
-// steps.  In each half-step one group issues its matrix-core work
-// (O += V(t)^T P(t)^T, then S(t+1) = K(t+1) Q^T) while the other turns
-// scores into probabilities on the vector ALUs, so each SIMD always has one
-// wave feeding its matrix core and one wave doing softmax.  (An earlier
-// 256-row design with 32 rows per wave on 32x32x16 MFMAs and 64-key steps
-// brought 1.5x the bytes into the CU per flop and ran at a lower clock.)
+// 384-row prefill, head_dim 128 ("ping-pong"): one work-group of 8 waves per
+// CU; waves 0-3 (group 0) and 4-7 (group 1) each own 48 query rows per wave
+// (three 16-row blocks) on v_mfma_f32_16x16x32_bf16, in 32-key steps.  In
+// each half-step one group issues its matrix-core work (O += V(t)^T P(t)^T,
+// then S(t+1) = K(t+1) Q^T) while the other turns scores into probabilities
+// on the vector ALUs, so each SIMD always has one wave feeding its matrix
+// core and one wave doing softmax.  (An earlier 256-row design with 32 rows
+// per wave on 32x32x16 MFMAs and 64-key steps brought 1.5x the bytes into the
+// CU per flop and ran at a lower clock.)
 //   Sᵀ = K Qᵀ per (16-key block kb, 16-row block rb): A = K (lane: key c16,
 //   d 32c + 8g..+7, one 16-byte LDS read), B = Qᵀ (lane: row c16, same d, in
 //   registers), D: lane holds row c16, keys 16kb + 4g + r.
@@ -386,6 +386,17 @@ __device__ __forceinline__ void wg_barrier() {
 //   c16).  D: lane holds row c16, d = 16db + 4g + r.
 // A row's 32 scores of a step sit in the four lanes c16 + 16g, reduced with
 // the permlane swaps.
+// E4M3 KV ([V41] kernels section: 8-bit KV to cut its footprint): the codes
+// reach LDS by the same LDS-filling loads (half the bytes of bf16), and each
+// step's K and V codes are widened to bf16 once per work-group (8 exact
+// conversions per lane and step, all eight waves sharing the work) into the
+// same tile layout the bf16 path reads, so the matrix-core code is the same.
+// The per-(block, head) scales stay in fp32: the key scale joins the score's
+// fused multiply-add, and the value scale enters the probability's exponent
+// (so P * s_v is what is rounded to bf16 for the value product); the row sum
+// l, which the matrix cores accumulate from those same bf16 values, is kept
+// in units of the current step's value scale and rescaled by s_v(t)/s_v(t-1)
+// when the step changes (divided out at the end).
 constexpr int kW48Step = 32;                        // keys per step
 // K (or V) of one 32-key step in LDS: 8 blocks of 4 key rows, each block
 // 1,024 bytes of data and 32 of padding (the layout is described at the
@@ -396,9 +407,14 @@ constexpr int kW48TileBytes = 8 * kW48BlockBytes;
 #define PA_W48_STAGES 4
 #endif
 constexpr int kW48Stages = PA_W48_STAGES;
+constexpr int kW48CodeStages = 4;                // E4M3: stages of the code ring
+constexpr int kW48CodeBytes = kW48Step * 128;    // E4M3 codes of one step's K (or V)
+constexpr int kW48ScaleSlots = 8;                // E4M3: steps held by the scale ring
+constexpr int kW48ScaleSlotBytes = 1024;         // K half 0, K half 1, V half 0, V half 1: 256 bytes each
+constexpr int kW48Fp8Lds = 4 * kW48TileBytes + kW48CodeStages * 2 * kW48CodeBytes + kW48ScaleSlots * kW48ScaleSlotBytes;
 
-template <int BS>
-__device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8 *smem, int *bt_lds) {
+template <int BS, bool FP8>
+__device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u8 *smem) {
   constexpr int D = 128;
   constexpr int NCQ = D / 32;  // k-steps of the score product
   constexpr int NDB = D / 16;  // d-blocks of the value product
@@ -406,25 +422,35 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   constexpr int TILEB = kW48TileBytes;
   constexpr int STAGEB = 2 * TILEB;
   constexpr int NST = kW48Stages;
+  constexpr int NCS = kW48CodeStages;
+  constexpr int CB = kW48CodeBytes;
+  // E4M3, block 16: a step's two 16-key halves lie in different blocks (two
+  // scales per step, l kept per half); block 64: one block per step
+  constexpr bool SPLIT = FP8 && BS == 16;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
   const float scale_log2 = a.scale_log2;
-  const int kv_hi = it.kv_hi, kvh = it.kvh, hkv = a.c.hkv;
+  const int kvh = it.kvh, hkv = a.c.hkv;
+  const int nq = it.nq;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int c16 = lane & 15, g = lane >> 4;
 
-  // Q as stored (bf16, exact): the score MFMAs produce raw q.k, and one fused
-  // multiply-add per score applies scale * log2(e) and the row's reference
-  // exponent in fp32.
+  // Q as stored (bf16, exact): the score MFMAs produce raw q.k, and one
+  // fused multiply-add per score applies scale * log2(e) (times the key scale
+  // for E4M3) and the row's reference exponent in fp32.
   bf16x8 qf[RB][NCQ];
+  f32x4 o[NDB + 1][RB];  // O^T accumulators; o[NDB] is the row sum l
+  float negm[RB];        // -m per row block; m itself is not kept
+  int all_live = 0;      // every row of the wave has weight (wave-uniform)
+  float isv[2] = {0.f, 0.f};  // E4M3: 1 / value scale of the last step's two 16-key halves
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
     const int row = wave * 48 + rb * 16 + c16;
     const int tok = row >> a.lg, gq = row & (a.group - 1);
-    const bool act = tok < it.nq;
+    const bool act = tok < nq;
     const unsigned char *qrow =
         (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq) * D) * 2;
 #pragma unroll
@@ -432,18 +458,32 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       uint4 v = act ? gload16(qrow + (32 * c + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
       qf[rb][c] = as_bf16x8(v);
     }
+    negm[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
   }
+  f32x4 S[2][RB];
+  bf16x8 pb[RB];
+  // the row-sum operand: all ones, or for E4M3 block 16 one half per 16-key
+  // half (A rows 0-7 sum keys 0-15, rows 8-15 keys 16-31: lanes with g < 2
+  // accumulate the first half's l, g >= 2 the second's)
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; e++) ones[e] = (__bf16)(SPLIT ? (((e < 4) == (c16 < 8)) ? 1.0f : 0.0f) : 1.0f);
 
+  const int kv_hi = it.kv_hi;
   const int t_begin = it.kv_lo / kW48Step;
   const int t_end = (kv_hi + kW48Step - 1) / kW48Step;
   const int t_full = max(t_begin, min(t_end, min(it.pos0 + 1, kv_hi) / kW48Step));
-  const int blk0 = it.kv_lo / BS;
   const int last_blk = (kv_hi - 1) / BS;
-
-  {  // stage the item's block ids
-    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
-    for (int i = tid; i <= last_blk - blk0; i += 512) bt_lds[i] = btr[i];
-  }
+  // The block ids (and E4M3 scales) are read through the scalar cache with
+  // wave-uniform loads, each well before it is used: a vector load would be
+  // counted with the K/V stream by vmcnt, and staging them in LDS would bound
+  // the length of an item (the planner never cuts an item for length).
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  typedef const __attribute__((address_space(4))) float cfloat;
+  const cint *btr = (const cint *)(a.bt + (int64_t)it.seq * a.max_blocks);
+  auto block_of = [&](int key) __attribute__((always_inline)) { return btr[min(key / BS, last_blk)]; };
 
   // LDS tile of one step (32 keys, 256 bytes each): key row k lies in block
   // k / 4 (blocks kW48BlockBytes apart: 1 KB of data + 32 bytes), and within
@@ -464,71 +504,105 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   const int vbase = g * kW48BlockBytes + (c16 >> 2) * 64 + ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8;
   auto kofs = [&](int c) { return kbase + c * 256; };
   auto vofs = [&](int db) { return vbase + (db >> 1) * 256 + (db & 1) * 32; };
-  // this wave's DMA lanes fill block `wave` (tile rows 4*wave .. 4*wave+3):
-  // lane l writes byte 16 l of the block, i.e. row (l / 4) % 4, chunk
-  // 4 (l / 16) + l % 4
-  const int voff = ((lane >> 2) & 3) * 256 + (4 * (lane >> 4) + (lane & 3)) * 16;
   const unsigned char *kc = (const unsigned char *)a.c.k;
   const unsigned char *vc = (const unsigned char *)a.c.v;
 
-  __syncthreads();  // block ids visible
-
-  // K/V requests walk the item's steps in order (the prologue's NST-1 steps,
-  // then one per step), so their positions are running counters.  Items
-  // start on a step boundary (the planner cuts key ranges in multiples of
-  // 64 keys), so rpos >= kv_lo.  A request past the range end has a buffer
-  // size of zero: it moves no data but keeps the per-step vmcnt accounting.
+  // K/V requests walk the item's steps in order, so their positions are
+  // running counters.  Items start on a step boundary (the planner cuts key
+  // ranges in multiples of 64 keys), so rpos >= kv_lo.  A request past the
+  // range end has a buffer size of zero: it moves no data but keeps the
+  // per-step vmcnt accounting.
   constexpr int LGBS = BS == 16 ? 4 : 6;
   static_assert(BS == 16 || BS == 64, "block size");
-  const uint32_t blk_bytes = (uint32_t)hkv * BS * D * 2;
-  const uint64_t kc_head = (uint64_t)(kc + (int64_t)kvh * BS * D * 2);
-  const uint64_t vc_head = (uint64_t)(vc + (int64_t)kvh * BS * D * 2);
-  const int bt_last = last_blk - blk0;
-  int rpos = t_begin * kW48Step + 4 * wave;  // first key row of this wave's next request
-  uint32_t st_off = 0;                         // its ring stage, in bytes
-  int blk_next = bt_lds[min((rpos >> LGBS) - blk0, bt_last)];
-  auto issue = [&](int) __attribute__((always_inline)) {
+  constexpr int ELEM = FP8 ? 1 : 2;
+  const uint32_t blk_bytes = (uint32_t)hkv * BS * D * ELEM;
+  // bf16: this wave's requests fill block `wave` of the step's K and V tiles
+  // (key rows 4*wave .. +3): lane l writes byte 16 l of the block, i.e. row
+  // (l / 4) % 4, chunk 4 (l / 16) + l % 4.  E4M3: waves 0-3 request K codes,
+  // waves 4-7 V codes, rows 8 (wave % 4) .. +7 of the step (1 KB, one block),
+  // into the code ring, where row R's 16-byte chunk j sits at position
+  // j ^ (4 ((R >> 1) & 1)) (so that the widening reads below are free of bank
+  // conflicts): lane l fetches the chunk its LDS position holds.
+  const int voff = FP8 ? (lane >> 3) * 128 + 16 * ((lane & 7) ^ (((lane >> 4) & 1) << 2))
+                       : ((lane >> 2) & 3) * 256 + (4 * (lane >> 4) + (lane & 3)) * 16;
+  const int qw = wave & 3;
+  const unsigned char *mine = FP8 && wave >= 4 ? vc : kc;
+  const uint64_t kc_head = (uint64_t)(kc + (int64_t)kvh * BS * D * ELEM);
+  const uint64_t vc_head = (uint64_t)(vc + (int64_t)kvh * BS * D * ELEM);
+  const uint64_t my_head = (uint64_t)(mine + (int64_t)kvh * BS * D * ELEM);
+  int rpos = t_begin * kW48Step + (FP8 ? 8 * qw : 4 * wave);  // first key row of this wave's next request
+  uint32_t st_off = 0;                                        // its ring stage, in bytes
+  int blk_next = block_of(rpos);
+  constexpr int RING = FP8 ? 4 * TILEB : 0;  // E4M3: the code ring follows the four bf16 tiles
+  constexpr int SCB = RING + NCS * 2 * CB;   // E4M3: then the scale ring
+  // E4M3: with its codes, each wave requests the scale of the block its rows
+  // lie in (K waves the K scale, V waves the V scale) into the step's slot
+  // of the scale ring (the 16-key half of its rows: (wave % 4) / 2); every
+  // lane reads the same 4 bytes.  Two requests per wave and step.
+  const uint64_t sc_head = (uint64_t)(FP8 && wave >= 4 ? a.c.vs : a.c.ks) + (uint64_t)kvh * 4;
+  const uint32_t sc_lane0 = SCB + (wave >= 4 ? 512 : 0) + (qw >> 1) * 256;
+  uint32_t sc_off = 0;
+  const int zero = 0;
+  auto issue = [&]() __attribute__((always_inline)) {
     const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(blk_next);
-    const uint64_t off = (uint64_t)blk * blk_bytes + (uint32_t)((rpos & (BS - 1)) * (D * 2));
-    const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 4) * (D * 2));
-    const uint32_t st = smem_addr + st_off;
-    const uint64_t ka = kc_head + off, va = vc_head + off;
-    // (readfirstlane keeps the descriptor in SGPRs, as the asm operand needs)
-    const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
-                        __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-    const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
-                        __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
-    dma_load16(rk, voff, st + wave * kW48BlockBytes);
-    dma_load16(rv, voff, st + TILEB + wave * kW48BlockBytes);
+    const uint64_t off = (uint64_t)blk * blk_bytes + (uint32_t)((rpos & (BS - 1)) * (D * ELEM));
+    if constexpr (FP8) {
+      const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 8) * D);
+      const uint64_t ga = my_head + off;
+      const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ga),
+                         __builtin_amdgcn_readfirstlane((int)((ga >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16(r, voff, smem_addr + RING + st_off + (wave >= 4 ? CB : 0) + qw * 1024);
+      st_off = st_off + 2 * CB == NCS * 2 * CB ? 0 : st_off + 2 * CB;
+      const uint64_t sa = sc_head + (uint64_t)blk * ((uint32_t)hkv * 4);
+      const i32x4_t rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)sa),
+                          __builtin_amdgcn_readfirstlane((int)((sa >> 32) & 0xFFFF)), 4, kRsrcFlags};
+      dma_load4(rs, zero, smem_addr + sc_lane0 + sc_off);
+      sc_off = (sc_off + kW48ScaleSlotBytes) & (kW48ScaleSlots * kW48ScaleSlotBytes - 1);
+    } else {
+      const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 4) * (D * 2));
+      const uint32_t st = smem_addr + st_off;
+      const uint64_t ka = kc_head + off, va = vc_head + off;
+      // (readfirstlane keeps the descriptor in SGPRs, as the asm operand needs)
+      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ka),
+                          __builtin_amdgcn_readfirstlane((int)((ka >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)va),
+                          __builtin_amdgcn_readfirstlane((int)((va >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16(rk, voff, st + wave * kW48BlockBytes);
+      dma_load16(rv, voff, st + TILEB + wave * kW48BlockBytes);
+      st_off = st_off + STAGEB == NST * STAGEB ? 0 : st_off + STAGEB;
+    }
     rpos += kW48Step;
-    st_off = st_off + STAGEB == NST * STAGEB ? 0 : st_off + STAGEB;
-    blk_next = bt_lds[min((rpos >> LGBS) - blk0, bt_last)];
+    blk_next = block_of(rpos);
   };
-  static_assert((NST & (NST - 1)) == 0, "ring stages: a power of two");
-  auto stage = [&](int t) __attribute__((always_inline)) {
-    return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
+  (void)my_head;
+  static_assert((NST & (NST - 1)) == 0 && (NCS & (NCS - 1)) == 0, "ring stages: a power of two");
+  // bf16 tiles of step t: the DMA ring (bf16) or the widened double buffers (E4M3)
+  auto ktile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8) return (const lds_u8 *)(smem + (t & 1) * TILEB);
+    else return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
+  };
+  auto vtile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8) return (const lds_u8 *)(smem + 2 * TILEB + (t & 1) * TILEB);
+    else return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB + TILEB);
+  };
+  // E4M3 widening: wave w converts block w (key rows 4w .. 4w+3) of a step's
+  // K or V tile; lane (Q, r, qq) = (lane / 16, lane / 4 % 4, lane % 4) reads
+  // the 8 codes of chunk q = 4Q + qq of row 4w + r and writes them as one
+  // 16-byte bf16 chunk.  Reads and writes each cover 64 banks per 16 lanes.
+  const int wrow = 4 * wave + ((lane >> 2) & 3);
+  const int wq = 4 * (lane >> 4) + (lane & 3);
+  const int w_rd = wrow * 128 + 16 * ((wq >> 1) ^ (((wrow >> 1) & 1) << 2)) + 8 * (wq & 1);
+  const int w_wr = wave * kW48BlockBytes + 256 * (lane >> 4) + 64 * ((lane >> 2) & 3) + 16 * (lane & 3);
+  auto widen_src = [&](int t, bool v) __attribute__((always_inline)) {
+    return (const lds_u8 *)(smem + RING + ((t - t_begin) & (NCS - 1)) * 2 * CB + (v ? CB : 0) + w_rd);
+  };
+  auto widen_dst = [&](int t, bool v) __attribute__((always_inline)) {
+    return smem + (v ? 2 * TILEB : 0) + (t & 1) * TILEB + w_wr;
+  };
+  auto widen = [&](int t, bool v) __attribute__((always_inline)) {
+    lds_store16(widen_dst(t, v), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(lds_load8(widen_src(t, v)))));
   };
 
-  // m[rb]: the row's reference exponent (base 2).  A score's exponent is
-  // fma(q.k, scale * log2 e, -m), so a probability is one exp2; m moves up
-  // only when a step's maximum exceeds it by kRescaleSlack, and while the
-  // row has no weight yet it follows the maximum.
-  // o[NDB][rb] is the row sum l: the value product runs one more d-block
-  // whose A operand is all ones, so l comes from the matrix cores (over the
-  // same bf16 probabilities the output uses) and is rescaled with o.
-  f32x4 o[NDB + 1][RB];
-  f32x4 S[2][RB];
-  bf16x8 pb[RB];
-  float negm[RB];  // -m[rb]; m[rb] itself is not kept
-  int all_live = 0;  // every row of the wave has weight (wave-uniform)
-#pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    negm[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db <= NDB; db++) o[db][rb] = f32x4{};
-  }
-
-  auto cinit = [&](int) __attribute__((always_inline)) { return f32x4{}; };
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
   // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
   auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
@@ -544,13 +618,8 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     for (int db = 0; db < NDB; db++)
 #pragma unroll
       for (int rb = 0; rb < RB; rb++) o[db][rb] = mfma16x16x32(vf[db], pb[rb], o[db][rb]);
-    {
-      bf16x8 ones;
 #pragma unroll
-      for (int e = 0; e < 8; e++) ones[e] = (__bf16)1.0f;
-#pragma unroll
-      for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
-    }
+    for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
     if constexpr (with_qk) {
       bf16x8 kf[NCQ][2];
 #pragma unroll
@@ -563,7 +632,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
           for (int rb = 0; rb < RB; rb++)
-            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? cinit(rb) : S[kb][rb]);
+            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} : S[kb][rb]);
       // order: the first three V fragments' reads; then per three MFMAs
       // (one fragment's worth) the reads of the fragment three ahead -- V
       // reads during the value product's first 15 MFMAs, K reads during its
@@ -598,16 +667,77 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
       for (int kb = 0; kb < 2; kb++) {
         const bf16x8 kf = as_bf16x8(lds_load16(Kb + kb * KB16 + kofs(c)));
 #pragma unroll
-        for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? cinit(rb) : S[kb][rb]);
+        for (int rb = 0; rb < RB; rb++) S[kb][rb] = mfma16x16x32(kf, qf[rb][c], c == 0 ? f32x4{} : S[kb][rb]);
       }
   };
+  // E4M3: each step's scales reach the scale ring with the step's code
+  // requests (slot (s - t_begin) % kW48ScaleSlots, landed when the codes
+  // have); the
+  // softmax of step t reads those of step t + 1 for the next call.
+  float sk_n[2] = {0.f, 0.f}, sv_n[2] = {1.f, 1.f};
+  auto read_scales = [&](int t) __attribute__((always_inline)) {
+    const lds_u8 *slot = smem + SCB + ((t - t_begin) & (kW48ScaleSlots - 1)) * kW48ScaleSlotBytes;
+#pragma unroll
+    for (int kb = 0; kb < (SPLIT ? 2 : 1); kb++) {
+      sk_n[kb] = *(const __attribute__((address_space(3))) float *)(slot + 256 * kb);
+      sv_n[kb] = *(const __attribute__((address_space(3))) float *)(slot + 512 + 256 * kb);
+    }
+  };
+  // m[rb]: the row's reference exponent (base 2).  A score's exponent is
+  // fma(q.k, scale * log2 e, -m) (E4M3: fma(q.k_code, scale * log2 e * s_k,
+  // -m + log2 s_v)), so a probability is one exp2; m moves up only when a
+  // step's maximum exceeds it by kRescaleSlack, and while the row has no
+  // weight yet it follows the maximum.
+  // E4M3, block 64 (both halves of a step in one block): the scales change
+  // every other step, so they are applied per block -- negm then holds
+  // -m + log2 s_v of the current block, and the slack test compares against
+  // kRescaleSlack + log2 s_v.
+  float mul_k = scale_log2, lsv_cur = 0.f, thr = kRescaleSlack;
   auto softmax = [&](auto masked_tag, int t) __attribute__((always_inline)) {
+    float mul[2] = {scale_log2, scale_log2}, lsv[2] = {0.f, 0.f};
+    if constexpr (FP8 && !SPLIT) {
+      if (((t * kW48Step) & (BS - 1)) == 0) {  // a new block: its scales
+        mul_k = scale_log2 * sk_n[0];
+        const float l_new = __builtin_amdgcn_logf(sv_n[0]);
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) negm[rb] += l_new - lsv_cur;
+        lsv_cur = l_new;
+        thr = kRescaleSlack + l_new;
+        const float rv = sv_n[0] * isv[0];  // l: from units of the last block's s_v to this one's
+        isv[0] = __builtin_amdgcn_rcpf(sv_n[0]);
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) o[NDB][rb][0] *= rv;
+      }
+      if ((((t + 1) * kW48Step) & (BS - 1)) == 0) read_scales(t + 1);
+      mul[0] = mul[1] = mul_k;
+    } else if constexpr (FP8) {
+      float rv[2];
+#pragma unroll
+      for (int kb = 0; kb < (SPLIT ? 2 : 1); kb++) {
+        mul[kb] = scale_log2 * sk_n[kb];
+        lsv[kb] = __builtin_amdgcn_logf(sv_n[kb]);
+        rv[kb] = sv_n[kb] * isv[kb];  // l: from units of the last step's s_v to this step's
+        isv[kb] = __builtin_amdgcn_rcpf(sv_n[kb]);
+      }
+      if constexpr (!SPLIT) {
+        mul[1] = mul[0];
+        lsv[1] = lsv[0];
+        rv[1] = rv[0];
+        isv[1] = isv[0];
+      }
+      const float rl = SPLIT && g >= 2 ? rv[1] : rv[0];
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) o[NDB][rb][0] *= rl;
+      read_scales(t + 1);  // in flight during the rest of the phase
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
+      for (int kb = 0; kb < 2; kb++) {
+        const float add = SPLIT ? negm[rb] + lsv[kb] : negm[rb];
 #pragma unroll
-        for (int r = 0; r < 4; r++) S[kb][rb][r] = __builtin_fmaf(S[kb][rb][r], scale_log2, negm[rb]);
+        for (int r = 0; r < 4; r++) S[kb][rb][r] = __builtin_fmaf(S[kb][rb][r], mul[kb], add);
+      }
     if constexpr (decltype(masked_tag)::value) {
       const int key0 = t * kW48Step + 4 * g;
 #pragma unroll
@@ -619,21 +749,26 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
           for (int r = 0; r < 4; r++) S[kb][rb][r] = key0 + kb * 16 + r <= lim ? S[kb][rb][r] : -INFINITY;
       }
     }
-    // S holds s - m.  A row's maximum is needed only when m has to move:
-    // test the lane's own maximum first, reduce across the row's four lanes
-    // only if some lane exceeds the slack (rare once m has settled) or some
-    // row has no weight yet (m then follows the row maximum).
+    // S holds s - m (E4M3: plus log2 s_v).  A row's maximum is needed only
+    // when m has to move: test the lane's own maximum first, reduce across
+    // the row's four lanes only if some lane exceeds the slack (rare once m
+    // has settled) or some row has no weight yet (m then follows the row
+    // maximum).
     auto rescale = [&]() __attribute__((always_inline)) {
       bool live = true;
 #pragma unroll
       for (int rb = 0; rb < RB; rb++) {
         float lmx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+        for (int kb = 0; kb < 2; kb++) {
+          float k = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 4; r++) lmx = fmaxf(lmx, S[kb][rb][r]);
+          for (int r = 0; r < 4; r++) k = fmaxf(k, S[kb][rb][r]);
+          lmx = fmaxf(lmx, SPLIT ? k - lsv[kb] : k);
+        }
+        if constexpr (FP8 && !SPLIT) lmx -= lsv_cur;
         const float mx = xor32_max(xor16_max(lmx));
-        const bool empty = o[NDB][rb][0] == 0.f;
+        const bool empty = (SPLIT ? xor32_sum(o[NDB][rb][0]) : o[NDB][rb][0]) == 0.f;
         const bool mv = mx > kRescaleSlack || (empty && mx > -INFINITY);
         live = live && (!empty || mx > -INFINITY);
         const float shift = mv ? mx : 0.f;
@@ -648,12 +783,15 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     };
     float mx = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < RB; rb++)
+    for (int kb = 0; kb < 2; kb++) {
+      float k = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
+      for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) mx = fmaxf(mx, S[kb][rb][r]);
-    if (__any(mx > kRescaleSlack) || !all_live) rescale();
+        for (int r = 0; r < 4; r++) k = fmaxf(k, S[kb][rb][r]);
+      mx = fmaxf(mx, SPLIT ? k - lsv[kb] : k);
+    }
+    if (__any(mx > (FP8 && !SPLIT ? thr : kRescaleSlack)) || !all_live) rescale();
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
@@ -662,20 +800,66 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
         pb[rb][4 + r] = (__bf16)fast_exp2(S[1][rb][r]);
       }
     }
+    // the phase's scalar loads (block ids, scales) have landed: with none
+    // outstanding, the compiler's LDS waits in the matrix-core phase that
+    // follows count reads precisely instead of waiting for all of them
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   };
 
-  // prologue: NST-1 steps requested; S(t0) for both groups, P(t0) for group 0
+  // prologue.  bf16: NST-1 steps requested, step t0 waited.  E4M3: NCS steps
+  // requested, t0 and t0+1 waited, then K(t0), V(t0), K(t0+1) widened.
+  if constexpr (FP8) {
 #pragma unroll
-  for (int k = 0; k < NST - 1; k++) issue(t_begin + k);
-  PA_WAIT_VMCNT(2 * (NST - 2));
-  wg_barrier();
-  qk_only(stage(t_begin));
-  // step t opens once this wave's share of step t+1 has landed (steps t+2 ..
-  // t+NST-2 may be in flight); step t+NST-1 is requested into the stage step
-  // t-1 left, during the wave's softmax phase.
+    for (int k = 0; k < NCS; k++) issue();
+    PA_WAIT_VMCNT(2 * (NCS - 2));
+    wg_barrier();
+    widen(t_begin, false);
+    widen(t_begin, true);
+    widen(t_begin + 1, false);  // (past the range end: a tile nothing reads)
+    read_scales(t_begin);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the widened tiles are written
+    wg_barrier();
+  } else {
+#pragma unroll
+    for (int k = 0; k < NST - 1; k++) issue();
+    PA_WAIT_VMCNT(2 * (NST - 2));
+    wg_barrier();
+  }
+  qk_only(ktile(t_begin));
+  // Each step opens once this wave's share of what the step reads has landed:
+  // bf16, step t+1 (steps t+2 .. t+NST-2 may be in flight; step t+NST-1 is
+  // requested into the stage step t-1 left); E4M3, the codes of step t+2
+  // (steps t+3 .. t+NCS-1 in flight; t+NCS requested into the stage of step
+  // t, whose codes were widened before), and the work-group then widens
+  // K(t+2) and V(t+1) during the step -- the tiles the next step reads.
   // With one barrier per step the groups stay half a step apart: the
   // barrier of step t finds group 0 about to start its matrix-core phase and
   // group 1 its vector phase.
+  auto open_step = [&]() __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      PA_WAIT_VMCNT(2 * (NCS - 3));
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's widened chunks are written
+    } else {
+      PA_WAIT_VMCNT(2 * (NST - 3));
+    }
+    wg_barrier();
+  };
+  // E4M3 widening of K(t+2) and V(t+1) around a softmax: the code reads go
+  // out first, the conversions and writes follow the softmax.  (Past the
+  // range end these touch only tiles nothing reads: no branch needed.)
+  uint2 wk = {}, wv = {};
+  auto widen_read = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      wk = lds_load8(widen_src(t + 2, false));
+      wv = lds_load8(widen_src(t + 1, true));
+    }
+  };
+  auto widen_write = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      lds_store16(widen_dst(t + 2, false), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(wk)));
+      lds_store16(widen_dst(t + 1, true), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(wv)));
+    }
+  };
   auto prio_hi = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
   };
@@ -694,38 +878,38 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
     softmax_rt(t_begin);
     int t = t_begin;
     auto body = [&](auto mtag) __attribute__((always_inline)) {
-      PA_WAIT_VMCNT(2 * (NST - 3));
-      wg_barrier();
+      open_step();
       prio_hi();
-      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase A: matrix cores
+      gemm(std::true_type{}, vtile(t), ktile(t + 1));  // phase A: matrix cores
       prio_lo();
-        issue(t + NST - 1);                                      // phase B: loads, vector ALUs
+      issue();                                          // phase B: loads, widening, vector ALUs
+      widen_read(t);
       softmax(mtag, t + 1);
+      widen_write(t);
     };
     for (const int t_open = min(t_full, t_end) - 1; t < t_open; t++) body(open);
     for (; t + 1 < t_end; t++) body(masked);
-    PA_WAIT_VMCNT(2 * (NST - 3));
-    wg_barrier();
-    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
-    issue(t + NST - 1);
+    open_step();
+    gemm(std::false_type{}, vtile(t), nullptr);
+    issue();
   } else {
     int t = t_begin;
     auto body = [&](auto mtag) __attribute__((always_inline)) {
-      PA_WAIT_VMCNT(2 * (NST - 3));
-      wg_barrier();
-      issue(t + NST - 1);
-      softmax(mtag, t);                                        // phase A: vector ALUs
-        prio_hi();
-      gemm(std::true_type{}, stage(t) + TILEB, stage(t + 1));  // phase B: matrix cores
+      open_step();
+      issue();
+      widen_read(t);
+      softmax(mtag, t);                                 // phase A: vector ALUs
+      widen_write(t);
+      prio_hi();
+      gemm(std::true_type{}, vtile(t), ktile(t + 1));  // phase B: matrix cores
       prio_lo();
     };
     for (const int t_open = min(t_full, t_end - 1); t < t_open; t++) body(open);
     for (; t + 1 < t_end; t++) body(masked);
-    PA_WAIT_VMCNT(2 * (NST - 3));
-    wg_barrier();
-    issue(t + NST - 1);
+    open_step();
+    issue();
     softmax_rt(t);
-    gemm(std::false_type{}, stage(t) + TILEB, nullptr);
+    gemm(std::false_type{}, vtile(t), nullptr);
   }
   PA_WAIT_VMCNT(0);  // the trailing (empty) step requests complete before exit
 
@@ -733,10 +917,14 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   for (int rb = 0; rb < RB; rb++) {
     const int row = wave * 48 + rb * 16 + c16;
     const int tok = row >> a.lg, gq = row & (a.group - 1);
-    const float lt = o[NDB][rb][0];
-    if (tok >= it.nq) continue;
+    float lt = o[NDB][rb][0];
+    if constexpr (FP8) {
+      lt *= SPLIT && g >= 2 ? isv[1] : isv[0];  // back from units of the last step's s_v
+      if constexpr (SPLIT) lt = xor32_sum(lt);
+    }
+    if (tok >= nq) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float mrow = -negm[rb];
+    const float mrow = -negm[rb] + (FP8 && !SPLIT ? lsv_cur : 0.f);
     const float lse2 = lt > 0.f ? mrow + __log2f(lt) : -INFINITY;
     if (it.part < 0) {
       const int64_t orow = (int64_t)(it.row0 + tok) * a.hq + kvh * a.group + gq;
@@ -758,15 +946,15 @@ __device__ __forceinline__ void w48_item(const AttnArgs a, const Item it, lds_u8
   }
 }
 
-template <int BS>
+template <int BS, bool FP8>
 __global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kW48Stages * 2 * kW48TileBytes];
-  __shared__ int bt_lds[kMaxDmaItemKeys / BS + 2];
+  constexpr int RING = FP8 ? kW48Fp8Lds : kW48Stages * 2 * kW48TileBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[RING];
   const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
   const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
   for (int i = first; i < last; i++) {
     if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
-    w48_item<BS>(a, a.items[i], (lds_u8 *)smem_raw, bt_lds);
+    w48_item<BS, FP8>(a, a.items[i], (lds_u8 *)smem_raw);
   }
 }
 
@@ -1575,9 +1763,9 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a, int first)
 // =============================================================================
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
-  if constexpr (!FP8 && D == 128) {
+  if constexpr (D == 128) {
     if (a.tile_rows == kW48TileRows) {
-      hipLaunchKernelGGL((prefill_w48_kernel<BS>), dim3(n), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((prefill_w48_kernel<BS, FP8>), dim3(n), dim3(512), 0, s, a);
       return hipGetLastError();
     }
   }

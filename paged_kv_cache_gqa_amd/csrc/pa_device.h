@@ -203,6 +203,12 @@ __device__ __forceinline__ void dma_load16_nt(i32x4_t rsrc, int voff, uint32_t l
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
+// one dword per lane (buffer_load_dword ... lds writes lane l's 4 bytes to
+// M0 + 4 * lane): with the same offset in every lane, 64 copies of one value
+__device__ __forceinline__ void dma_load4(i32x4_t rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
 // s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (n < 64: the count's
 // low four bits sit in bits 3:0 of the immediate, its high two in bits 15:14)
 #define PA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))

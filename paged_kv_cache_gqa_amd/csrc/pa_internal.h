@@ -107,36 +107,10 @@ struct GatherArgs {
   int32_t row_bytes;      // d * element bytes
 };
 
-// E4M3 caches feed the bf16 prefill kernels through a bf16 copy of each
-// prefilled sequence's context: blocks j0 .. j1-1 of sequence seq go to
-// compact blocks base + j0 .. base + j1-1 (block j of the sequence at compact
-// block base + j, all KV heads).
-struct DqItem {
-  int32_t seq, j0, j1, base;
-};
-static_assert(sizeof(DqItem) == 16, "DqItem layout");
-
-struct DequantArgs {
-  const void *k;            // E4M3 codes [num_blocks][hkv][bs][d]
-  const void *v;
-  const float *ks;          // [num_blocks][hkv]
-  const float *vs;
-  const int32_t *bt;        // the caller's block tables [num_seqs][max_blocks]
-  int32_t max_blocks;
-  int32_t hkv, bs, d;
-  const DqItem *items;
-  void *k_out;              // bf16 [compact blocks][hkv][bs][d]
-  void *v_out;
-  int32_t *bt_out;          // compact block tables [num_seqs][mb_out]
-  int32_t mb_out;
-};
-
 constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
 constexpr int kW48TileRows = 384;  // query rows per tile of prefill_w48_kernel
 constexpr int kDmaTileRows = kW48TileRows;  // the LDS-DMA prefill (head_dim 128)
 constexpr int kPrefillRowsMax = 384;
-// keys per item of the LDS-DMA prefill kernel (its block ids are staged in LDS)
-constexpr int kMaxDmaItemKeys = 131072;
 constexpr int kMaxDecItemKeys = 32768;  // keys per decode item (block ids staged in LDS)
 constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
@@ -156,7 +130,6 @@ hipError_t launch_peak_mfma(float *out, int iters, hipStream_t s);
 hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_xcc_ids(int32_t *out, int n, hipStream_t s);
-hipError_t launch_dequant(const DequantArgs &a, int n_items, hipStream_t s);
 hipError_t launch_stage(const void *src_host, void *dst, size_t bytes, hipStream_t s);
 
 }  // namespace pa

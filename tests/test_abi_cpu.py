@@ -143,8 +143,6 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
     for idx, it in enumerate(items):
         seq, kvh, row0, pos0, nq, lo, hi, part = (int(x) for x in it)
         assert 0 <= kvh < hkv and nq >= 1 and nq * G <= (384 if d == 128 else 128)
-        if d == 128 and nq * G > 16:  # LDS-staged block ids bound the item's span
-            assert hi - lo <= 131072
         assert lo % 64 == 0 and hi > lo
         assert rowstart[seq] <= row0 and row0 + nq <= rowstart[seq] + incr[seq]
         assert pos0 == hist[seq] + (row0 - rowstart[seq])
@@ -165,7 +163,26 @@ def check_cover(pa, hist, incr, hq, hkv, d=128, bs=16):
             assert rng[-1][1] >= pos + 1
     assert all(v == 1 for v in parts.values())
     assert len(parts) == counts[3]
+    if d == 128:
+        # the persistent prefill never cuts a (tile, head) for length: a
+        # partial slot per work-group boundary it crosses, at most
+        units = {(int(it[2]), int(it[1])) for it in items[:counts[0]]}
+        pre_parts = sum(1 for k in parts if k[0])
+        assert pre_parts <= len(units) + 256, (pre_parts, len(units))
     return items, counts
+
+
+def test_prefill_workspace_does_not_grow_with_context(palib):
+    """An E4M3 incremental prefill of 4,096 tokens over 128K, 512K and 1M
+    cached tokens: the work list and partials hold the same few slots (no
+    per-context copy, no per-length cuts); coverage checked at 1M."""
+    pa = palib
+    c = cache(pa, dtype=pa.PA_KV_FP8_E4M3, k_scale=FAKE, v_scale=FAKE, block_size=64)
+    sizes = [pa.pa_workspace_size([h], [4096], 32, c) for h in (131_072, 524_288, 1_044_480)]
+    bound = (43 * 8 + 256) * 384 * (128 + 1) * 4 + (1 << 20)  # (units + boundaries) partials + list
+    assert all(x <= bound for x in sizes), (sizes, bound)
+    assert max(sizes) <= 1.05 * min(sizes), sizes
+    check_cover(pa, [1_044_480], [4096], 32, 8, bs=64)
 
 
 def test_planner_balances_persistent_prefill(palib):
