@@ -158,6 +158,29 @@ PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
                              float *lse_out, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Maximum scratch of paged_attn_forward_noalloc, bytes per device. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * paged_attn_forward_noalloc -- paged_attn_forward for callers that cannot
+ * allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * error behaviour, without the workspace arguments.  Its scratch is a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES, one per device, that the
+ * library holds until the process ends; the call allocates no device or
+ * pinned host memory (the work list reaches the device by a stream-ordered
+ * copy from host memory).  A step that needs more scratch than that fails
+ * with PA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (use
+ * paged_attn_forward with a workspace).  Calls that overlap on one device
+ * share the array and race; calls ordered on one stream are safe.  The
+ * scratch keeps the last call's contents; no call relies on them.
+ */
+PA_API pa_status paged_attn_forward_noalloc(const void *q, const pa_kv_cache *cache,
+                                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t *hist_lens, const int32_t *incr_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                                            void *out, float *lse_out, void *stream);
+
 /* Bytes of workspace paged_attn_forward needs for these HOST lengths.
  * Returns 0 and sets pa_last_error() if the arguments are invalid. */
 PA_API size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int32_t num_seqs,

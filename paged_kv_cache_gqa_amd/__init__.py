@@ -24,7 +24,8 @@ TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
            "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read", "pa_device_shape",
-           "pa_debug_xcc_ids")
+           "pa_debug_xcc_ids", "paged_attn_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
 class pa_kv_cache(C.Structure):
@@ -62,7 +63,8 @@ def _load():
     L.pa_peak_read.argtypes = [P, sz, P, P]
     L.pa_device_shape.argtypes = [C.POINTER(i32), C.POINTER(i32)]
     L.pa_debug_xcc_ids.argtypes = [P, i32, P]
-    for f in ("kv_append", "paged_attn_forward", "pa_debug_gather", "pa_timing_enable",
+    L.paged_attn_forward_noalloc.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P]
+    for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "pa_debug_gather", "pa_timing_enable",
               "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
               "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids"):
         getattr(L, f).restype = C.c_int
@@ -221,6 +223,33 @@ def paged_attn_forward(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens
         h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq,
         float(scale), _ptr(out), _ptr(lse_out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _stream_ptr(stream)))
+
+
+def paged_attn_forward_noalloc(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale,
+                               out, lse_out=None, stream=None):
+    """paged_attn_forward without a workspace: the library's static scratch
+    (for callers that cannot allocate)."""
+    import torch
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    if h.shape != n.shape or h.ndim != 1:
+        _bad("hist_lens and incr_lens must be 1-D of equal length")
+    dev = getattr(cache, "device", None)
+    total_q = int(n.astype(np.int64).sum())
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        _bad("q must be a 3-D tensor [total_q, num_q_heads, head_dim]")
+    hq = int(q.shape[1])
+    ok = [_tensor(q, "q", _bf16(), (total_q, hq, cache.head_dim)),
+          _tensor(out, "out", _bf16(), (total_q, hq, cache.head_dim))]
+    if lse_out is not None:
+        ok.append(_tensor(lse_out, "lse_out", (torch.float32,), (total_q, hq)))
+    ok.append(_tensor(block_tables, "block_tables", (torch.int32,), (None, None)))
+    if int(block_tables.shape[0]) < len(h):
+        _bad(f"block_tables has {int(block_tables.shape[0])} rows for {len(h)} sequences")
+    _on_device(ok, dev)
+    _check(lib.paged_attn_forward_noalloc(
+        _ptr(q), C.byref(cache), _ptr(block_tables), int(block_tables.shape[1]),
+        h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq,
+        float(scale), _ptr(out), _ptr(lse_out), _stream_ptr(stream)))
 
 
 def pa_debug_gather(cache: pa_kv_cache, block_table_row, ctx, k_out, v_out, stream=None):

@@ -22,6 +22,9 @@
 
 using namespace pa;
 
+// The no-allocation entry point's scratch (see scratch_address below).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -489,6 +492,41 @@ pa_status stage_copy(const void *src, size_t bytes, void *dst_dev, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
+// Scratch of paged_attn_forward_noalloc: a static device array, one copy per
+// device the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address (in host code it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.  Its contents need no initialisation
+// (the work list is copied in by each call; every partial result is written
+// before it is read), and calls that overlap on one device share it and race.
+// (the array itself: file scope, above)
+
+struct DeviceScratch {
+  int device;
+  unsigned char *ptr;
+};
+std::mutex g_scratch_mu;
+std::vector<DeviceScratch> g_scratch;
+
+pa_status scratch_address(unsigned char **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  for (const auto &d : g_scratch)
+    if (d.device == dev) {
+      *out = d.ptr;
+      return PA_OK;
+    }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+  g_scratch.push_back({dev, (unsigned char *)p});
+  *out = (unsigned char *)p;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 constexpr int kKinds = 5;
 std::mutex g_time_mu;
@@ -617,12 +655,18 @@ size_t pa_workspace_size(const int32_t *hist_lens, const int32_t *incr_lens, int
   return std::max<size_t>(P.total, 256);
 }
 
-pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
-                             const int32_t *block_tables, int32_t max_blocks_per_seq,
-                             const int32_t *hist_lens, const int32_t *incr_lens,
-                             int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
-                             float *lse_out, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation, planning and launches shared by both forward entry points.
+// workspace == nullptr: the static scratch (no allocation anywhere: the work
+// list goes in by a stream-ordered copy from host memory instead of through
+// the pinned staging ring, which is allocated on first use).
+pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_tables,
+                  int32_t max_blocks_per_seq, const int32_t *hist_lens, const int32_t *incr_lens,
+                  int32_t num_seqs, int32_t num_q_heads, float scale, void *out, float *lse_out,
+                  void *workspace, size_t workspace_bytes, void *stream, bool no_alloc) {
   pa_status st = check_cache(cache);
   if (st) return st;
   if (max_blocks_per_seq < 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq < 0");
@@ -638,6 +682,18 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
   make_plan(hist_lens, incr_lens, num_seqs, cache, group, P);
+  if (no_alloc) {
+    if (P.total > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                  "this step needs %zu bytes of scratch, more than the %zu of the no-allocation entry point "
+                  "(use paged_attn_forward with a workspace)",
+                  P.total, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+    unsigned char *sp = nullptr;
+    st = scratch_address(&sp);
+    if (st) return st;
+    workspace = sp;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace) return fail(PA_ERR_NULL_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(PA_ERR_BAD_SHAPE, "workspace not 256-byte aligned");
   if (workspace_bytes < P.total)
@@ -652,9 +708,13 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
     memcpy(host.data() + P.off_wg, P.wg_first.data(), P.wg_first.size() * sizeof(int32_t));
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
-  st = stage_copy(host.data(), P.plan_bytes, ws, s);
-  if (st) return st;
-
+  if (no_alloc) {
+    hipError_t e = hipMemcpyAsync(ws, host.data(), P.plan_bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "work-list copy");
+  } else {
+    st = stage_copy(host.data(), P.plan_bytes, ws, s);
+    if (st) return st;
+  }
   AttnArgs a{};
   a.q = q;
   a.c.k = cache->k_cache;
@@ -717,6 +777,29 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *hist_lens, const int32_t *incr_lens,
+                             int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
+                             float *lse_out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs,
+                 num_q_heads, scale, out, lse_out, workspace, workspace_bytes, stream, false);
+}
+
+pa_status paged_attn_forward_noalloc(const void *q, const pa_kv_cache *cache,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *hist_lens, const int32_t *incr_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
+                                     float *lse_out, void *stream) {
+  return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs,
+                 num_q_heads, scale, out, lse_out, nullptr, 0, stream, true);
 }
 
 pa_status pa_device_shape(int32_t *num_cus, int32_t *num_xcds) {

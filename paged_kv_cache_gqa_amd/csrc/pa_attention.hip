@@ -481,7 +481,6 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // counted with the K/V stream by vmcnt, and staging them in LDS would bound
   // the length of an item (the planner never cuts an item for length).
   typedef const __attribute__((address_space(4))) int32_t cint;
-  typedef const __attribute__((address_space(4))) float cfloat;
   const cint *btr = (const cint *)(a.bt + (int64_t)it.seq * a.max_blocks);
   auto block_of = [&](int key) __attribute__((always_inline)) { return btr[min(key / BS, last_blk)]; };
 

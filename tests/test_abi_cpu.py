@@ -365,3 +365,18 @@ def test_binding_rejects_bad_tensors(palib):
     _expect_bad(pa, lambda: pa.pa_debug_gather(c, torch.zeros(4, dtype=i32), 40,
                                                torch.zeros((40, 2, 32), dtype=bf),
                                                torch.zeros((40, 2, 64), dtype=bf)), "shape")
+
+
+def test_noalloc_rejects_steps_beyond_its_scratch(palib):
+    """The no-allocation entry point refuses, before touching the device, a
+    step whose plan needs more than its static scratch."""
+    pa = palib
+    c = cache(pa, num_blocks=1 << 30)
+    h = np.full(512, 1_000_000, np.int32)  # 512 decodes over a million tokens each
+    n = np.full(512, 1, np.int32)
+    need = pa.pa_workspace_size(h, n, 32, c)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    st = pa.lib.paged_attn_forward_noalloc(FAKE, C.byref(c), FAKE, 62_501, h.ctypes.data_as(C.c_void_p),
+                                           n.ctypes.data_as(C.c_void_p), 512, 32, 0.088, FAKE, None, None)
+    assert st == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in pa.pa_last_error()
