@@ -94,9 +94,25 @@ class Runner:
                                dtype=torch.bfloat16, device=dev)
         self.stream = torch.cuda.current_stream()
 
+    def use_cascade(self):
+        """Run steps through paged_attn_forward_cascade with the workload's
+        shared-prefix group declared (the sub-agents of the mixed step)."""
+        spec, b, pa = self.spec, self.b, self.pa
+        self.group_of = [0 if s in spec.shared_seqs else -1 for s in range(spec.num_seqs)]
+        self.group_len = [spec.shared_prefix_tokens]
+        need = pa.cascade_workspace_size(b.hist, b.incr, spec.num_q_heads, self.cache, self.bt,
+                                         self.group_of, self.group_len, spec.scale)
+        self.ws = self.torch.empty(need, dtype=self.torch.uint8, device=self.ws.device)
+        self.cascade = True
+
     def step(self):
         b, pa = self.b, self.pa
         pa.kv_append(self.cache, b.k_new, b.v_new, self.slots, stream=self.stream)
+        if getattr(self, "cascade", False):
+            pa.paged_attn_forward_cascade(b.q, self.cache, self.bt, b.hist, b.incr, self.spec.scale,
+                                          self.out, self.ws, self.group_of, self.group_len,
+                                          stream=self.stream)
+            return
         pa.paged_attn_forward(b.q, self.cache, self.bt, b.hist, b.incr, self.spec.scale, self.out,
                               self.ws, stream=self.stream)
 
@@ -131,7 +147,7 @@ class Runner:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         kern = {}
-        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "dequant")):
+        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "cascade")):
             tot, cnt = pa.pa_timing_read(kind)
             if cnt:
                 kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step
@@ -265,15 +281,20 @@ def mixed_parts(spec):
     return fl, dfl, byts
 
 
-def report_mixed(pa, torch, spec, dev, steps, warmup, label):
+def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False):
     """One call holding 4 incremental prefills and 48 decodes: the prefill
-    part in TFLOP/s over its kernel, the decode part in GB/s over its kernel
-    (the shared prefix's blocks counted once)."""
+    part in TFLOP/s over its kernel, the decode part in GB/s over its kernels
+    (decode, plus the shared-prefix cascade when the sub-agents are declared as
+    a group; the shared prefix's blocks counted once either way)."""
     r = Runner(pa, torch, spec, dev)
+    if cascade:
+        r.use_cascade()
     ms, kern = r.timed(steps, warmup)
     fl, _, byts = mixed_parts(spec)
     p_ms = kern["prefill"][0] * kern["prefill"][1]
     d_ms = kern["decode"][0] * kern["decode"][1]
+    if "cascade" in kern:
+        d_ms += kern["cascade"][0] * kern["cascade"][1]
     d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
          "prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
          "prefill_frac": round(fl / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -332,6 +353,44 @@ def report_append(pa, torch, dev, tokens, steps, label):
     return out
 
 
+def report_append_e4m3(pa, torch, dev, tokens, steps, label):
+    """The long-context step's quantising kv_append: `tokens` bf16 tokens (8 KV
+    heads, d 128) into an E4M3 cache of block 64 with per-(block, head)
+    scales, in a seeded permuted block order."""
+    import workloads as W
+    hkv, d, bs = 8, 128, 64
+    nb = (tokens + bs - 1) // bs
+    kc = torch.zeros((nb, hkv, bs, d), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    k_new = W.randn_bf16((tokens, hkv, d), dev, 91, 3)
+    v_new = W.randn_bf16((tokens, hkv, d), dev, 91, 4)
+    ks = torch.full((nb, hkv), 4.5 / 448, dtype=torch.float32, device=dev)
+    vs = torch.full((nb, hkv), 4.5 / 448, dtype=torch.float32, device=dev)
+    cache = pa.make_cache(kc, vc, ks, vs)
+    perm = torch.from_numpy(np.random.default_rng(91).permutation(nb).astype(np.int64)).to(dev)
+    pos = torch.arange(tokens, device=dev, dtype=torch.int64)
+    slots = perm[pos // bs] * bs + pos % bs
+    s = torch.cuda.current_stream()
+    pa.kv_append(cache, k_new, v_new, slots, stream=s)
+    torch.cuda.synchronize()
+    pa.pa_timing_read(0)
+    pa.pa_timing_enable(True)
+    for _ in range(steps):
+        pa.kv_append(cache, k_new, v_new, slots, stream=s)
+    torch.cuda.synchronize()
+    pa.pa_timing_enable(False)
+    tot, cnt = pa.pa_timing_read(0)
+    k_ms = tot / cnt
+    # K and V: bf16 read, E4M3 written; slots; each (token, head)'s two scales
+    byts = 2 * tokens * hkv * d * (2 + 1) + tokens * 8 + tokens * hkv * 2 * 4
+    out = {"workload": label, "tokens": tokens, "kernel_ms": round(k_ms, 4),
+           "GB/s": round(byts / (k_ms * 1e-3) / 1e9, 1),
+           "frac": round(byts / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byts)}
+    del kc, vc, k_new, v_new
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_peaks(pa, torch, dev):
     """The chip's practical ceilings, measured with the instructions the
     kernels use (the library's measurement hooks): back-to-back bf16 MFMAs on
@@ -381,41 +440,72 @@ def add_measured_fractions(obj, peaks):
             add_measured_fractions(v, peaks)
 
 
-def run_cpu_baseline(spec, budget_s):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_baseline(spec, budget_s, min_rows=512):
     """The oracle, as it stands, on a bounded sample of the workload's query rows
-    (all heads), on this host's cores.  Rate in the metric's unit."""
+    (all heads), on this host's cores: at least min_rows rows (more if the
+    budget allows), with the host's provenance and a one-thread rate on the
+    tiny workload and on a few rows of this one.  Rate in the metric's unit."""
     import oracle
     import torch
     import workloads as W
-    b = W.make_batch(spec, "cpu")
 
     def bits(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    kc, vc = bits(b.k_pool).copy(), bits(b.v_pool).copy()
-    oracle.kv_append(kc, vc, None, None, oracle.KV_BF16, bits(b.k_new), bits(b.v_new),
-                     b.slot_mapping.numpy())
-    q = bits(b.q)
+    def prepared(sp):
+        b = W.make_batch(sp, "cpu")
+        kc, vc = bits(b.k_pool).copy(), bits(b.v_pool).copy()
+        oracle.kv_append(kc, vc, None, None, oracle.KV_BF16, bits(b.k_new), bits(b.v_new),
+                         b.slot_mapping.numpy())
+        return b, kc, vc, bits(b.q)
+
+    def timed_rows(b, kc, vc, q, sp, rows):
+        t0 = time.time()
+        oracle.attention(q, kc, vc, None, None, oracle.KV_BF16, b.block_tables, b.hist, b.incr,
+                         sp.num_q_heads, sp.scale, rows=rows)
+        dt = max(time.time() - t0, 1e-6)
+        rs = np.concatenate([[0], np.cumsum(b.incr)])
+        pairs = 0
+        for r in rows:
+            s = int(np.searchsorted(rs, r, side="right") - 1)
+            pairs += int(b.hist[s]) + int(r - rs[s]) + 1
+        return 4 * sp.head_dim * sp.num_q_heads * pairs / dt / 1e12, dt
+
+    b, kc, vc, q = prepared(spec)
     rng = np.random.default_rng(0)
     n_incr = int(b.incr[0])
-    # calibrate with a few rows, then size the sample to the budget
-    rows = [n_incr - 1]
-    t0 = time.time()
-    oracle.attention(q, kc, vc, None, None, oracle.KV_BF16, b.block_tables, b.hist, b.incr,
-                     spec.num_q_heads, spec.scale, rows=rows)
-    t1 = max(time.time() - t0, 1e-3)
-    n = int(max(1, min(n_incr, budget_s / t1)))
+    # calibrate with a few rows, then size the sample to the budget (at least min_rows)
+    _, t1 = timed_rows(b, kc, vc, q, spec, [n_incr - 1])
+    n = int(max(min(min_rows, n_incr), min(n_incr, budget_s / t1)))
     rows = np.sort(rng.choice(n_incr, size=n, replace=False)).astype(np.int64)
-    t0 = time.time()
-    oracle.attention(q, kc, vc, None, None, oracle.KV_BF16, b.block_tables, b.hist, b.incr,
-                     spec.num_q_heads, spec.scale, rows=rows)
-    dt = time.time() - t0
-    pairs = sum(int(b.hist[0]) + int(r) + 1 for r in rows)
-    flops = 4 * spec.head_dim * spec.num_q_heads * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    value, dt = timed_rows(b, kc, vc, q, spec, rows)
+    threads = oracle.num_threads()
+    # one thread: the tiny workload (all rows) and four rows of this one
+    prev = oracle.set_num_threads(1)
+    try:
+        tb = prepared(W.tiny())
+        tiny_1t, tiny_s = timed_rows(*tb, W.tiny(), list(range(W.tiny().total_q)))
+        incr_1t, incr_s = timed_rows(b, kc, vc, q, spec, list(rows[:: max(1, len(rows) // 4)][:4]))
+    finally:
+        oracle.set_num_threads(prev)
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {n_incr} query rows (all {spec.num_q_heads} heads) of the headline "
-                      f"workload, fp64, {dt:.1f} s, host {os.cpu_count()} CPUs"}
+                      f"workload, fp64, {dt:.1f} s on {threads} threads",
+            "host": {"cpu_model": _cpu_model(), "nproc": len(os.sched_getaffinity(0)),
+                     "os_cpu_count": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")},
+            "one_thread": {"tiny_TFLOP/s": tiny_1t, "tiny_s": round(tiny_s, 3),
+                           "incremental_TFLOP/s": incr_1t, "incremental_rows": 4,
+                           "incremental_s": round(incr_s, 2)}}
 
 
 # ---------------------------------------------------------------------------
@@ -446,7 +536,8 @@ KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_append.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-PREFILL_KERNEL = "void pa::prefill_w48_kernel<16>(pa::AttnArgs)"
+PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, false>(pa::AttnArgs)"
+PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, true>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
 APPEND_KERNEL = "void pa::append_kernel<false>(pa::AppendArgs)"
@@ -727,7 +818,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill_incremental_bytes"),
-                     "kernel": "prefill_w48_kernel<16>",
+                     "kernel": "prefill_w48_kernel<16, false>",
                      "kernel_ms": round(k_ms, 4)},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
     }
@@ -773,7 +864,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_incremental_128k_bytes"),
-                         "kernel": "prefill_w48_kernel<16>", "kernel_ms": round(pk_ms, 4)},
+                         "kernel": "prefill_w48_kernel<16, false>", "kernel_ms": round(pk_ms, 4)},
         }
         del r
         torch.cuda.empty_cache()
@@ -791,6 +882,10 @@ def main():
             pa, torch, W.mixed(), dev, rs, rw,
             "mixed: 4 incremental prefills (lognormal histories, median 100K) + 48 decodes "
             "(8 over a shared 10,000-token prefix), 32 q / 8 KV, d 128, block 16, bf16, one call")
+        rep["mixed_step_cascade"] = report_mixed(
+            pa, torch, W.mixed(), dev, rs, rw,
+            "the same mixed step through paged_attn_forward_cascade, the 8 sub-agents declared as a "
+            "group over their shared 10,000 tokens", cascade=True)
         lspec = W.long_context()
         lr = Runner(pa, torch, lspec, dev)
         rep["long_context_prefill_e4m3"] = report_prefill(
@@ -807,6 +902,9 @@ def main():
                                                "kv_append of 45,700 bf16 tokens (initial prefill)")
         rep["kv_append_1m"] = report_append(pa, torch, dev, 1_048_576, 5,
                                             "kv_append of 1,048,576 bf16 tokens")
+        rep["kv_append_e4m3_4096"] = report_append_e4m3(
+            pa, torch, dev, 4_096, 20,
+            "kv_append of the long-context step's 4,096 tokens into the E4M3 cache (block 64, quantising)")
         line["reports"] = rep
     if not args.no_peaks:
         peaks = measure_peaks(pa, torch, dev)

@@ -158,6 +158,37 @@ PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
                              float *lse_out, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * paged_attn_forward_cascade -- paged_attn_forward for a step in which groups
+ * of sequences share a prefix: the same physical blocks hold their first
+ * tokens ([Agentic] §2.1: sub-agents fan out from the main agent's context;
+ * §4.1: prefix reuse).  Same computation and arguments as paged_attn_forward,
+ * plus:
+ *   group_of   HOST int32 [num_seqs]: each sequence's prefix group, -1 for
+ *              none (NULL allowed when num_groups == 0).
+ *   group_len  HOST int32 [num_groups]: tokens of the group's shared prefix,
+ *              a multiple of block_size.  Caller promise: every member s of
+ *              group g has the same block ids in block_tables[s][0 ..
+ *              group_len[g] / block_size - 1] (results are undefined if not).
+ *   workspace_bytes  in: the workspace's size; with workspace == NULL the
+ *              call only writes the size it needs there and returns PA_OK.
+ * With bf16 KV and head_dim 128, the members of a group that decode one token
+ * over a history covering the shared prefix (at least two of them) read the
+ * prefix once: their rows (up to 64 per tile) are computed against it as one
+ * tile per KV head and key range, and each member's partial result is merged
+ * by LSE with its own suffix's.  Other sequences, and other cache types, are
+ * computed as paged_attn_forward computes them.  Results agree with
+ * paged_attn_forward within rounding (the key ranges are split differently),
+ * not bit for bit.
+ */
+PA_API pa_status paged_attn_forward_cascade(const void *q, const pa_kv_cache *cache,
+                                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t *hist_lens, const int32_t *incr_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                                            void *out, float *lse_out, const int32_t *group_of,
+                                            const int32_t *group_len, int32_t num_groups,
+                                            void *workspace, size_t *workspace_bytes, void *stream);
+
 /* Maximum scratch of paged_attn_forward_noalloc, bytes per device. */
 #define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
@@ -201,7 +232,7 @@ PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_
  * records HIP events on the call's stream around the kernel; the durations
  * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
  * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention,
- * 3 = LSE merge, 4 = unused (kept for numbering), the summed
+ * 3 = LSE merge, 4 = shared-prefix cascade, the summed
  * milliseconds and launch count since the last reset (it synchronises on the
  * recorded events), then resets that kind. */
 PA_API pa_status pa_timing_enable(int enable);

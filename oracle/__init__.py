@@ -71,6 +71,8 @@ def lib():
         L.orc_merge.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = C.c_int
+        L.orc_set_num_threads.argtypes = [C.c_int]
+        L.orc_set_num_threads.restype = C.c_int
         _lib = L
     return _lib
 
@@ -112,6 +114,11 @@ def div_f32(x: float, s: float) -> float:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Threads for the following calls; returns the previous count."""
+    return int(lib().orc_set_num_threads(int(n)))
 
 
 def kv_append(k_cache, v_cache, k_scale, v_scale, dtype, k_new, v_new, slot_mapping):

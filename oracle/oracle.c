@@ -387,3 +387,13 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the following calls (n >= 1); returns the previous setting.
+ * Only the distribution of independent outputs changes, not the arithmetic. */
+int orc_set_num_threads(int n) {
+  const int prev = orc_num_threads();
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#endif
+  return prev;
+}

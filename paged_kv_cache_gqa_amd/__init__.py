@@ -18,13 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK, PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = 4, 5
 PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
-TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
+TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE, TIMING_CASCADE = 0, 1, 2, 3, 4
 
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
            "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read", "pa_device_shape",
-           "pa_debug_xcc_ids", "paged_attn_forward_noalloc")
+           "pa_debug_xcc_ids", "paged_attn_forward_noalloc", "paged_attn_forward_cascade")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
@@ -64,7 +64,9 @@ def _load():
     L.pa_device_shape.argtypes = [C.POINTER(i32), C.POINTER(i32)]
     L.pa_debug_xcc_ids.argtypes = [P, i32, P]
     L.paged_attn_forward_noalloc.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P]
-    for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "pa_debug_gather", "pa_timing_enable",
+    L.paged_attn_forward_cascade.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P, P, i32, P,
+                                             C.POINTER(sz), P]
+    for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "paged_attn_forward_cascade", "pa_debug_gather", "pa_timing_enable",
               "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
               "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids"):
         getattr(L, f).restype = C.c_int
@@ -223,6 +225,60 @@ def paged_attn_forward(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens
         h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq,
         float(scale), _ptr(out), _ptr(lse_out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _stream_ptr(stream)))
+
+
+def _groups(group_of, group_len, num_seqs):
+    go = _host_i32(group_of)
+    gl = _host_i32(group_len)
+    if go.shape != (num_seqs,) or gl.ndim != 1:
+        _bad("group_of must have one entry per sequence and group_len be 1-D")
+    return go, gl
+
+
+def cascade_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache, block_tables,
+                           group_of, group_len, scale) -> int:
+    """Workspace bytes paged_attn_forward_cascade needs for this step."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    go, gl = _groups(group_of, group_len, len(h))
+    need = C.c_size_t(0)
+    _check(lib.paged_attn_forward_cascade(
+        None, C.byref(cache), None, int(block_tables.shape[1]), h.ctypes.data_as(C.c_void_p),
+        n.ctypes.data_as(C.c_void_p), len(h), int(num_q_heads), float(scale), None, None,
+        go.ctypes.data_as(C.c_void_p), gl.ctypes.data_as(C.c_void_p), len(gl), None, C.byref(need), None))
+    return int(need.value)
+
+
+def paged_attn_forward_cascade(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale, out,
+                               workspace, group_of, group_len, lse_out=None, stream=None):
+    """paged_attn_forward with declared shared-prefix groups (group_of [num_seqs],
+    -1 = none; group_len [num_groups], tokens, multiples of the block size)."""
+    import torch
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    if h.shape != n.shape or h.ndim != 1:
+        _bad("hist_lens and incr_lens must be 1-D of equal length")
+    go, gl = _groups(group_of, group_len, len(h))
+    dev = getattr(cache, "device", None)
+    total_q = int(n.astype(np.int64).sum())
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        _bad("q must be a 3-D tensor [total_q, num_q_heads, head_dim]")
+    hq = int(q.shape[1])
+    ok = [_tensor(q, "q", _bf16(), (total_q, hq, cache.head_dim)),
+          _tensor(out, "out", _bf16(), (total_q, hq, cache.head_dim))]
+    if lse_out is not None:
+        ok.append(_tensor(lse_out, "lse_out", (torch.float32,), (total_q, hq)))
+    ok.append(_tensor(block_tables, "block_tables", (torch.int32,), (None, None)))
+    if int(block_tables.shape[0]) < len(h):
+        _bad(f"block_tables has {int(block_tables.shape[0])} rows for {len(h)} sequences")
+    if not isinstance(workspace, torch.Tensor):
+        _bad("workspace must be a torch.Tensor")
+    ok.append(_tensor(workspace, "workspace", (workspace.dtype,)))
+    _on_device(ok, dev)
+    cap = C.c_size_t(int(workspace.numel() * workspace.element_size()))
+    _check(lib.paged_attn_forward_cascade(
+        _ptr(q), C.byref(cache), _ptr(block_tables), int(block_tables.shape[1]),
+        h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq, float(scale),
+        _ptr(out), _ptr(lse_out), go.ctypes.data_as(C.c_void_p), gl.ctypes.data_as(C.c_void_p), len(gl),
+        _ptr(workspace), C.byref(cap), _stream_ptr(stream)))
 
 
 def paged_attn_forward_noalloc(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale,

@@ -132,7 +132,12 @@ struct Plan {
   std::vector<int32_t> wg_first;  // persistent prefill launch: items of work-group w are
                                   // prefill[wg_first[w] .. wg_first[w+1]); empty otherwise
   int64_t n_part_prefill = 0, n_part_decode = 0;
-  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, plan_bytes = 0;
+  // shared-prefix cascade: items and their member tables; the widest item's rows
+  std::vector<CascadeItem> cascade;
+  std::vector<CascadeMember> members;
+  int32_t cascade_rows = 0;
+  size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, off_cascade = 0, off_members = 0,
+         plan_bytes = 0;
   size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
 };
 
@@ -141,6 +146,15 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Tile {
   int32_t seq, row0, pos0, nq, keys;  // keys = last row's position + 1
   bool decode;
+  int32_t shared = 0;  // leading keys computed by a shared-prefix cascade item instead
+};
+
+// Prefix groups a caller declares (paged_attn_forward_cascade): group_of[s]
+// (-1 = none) and the shared length of each group.
+struct Groups {
+  const int32_t *group_of = nullptr;
+  const int32_t *group_len = nullptr;
+  int32_t num_groups = 0;
 };
 
 // Balanced cut of [0, keys) into n ranges whose inner boundaries are
@@ -292,7 +306,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
 }
 
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const pa_kv_cache *c,
-               int32_t group, Plan &P) {
+               int32_t group, Plan &P, const Groups *groups = nullptr) {
   const int32_t hkv = c->num_kv_heads, d = c->head_dim, tile_rows = prefill_tile_rows(c);
   const MachineShape M = machine_shape();
   const int64_t decode_target_items = (int64_t)kDecodeItemsPerCU * M.cus;
@@ -315,6 +329,25 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
     }
     row += n;
   }
+  // Shared-prefix cascade (bf16 KV, head_dim 128): a declared group's decode
+  // members (one new token, history covering the shared prefix) leave the
+  // prefix to cascade items; a group needs at least two such members.
+  std::vector<std::vector<int32_t>> group_tiles;
+  if (groups && groups->num_groups > 0 && c->dtype == PA_KV_BF16 && d == 128) {
+    group_tiles.resize(groups->num_groups);
+    for (size_t i = 0; i < tiles.size(); i++) {
+      const Tile &t = tiles[i];
+      const int32_t g = groups->group_of[t.seq];
+      if (!t.decode || t.nq != 1 || g < 0) continue;
+      const int32_t L = groups->group_len[g];
+      if (L > 0 && hist[t.seq] >= L) group_tiles[g].push_back((int32_t)i);
+    }
+    for (auto &v : group_tiles)
+      if (v.size() >= 2)
+        for (int32_t i : v) tiles[i].shared = groups->group_len[groups->group_of[tiles[i].seq]];
+      else
+        v.clear();
+  }
   int64_t wd = 0, wp = 0, np0 = 0;
   for (const Tile &t : tiles) {
     if (t.decode)
@@ -335,23 +368,37 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
     plan_persistent(tiles, hkv, tile_rows, M, P);
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
-  for (const Tile &t : tiles) {
+  // cascade members: the first partial slot of tile i's KV head kvh (its
+  // shared-prefix chunks come first, then its suffix items)
+  std::vector<int32_t> member_part0;
+  if (!group_tiles.empty()) member_part0.assign(tiles.size() * hkv, -1);
+  for (size_t ti = 0; ti < tiles.size(); ti++) {
+    const Tile &t = tiles[ti];
     if (persistent && !t.decode) continue;
     const int64_t chunk = t.decode ? dchunk : pchunk;
-    const int32_t nsplit = (int32_t)std::min<int64_t>(cdiv64(t.keys, chunk), INT32_MAX);
-    cut(t.keys, nsplit, ranges);
+    int32_t nsh = 0;  // shared-prefix chunks (cascade items) ahead of this tile's own ranges
+    if (t.shared > 0) {
+      nsh = (int32_t)cdiv64(t.shared, chunk);
+      cut(t.keys - t.shared, (int32_t)cdiv64(t.keys - t.shared, chunk), ranges);
+      for (auto &r : ranges) r.first += t.shared, r.second += t.shared;
+    } else {
+      const int32_t nsplit = (int32_t)std::min<int64_t>(cdiv64(t.keys, chunk), INT32_MAX);
+      cut(t.keys, nsplit, ranges);
+    }
     for (int32_t kvh = 0; kvh < hkv; kvh++) {
       int32_t part0 = -1;
-      if (ranges.size() > 1) {
+      const int32_t nparts = nsh + (int32_t)ranges.size();
+      if (nparts > 1) {
         int64_t &np = t.decode ? P.n_part_decode : P.n_part_prefill;
         part0 = (int32_t)np;
-        np += (int64_t)ranges.size();
-        P.merges.push_back({t.row0, t.nq, kvh, part0, (int32_t)ranges.size(),
+        np += (int64_t)nparts;
+        P.merges.push_back({t.row0, t.nq, kvh, part0, nparts,
                             t.decode ? kDecodeRows : tile_rows, t.decode ? 1 : 0, 0});
       }
+      if (nsh > 0) member_part0[ti * hkv + kvh] = part0;
       for (size_t i = 0; i < ranges.size(); i++) {
         Item it{t.seq, kvh, t.row0, t.pos0, t.nq, ranges[i].first, ranges[i].second,
-                part0 < 0 ? -1 : part0 + (int32_t)i};
+                part0 < 0 ? -1 : part0 + nsh + (int32_t)i};
         if (t.decode)
           P.decode.push_back(it);
         else
@@ -372,6 +419,27 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
       if (i < pre_by_head[k].size()) P.prefill.push_back(pre_by_head[k][i]);
   std::stable_sort(P.decode.begin(), P.decode.end(), longer);
 
+  // cascade items: per group, KV head, shared-prefix chunk and run of up to
+  // kCascadeRows / G members
+  const int32_t max_members = kCascadeRows / group;
+  for (const auto &v : group_tiles) {
+    if (v.empty()) continue;
+    const Tile &t0 = tiles[v[0]];
+    std::vector<std::pair<int32_t, int32_t>> sh;
+    cut(t0.shared, (int32_t)cdiv64(t0.shared, dchunk), sh);
+    for (int32_t kvh = 0; kvh < hkv; kvh++)
+      for (size_t c = 0; c < sh.size(); c++)
+        for (size_t m0 = 0; m0 < v.size(); m0 += max_members) {
+          const int32_t nm = (int32_t)std::min<size_t>(max_members, v.size() - m0);
+          P.cascade.push_back({t0.seq, kvh, sh[c].first, sh[c].second, (int32_t)P.members.size(), nm, {0, 0}});
+          for (int32_t k = 0; k < nm; k++) {
+            const int32_t ti = v[m0 + k];
+            P.members.push_back({tiles[ti].row0, member_part0[ti * hkv + kvh] + (int32_t)c});
+          }
+          P.cascade_rows = std::max(P.cascade_rows, nm * group);
+        }
+  }
+
   // merges with many parts last (they take the one-row-per-work-group kernel)
   std::stable_partition(P.merges.begin(), P.merges.end(),
                         [](const Merge &m) { return m.nparts <= kMergeSerialParts; });
@@ -385,6 +453,10 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
   off = align256(off + P.merges.size() * sizeof(Merge));
   P.off_wg = off;
   off = align256(off + P.wg_first.size() * sizeof(int32_t));
+  P.off_cascade = off;
+  off = align256(off + P.cascade.size() * sizeof(CascadeItem));
+  P.off_members = off;
+  off = align256(off + P.members.size() * sizeof(CascadeMember));
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -666,7 +738,8 @@ namespace {
 pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_tables,
                   int32_t max_blocks_per_seq, const int32_t *hist_lens, const int32_t *incr_lens,
                   int32_t num_seqs, int32_t num_q_heads, float scale, void *out, float *lse_out,
-                  void *workspace, size_t workspace_bytes, void *stream, bool no_alloc) {
+                  void *workspace, size_t workspace_bytes, void *stream, bool no_alloc,
+                  const Groups *groups = nullptr, size_t *size_query = nullptr) {
   pa_status st = check_cache(cache);
   if (st) return st;
   if (max_blocks_per_seq < 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq < 0");
@@ -676,12 +749,29 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   if (st) return st;
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PA_ERR_BAD_SHAPE, "scale must be finite and > 0 (got %g)", (double)scale);
-  if (total_q == 0) return PA_OK;
-  if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
+  if (groups) {
+    if (groups->num_groups < 0) return fail(PA_ERR_BAD_SHAPE, "num_groups %d < 0", groups->num_groups);
+    if (groups->num_groups > 0 && (!groups->group_of || !groups->group_len))
+      return fail(PA_ERR_NULL_ARG, "group_of/group_len is NULL");
+    for (int32_t g = 0; g < groups->num_groups; g++)
+      if (groups->group_len[g] < 0 || groups->group_len[g] % cache->block_size != 0)
+        return fail(PA_ERR_BAD_SHAPE, "group %d: shared length %d is not a non-negative multiple of the block size %d",
+                    g, groups->group_len[g], cache->block_size);
+    for (int32_t s = 0; s < num_seqs && groups->num_groups > 0; s++)
+      if (groups->group_of[s] < -1 || groups->group_of[s] >= groups->num_groups)
+        return fail(PA_ERR_BAD_SHAPE, "sequence %d: group %d out of range", s, groups->group_of[s]);
+  }
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
-  make_plan(hist_lens, incr_lens, num_seqs, cache, group, P);
+  if (size_query) {
+    make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups);
+    *size_query = std::max<size_t>(P.total, 256);
+    return PA_OK;
+  }
+  if (total_q == 0) return PA_OK;
+  if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
+  make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups);
   if (no_alloc) {
     if (P.total > (size_t)PA_NOALLOC_SCRATCH_BYTES)
       return fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -706,6 +796,10 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   if (!P.merges.empty()) memcpy(host.data() + P.off_merges, P.merges.data(), P.merges.size() * sizeof(Merge));
   if (!P.wg_first.empty())
     memcpy(host.data() + P.off_wg, P.wg_first.data(), P.wg_first.size() * sizeof(int32_t));
+  if (!P.cascade.empty()) {
+    memcpy(host.data() + P.off_cascade, P.cascade.data(), P.cascade.size() * sizeof(CascadeItem));
+    memcpy(host.data() + P.off_members, P.members.data(), P.members.size() * sizeof(CascadeMember));
+  }
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   if (no_alloc) {
@@ -744,6 +838,18 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     const int n = P.wg_first.empty() ? (int)P.prefill.size() : (int)P.wg_first.size() - 1;
     e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fp8, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  if (!P.cascade.empty()) {
+    AttnArgs ac = a;
+    ac.items = nullptr;
+    ac.wg_first = nullptr;
+    ac.part_o = (float *)(ws + P.off_po_dec);
+    ac.part_lse = (float *)(ws + P.off_pl_dec);
+    e = timed(4, s, [&] {
+      return launch_cascade(ac, (const CascadeItem *)(ws + P.off_cascade), (const CascadeMember *)(ws + P.off_members),
+                            (int)P.cascade.size(), P.cascade_rows, bs, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "cascade attention launch");
   }
   if (!P.decode.empty()) {
     a.items = (const Item *)(ws + P.off_decode);
@@ -791,6 +897,23 @@ pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
                              void *stream) {
   return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs,
                  num_q_heads, scale, out, lse_out, workspace, workspace_bytes, stream, false);
+}
+
+pa_status paged_attn_forward_cascade(const void *q, const pa_kv_cache *cache,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *hist_lens, const int32_t *incr_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, float scale, void *out,
+                                     float *lse_out, const int32_t *group_of, const int32_t *group_len,
+                                     int32_t num_groups, void *workspace, size_t *workspace_bytes,
+                                     void *stream) {
+  if (!workspace_bytes) return fail(PA_ERR_NULL_ARG, "workspace_bytes is NULL");
+  Groups g;
+  g.group_of = group_of;
+  g.group_len = group_len;
+  g.num_groups = num_groups;
+  return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs,
+                 num_q_heads, scale, out, lse_out, workspace, *workspace_bytes, stream, false, &g,
+                 workspace ? nullptr : workspace_bytes);
 }
 
 pa_status paged_attn_forward_noalloc(const void *q, const pa_kv_cache *cache,

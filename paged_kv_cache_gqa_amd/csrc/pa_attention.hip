@@ -780,16 +780,19 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
       }
       all_live = __builtin_amdgcn_readfirstlane(__all(live));
     };
-    float mx = -INFINITY;
+    // the lane's maximum as a shallow tree (a serial chain of max3 would put
+    // a dozen dependent instructions on the phase's critical path)
+    float kmx[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      float k = -INFINITY;
+      float r4[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; rb++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) k = fmaxf(k, S[kb][rb][r]);
-      mx = fmaxf(mx, SPLIT ? k - lsv[kb] : k);
+        r4[rb] = fmaxf(fmaxf(S[kb][rb][0], S[kb][rb][1]), fmaxf(S[kb][rb][2], S[kb][rb][3]));
+      kmx[kb] = fmaxf(fmaxf(r4[0], r4[1]), r4[2]);
+      if constexpr (SPLIT) kmx[kb] -= lsv[kb];
     }
+    const float mx = fmaxf(kmx[0], kmx[1]);
     if (__any(mx > (FP8 && !SPLIT ? thr : kRescaleSlack)) || !all_live) rescale();
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
@@ -1388,6 +1391,197 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
 }
 
 // =============================================================================
+// Shared-prefix cascade for bf16 KV, head_dim 128: the decode rows of the
+// members of a prefix group (up to 64 rows: NRB blocks of 16, G rows per
+// member) against one key range of their shared prefix.  The keys stream
+// exactly as in decode_dma_kernel (per-wave LDS rings of 16-key slices,
+// non-temporal LDS-filling loads), but each slice now feeds NRB score and
+// value products instead of one: the prefix is read once for all members, and
+// the work per byte grows NRB-fold.  No causal mask is needed (the shared
+// prefix lies before every member's own token); keys past the range end are
+// masked.  The four waves' states are combined per row block through LDS and
+// each member's rows go to its partial slot (row g of the slot = its head g).
+template <int BS, int NRB>
+__global__ __launch_bounds__(256, 1) void cascade_kernel(AttnArgs a, const CascadeItem *items,
+                                                         const CascadeMember *members) {
+  constexpr int D = 128;
+  constexpr int NCK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int NW = 4;
+  constexpr int NST = kDecStages;
+  constexpr int SB = kDecSliceBytes;
+  static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  lds_u8 *smem = (lds_u8 *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const CascadeItem it = items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q4 = lane >> 4;
+  const int hkv = a.c.hkv;
+  const int kv_lo = it.kv_lo, kv_hi = it.kv_hi;
+
+  bf16x8 qf[NRB][NCK];
+#pragma unroll
+  for (int rb = 0; rb < NRB; rb++) {
+    const int r = rb * 16 + n;
+    const int mi = r >> a.lg, g = r & (a.group - 1);
+    const bool active = mi < it.nmem;
+    const int row0 = active ? members[it.mem0 + mi].row0 : 0;
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)row0 * a.hq + it.kvh * a.group + g) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < NCK; c++) {
+      uint4 v = active ? gload16(qrow + (32 * c + 8 * q4) * 2) : make_uint4(0, 0, 0, 0);
+      qf[rb][c] = as_bf16x8(v);
+    }
+  }
+  float m[NRB], l[NRB];
+  f32x4 o[NRB][ND];
+#pragma unroll
+  for (int rb = 0; rb < NRB; rb++) {
+    m[rb] = kNegBig;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < ND; i++) o[rb][i] = f32x4{};
+  }
+
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+  const int n_slices = (kv_hi - kv_lo + kDecSlice - 1) / kDecSlice;
+  const int nw = n_slices > wave ? (n_slices - wave + NW - 1) / NW : 0;
+  const int blk0 = kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+  {
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 64 * NW) bt_lds[i] = btr[i];
+  }
+  PA_WAIT_VMCNT(0);
+  __syncthreads();
+
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    voff[q] = (lane >> 4) * 256 + (((lane & 15) ^ swz(4 * q + (lane >> 4))) << 4);
+  const uint32_t ring = smem_addr + wave * NST * 2 * SB;
+  lds_u8 *ring_p = smem + wave * NST * 2 * SB;
+  auto slice_key = [&](int k) { return kv_lo + kDecSlice * (wave + NW * k); };
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int key0 = slice_key(min(k, max(nw - 1, 0)));
+    const int64_t blk = __builtin_amdgcn_readfirstlane(bt_lds[min(key0 / BS, last_blk) - blk0]);
+    const int64_t base = ((blk * hkv + it.kvh) * BS + key0 % BS) * (D * 2);
+    const uint64_t ka = (uint64_t)(kc + base), va = (uint64_t)(vc + base);
+    const uint32_t st = ring + (k % NST) * 2 * SB;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int nrec = __builtin_amdgcn_readfirstlane(k < nw ? min(max(kv_hi - (key0 + 4 * q), 0), 4) * (D * 2) : 0);
+      const uint64_t kq = ka + q * 4 * D * 2, vq = va + q * 4 * D * 2;
+      const i32x4_t rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kq),
+                          __builtin_amdgcn_readfirstlane((int)((kq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      const i32x4_t rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vq),
+                          __builtin_amdgcn_readfirstlane((int)((vq >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+      dma_load16_nt(rk, voff[q], st + q * 1024);
+      dma_load16_nt(rv, voff[q], st + SB + q * 1024);
+    }
+  };
+  const int vr = 4 * q4 + (n >> 2);
+  const int vbase = vr * 256 + ((((n & 3) >> 1) ^ swz(vr)) << 4) + (n & 1) * 8;
+  auto compute = [&](int k) __attribute__((always_inline)) {
+    const lds_u8 *Ks = ring_p + (k % NST) * 2 * SB;
+    const lds_u8 *Vs = Ks + SB;
+    const int key0 = slice_key(k);
+    uint4 kraw[NCK];
+    bf16x4 vraw[ND];
+#pragma unroll
+    for (int c = 0; c < NCK; c++) kraw[c] = lds_load16(Ks + n * 256 + (((4 * c + q4) ^ swz(n)) << 4));
+#pragma unroll
+    for (int db = 0; db < ND; db++) vraw[db] = lds_read_tr(Vs + (vbase ^ (db << 5)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's bytes are in registers
+    __builtin_amdgcn_sched_barrier(0);
+    issue(k + NST);
+    const bool tail = key0 + kDecSlice > kv_hi;
+#pragma unroll
+    for (int rb = 0; rb < NRB; rb++) {
+      f32x4 s;
+#pragma unroll
+      for (int c = 0; c < NCK; c++) s = mfma16x16x32(as_bf16x8(kraw[c]), qf[rb][c], c == 0 ? f32x4{} : s);
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] = key0 + 4 * q4 + r < kv_hi ? s[r] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = xor32_max(xor16_max(mx));
+      const float mxs = mx * a.scale_log2;
+      if (__any(mxs > m[rb] + kRescaleSlack)) {
+        const float m_new = fmaxf(m[rb], mxs);
+        const float alpha = fast_exp2(m[rb] - m_new);
+        m[rb] = m_new;
+        l[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; db++) o[rb][db] *= alpha;
+      }
+      const float nm = -m[rb];
+      bf16x4 pb;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, nm));
+        l[rb] += p;
+        pb[r] = (__bf16)p;
+      }
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[rb][db] = mfma16x16x16(vraw[db], pb, o[rb][db]);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NST; k++) issue(k);
+  for (int k = 0; k < nw; k++) {
+    PA_WAIT_VMCNT(8 * (NST - 1));
+    compute(k);
+  }
+  PA_WAIT_VMCNT(0);
+
+  // combine the four waves' states one row block at a time through LDS
+  float *red_o = (float *)smem_raw;        // [NW][16][D]
+  float *red_m = red_o + NW * 16 * D;      // [NW][16]
+  float *red_l = red_m + NW * 16;          // [NW][16]
+#pragma unroll
+  for (int rb = 0; rb < NRB; rb++) {
+    float lt = xor32_sum(xor16_sum(l[rb]));
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < ND; db++) *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[rb][db];
+    if (q4 == 0) {
+      red_m[wave * 16 + n] = m[rb];
+      red_l[wave * 16 + n] = lt;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 16 * D; idx += 64 * NW) {
+      const int cn = idx / D, e = idx % D;
+      const int r = rb * 16 + cn;
+      const int mi = r >> a.lg, g = r & (a.group - 1);
+      if (mi >= it.nmem) continue;
+      float M = red_m[cn];
+#pragma unroll
+      for (int w = 1; w < NW; w++) M = fmaxf(M, red_m[w * 16 + cn]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; w++) {
+        const float sc = fast_exp2(red_m[w * 16 + cn] - M);
+        L += sc * red_l[w * 16 + cn];
+        O += sc * red_o[(w * 16 + cn) * D + e];
+      }
+      const int slot = members[it.mem0 + mi].part;
+      a.part_o[((int64_t)slot * kDecodeRows + g) * D + e] = L > 0.f ? O / L : 0.f;
+      if (e == 0) a.part_lse[(int64_t)slot * kDecodeRows + g] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
+// =============================================================================
 // Decode for E4M3 KV, head_dim 128, streamed through LDS like the bf16 one:
 // wave w takes the 32-key slices w, w+4, ... of the item's range; a slice of
 // K codes (and of V codes) is 4 KB, 32 rows of 128 bytes, moved into the
@@ -1819,6 +2013,24 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, bool fp8, hipS
   if (n <= 0) return hipSuccess;
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
+hipError_t launch_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members, int n_items,
+                          int rows, int bs, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  if (rows <= 0 || rows > kCascadeRows || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
+#define PA_CASCADE(B, R) hipLaunchKernelGGL((cascade_kernel<B, R>), dim3(n_items), dim3(256), 0, s, a, items, members)
+  if (bs == 16) {
+    if (rows <= 16) PA_CASCADE(16, 1);
+    else if (rows <= 32) PA_CASCADE(16, 2);
+    else PA_CASCADE(16, 4);
+  } else {
+    if (rows <= 16) PA_CASCADE(64, 1);
+    else if (rows <= 32) PA_CASCADE(64, 2);
+    else PA_CASCADE(64, 4);
+  }
+#undef PA_CASCADE
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s) {
   if (n_few > 0) hipLaunchKernelGGL(merge_kernel, dim3(n_few, kPrefillRowsMax / kMergeRows), dim3(256), 0, s, a);
   if (n_many > 0) hipLaunchKernelGGL(merge_many_kernel, dim3(n_many, many_rows), dim3(256), 0, s, a, n_few);

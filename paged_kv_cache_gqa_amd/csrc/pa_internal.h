@@ -37,6 +37,28 @@ struct Merge {
 };
 static_assert(sizeof(Merge) == 32, "Merge layout");
 
+// Shared-prefix cascade ([Agentic] §2.1: sub-agents start from the main
+// agent's context; §4.1: prefix reuse): the decode rows of up to
+// kCascadeRows / G sequences whose first keys lie in the same physical
+// blocks, against one key range of that shared prefix, as one tile.  Each
+// member writes its rows' partial result to its own slot, merged by LSE with
+// the partials of its own suffix.
+struct CascadeItem {
+  int32_t seq;    // a member: its block-table row names the shared blocks
+  int32_t kvh;
+  int32_t kv_lo;  // key range within the shared prefix
+  int32_t kv_hi;
+  int32_t mem0;   // this item's first entry in the member table
+  int32_t nmem;   // members; member i's G rows are tile rows i*G .. i*G+G-1
+  int32_t pad[2];
+};
+static_assert(sizeof(CascadeItem) == 32, "CascadeItem layout");
+struct CascadeMember {
+  int32_t row0;   // q row of the member's (single) new token
+  int32_t part;   // decode partial slot for this item's key range
+};
+constexpr int kCascadeRows = 64;  // query rows per cascade tile (4 row blocks of 16)
+
 struct CacheArgs {
   const void *k;
   const void *v;
@@ -118,6 +140,9 @@ constexpr int kKeyTile = 64;       // keys per inner-loop tile
 // Launchers (defined next to their kernels).
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
+// rows: the largest member count times G among the items (at most kCascadeRows)
+hipError_t launch_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members, int n_items,
+                          int rows, int bs, hipStream_t s);
 // merges [0, n_few) have at most kMergeSerialParts parts, [n_few, n_few +
 // n_many) more, with at most many_rows rows each
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
