@@ -131,7 +131,7 @@ class Runner:
             if n % 8 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        for k in range(5):
+        for k in range(pa.TIMING_KINDS):
             pa.pa_timing_read(k)  # drop anything recorded before
         pa.pa_timing_enable(True)
         for _ in range(steps):
@@ -147,7 +147,7 @@ class Runner:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         kern = {}
-        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "cascade")):
+        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge")):
             tot, cnt = pa.pa_timing_read(kind)
             if cnt:
                 kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step
@@ -206,7 +206,7 @@ def report_decode_steps(pa, torch, r, dev, label, nsteps=256, warmup=16):
     for j in range(warmup):
         step(j)
     torch.cuda.synchronize()
-    for k in range(5):
+    for k in range(pa.TIMING_KINDS):
         pa.pa_timing_read(k)
     pa.pa_timing_enable(True)
     for j in range(nsteps):
@@ -284,8 +284,9 @@ def mixed_parts(spec):
 def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False):
     """One call holding 4 incremental prefills and 48 decodes: the prefill
     part in TFLOP/s over its kernel, the decode part in GB/s over its kernels
-    (decode, plus the shared-prefix cascade when the sub-agents are declared as
-    a group; the shared prefix's blocks counted once either way)."""
+    (the decode launch holds the shared-prefix cascade items when the
+    sub-agents are declared as a group; the shared prefix's blocks are counted
+    once either way)."""
     r = Runner(pa, torch, spec, dev)
     if cascade:
         r.use_cascade()
@@ -293,8 +294,6 @@ def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False):
     fl, _, byts = mixed_parts(spec)
     p_ms = kern["prefill"][0] * kern["prefill"][1]
     d_ms = kern["decode"][0] * kern["decode"][1]
-    if "cascade" in kern:
-        d_ms += kern["cascade"][0] * kern["cascade"][1]
     d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
          "prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
          "prefill_frac": round(fl / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),

@@ -231,8 +231,9 @@ PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_
 /* Per-kernel timing for measurement.  When enabled (nonzero), each launch
  * records HIP events on the call's stream around the kernel; the durations
  * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
- * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention,
- * 3 = LSE merge, 4 = shared-prefix cascade, the summed
+ * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention
+ * (holding the shared-prefix cascade items of paged_attn_forward_cascade,
+ * which run in the same launch), 3 = LSE merge, the summed
  * milliseconds and launch count since the last reset (it synchronises on the
  * recorded events), then resets that kind. */
 PA_API pa_status pa_timing_enable(int enable);

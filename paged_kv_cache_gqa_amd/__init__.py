@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK, PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = 4, 5
 PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
-TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE, TIMING_CASCADE = 0, 1, 2, 3, 4
+TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
+TIMING_KINDS = 4
 
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",

@@ -600,7 +600,7 @@ pa_status scratch_address(unsigned char **out) {
 
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
-constexpr int kKinds = 5;
+constexpr int kKinds = 4;
 std::mutex g_time_mu;
 bool g_timing = false;
 struct TimedLaunch {
@@ -839,19 +839,18 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fp8, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
-  if (!P.cascade.empty()) {
-    AttnArgs ac = a;
-    ac.items = nullptr;
-    ac.wg_first = nullptr;
-    ac.part_o = (float *)(ws + P.off_po_dec);
-    ac.part_lse = (float *)(ws + P.off_pl_dec);
-    e = timed(4, s, [&] {
-      return launch_cascade(ac, (const CascadeItem *)(ws + P.off_cascade), (const CascadeMember *)(ws + P.off_members),
-                            (int)P.cascade.size(), P.cascade_rows, bs, s);
+  if (!P.cascade.empty()) {  // one launch: the cascade items, then the decode items
+    a.items = (const Item *)(ws + P.off_decode);
+    a.wg_first = nullptr;
+    a.part_o = (float *)(ws + P.off_po_dec);
+    a.part_lse = (float *)(ws + P.off_pl_dec);
+    e = timed(2, s, [&] {
+      return launch_decode_cascade(a, (const CascadeItem *)(ws + P.off_cascade),
+                                   (const CascadeMember *)(ws + P.off_members), (int)P.cascade.size(),
+                                   (int)P.decode.size(), P.cascade_rows, bs, s);
     });
-    if (e != hipSuccess) return hip_fail(e, "cascade attention launch");
-  }
-  if (!P.decode.empty()) {
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  } else if (!P.decode.empty()) {
     a.items = (const Item *)(ws + P.off_decode);
     a.wg_first = nullptr;
     a.part_o = (float *)(ws + P.off_po_dec);

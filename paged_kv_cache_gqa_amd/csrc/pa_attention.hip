@@ -1242,18 +1242,16 @@ constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4
 constexpr int kDecStages = PA_DEC_STAGES;
 
 template <int BS, int NW, int NST>
-__global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
+__device__ __forceinline__ void decode_dma_item(const AttnArgs &a, const Item it, unsigned char *smem_raw,
+                                                int *bt_lds) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;  // score MFMAs per slice
   constexpr int ND = D / 16;   // 16-wide d blocks of the output
   constexpr int SB = kDecSliceBytes;
   static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  const Item it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1390,6 +1388,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
   decode_combine<D, NW>(a, it, smem_raw, m, l, o);
 }
 
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  decode_dma_item<BS, NW, NST>(a, a.items[blockIdx.x], smem_raw, bt_lds);
+}
+
 // =============================================================================
 // Shared-prefix cascade for bf16 KV, head_dim 128: the decode rows of the
 // members of a prefix group (up to 64 rows: NRB blocks of 16, G rows per
@@ -1402,8 +1407,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
 // masked.  The four waves' states are combined per row block through LDS and
 // each member's rows go to its partial slot (row g of the slot = its head g).
 template <int BS, int NRB>
-__global__ __launch_bounds__(256, 1) void cascade_kernel(AttnArgs a, const CascadeItem *items,
-                                                         const CascadeMember *members) {
+__device__ __forceinline__ void cascade_item(const AttnArgs &a, const CascadeItem it, const CascadeMember *members,
+                                             unsigned char *smem_raw, int *bt_lds) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;
   constexpr int ND = D / 16;
@@ -1411,12 +1416,9 @@ __global__ __launch_bounds__(256, 1) void cascade_kernel(AttnArgs a, const Casca
   constexpr int NST = kDecStages;
   constexpr int SB = kDecSliceBytes;
   static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  const CascadeItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1579,6 +1581,20 @@ __global__ __launch_bounds__(256, 1) void cascade_kernel(AttnArgs a, const Casca
       if (e == 0) a.part_lse[(int64_t)slot * kDecodeRows + g] = L > 0.f ? M + __log2f(L) : -INFINITY;
     }
   }
+}
+
+// The decode launch of a step with shared-prefix groups: work-groups
+// [0, n_cascade) run the cascade items (first: each carries several members'
+// rows), the rest the ordinary decode items, in one grid.
+template <int BS, int NRB>
+__global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, const CascadeItem *citems,
+                                                                const CascadeMember *members, int n_cascade) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kDecStages * 2 * kDecSliceBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  if ((int)blockIdx.x < n_cascade)
+    cascade_item<BS, NRB>(a, citems[blockIdx.x], members, smem_raw, bt_lds);
+  else
+    decode_dma_item<BS, 4, kDecStages>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
 }
 
 // =============================================================================
@@ -2013,11 +2029,14 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, bool fp8, hipS
   if (n <= 0) return hipSuccess;
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
-hipError_t launch_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members, int n_items,
-                          int rows, int bs, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
+hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,
+                                 int n_cascade, int n_decode, int rows, int bs, hipStream_t s) {
+  if (n_cascade + n_decode <= 0) return hipSuccess;
   if (rows <= 0 || rows > kCascadeRows || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
-#define PA_CASCADE(B, R) hipLaunchKernelGGL((cascade_kernel<B, R>), dim3(n_items), dim3(256), 0, s, a, items, members)
+  static_assert(PA_DEC_WAVES == 4, "the fused decode launch runs 4-wave work-groups");
+  const dim3 grid(n_cascade + n_decode);
+#define PA_CASCADE(B, R) \
+  hipLaunchKernelGGL((decode_cascade_kernel<B, R>), grid, dim3(256), 0, s, a, items, members, n_cascade)
   if (bs == 16) {
     if (rows <= 16) PA_CASCADE(16, 1);
     else if (rows <= 32) PA_CASCADE(16, 2);

@@ -140,9 +140,10 @@ constexpr int kKeyTile = 64;       // keys per inner-loop tile
 // Launchers (defined next to their kernels).
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
-// rows: the largest member count times G among the items (at most kCascadeRows)
-hipError_t launch_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members, int n_items,
-                          int rows, int bs, hipStream_t s);
+// bf16 head_dim 128 decode launch with shared-prefix cascade items first
+// (rows: the largest member count times G among them, at most kCascadeRows)
+hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,
+                                 int n_cascade, int n_decode, int rows, int bs, hipStream_t s);
 // merges [0, n_few) have at most kMergeSerialParts parts, [n_few, n_few +
 // n_many) more, with at most many_rows rows each
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
