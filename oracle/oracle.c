@@ -35,6 +35,16 @@
  *     separate for K and V, value = decode(code) * scale.  Encoding rounds
  *     x / scale (fp32 division, correctly rounded) to nearest-even and
  *     saturates to +-448.
+ *   - 4-bit KV ([V41] kernels section: an FP4 KV cache, about half the bytes
+ *     of FP8) is OCP MXFP4: E2M1 elements (1 sign, 2 exponent bits with bias
+ *     1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one
+ *     E8M0 scale (2^(byte - 127), byte 255 = NaN) per 32 consecutive head_dim
+ *     elements of one token and KV head.  Encoding a group: its shared
+ *     exponent is floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+ *     clamped to [-127, 127] (amax = 0 gives -127); each element x / 2^that
+ *     rounds to the nearest E2M1 value, ties to the even mantissa, and
+ *     saturates to +-6; the sign bit is x's.  A group holding a NaN or an
+ *     infinity gets the NaN scale and zero codes.
  *
  * Parity pins for every function here live in tests/test_oracle_*.py.
  */
@@ -114,6 +124,77 @@ uint8_t orc_e4m3_from_float(float x) {
   return (uint8_t)(sign | code);
 }
 
+/* OCP MX E2M1 (the low 4 bits of `code`): exponent field 0 holds the
+ * subnormal m * 0.5; otherwise (1 + m / 2) * 2^(e - 1). */
+double orc_e2m1_to_double(uint8_t code) {
+  int sign = (code >> 3) & 1;
+  int e = (code >> 1) & 3;
+  int m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -v : v;
+}
+
+/* OCP MX E8M0 scale: 2^(byte - 127); 0xFF is NaN. */
+double orc_e8m0_to_double(uint8_t byte) {
+  if (byte == 0xFF) return NAN;
+  return ldexp(1.0, (int)byte - 127);
+}
+
+/* E2M1 code of a value already divided by its group's scale: the nearest of
+ * the eight magnitudes, ties to the even mantissa, magnitudes >= 6 saturate
+ * to 6.  The rounding is nearbyint() (round-to-nearest-even) on the value
+ * expressed in units of its binade's step: 0.5 below 2, 1 in [2, 4), 2 from
+ * 4 on -- an even multiple of the step is a zero mantissa bit. */
+uint8_t orc_e2m1_from_double(double v) {
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  double a = fabs(v);
+  double r;
+  if (a >= 6.0)
+    r = 6.0;
+  else if (a < 2.0)
+    r = 0.5 * nearbyint(a * 2.0);
+  else if (a < 4.0)
+    r = nearbyint(a);
+  else
+    r = 2.0 * nearbyint(a * 0.5);
+  for (uint8_t c = 0; c < 8; c++)
+    if (orc_e2m1_to_double(c) == r) return (uint8_t)(sign | c);
+  return sign; /* not reached: r is one of the magnitudes */
+}
+
+/* Shared-exponent byte of a group with largest magnitude amax (finite):
+ * floor(log2(amax)) - 2 + 127, clamped to [0, 254]; amax = 0 gives 0. */
+uint8_t orc_mxfp4_scale_byte(double amax) {
+  if (amax == 0.0) return 0;
+  int k;
+  (void)frexp(amax, &k); /* amax = f * 2^k, f in [0.5, 1): floor(log2 amax) = k - 1 */
+  int e = (k - 1) - 2 + 127;
+  if (e < 0) e = 0;
+  if (e > 254) e = 254;
+  return (uint8_t)e;
+}
+
+/* Encode one group of n bf16 values (n = 32) into n E2M1 codes (one per
+ * byte, low 4 bits) and its scale byte, by the rule in the header above. */
+void orc_mxfp4_encode_group(const uint16_t *x, int32_t n, uint8_t *codes, uint8_t *scale) {
+  double amax = 0.0;
+  int finite = 1;
+  for (int32_t i = 0; i < n; i++) {
+    double v = orc_bf16_to_double(x[i]);
+    if (!isfinite(v)) finite = 0;
+    else if (fabs(v) > amax) amax = fabs(v);
+  }
+  if (!finite) {
+    *scale = 0xFF;
+    for (int32_t i = 0; i < n; i++) codes[i] = 0;
+    return;
+  }
+  uint8_t sb = orc_mxfp4_scale_byte(amax);
+  double X = orc_e8m0_to_double(sb);
+  *scale = sb;
+  for (int32_t i = 0; i < n; i++) codes[i] = orc_e2m1_from_double(orc_bf16_to_double(x[i]) / X);
+}
+
 /* Correctly rounded binary32 quotient: the binary64 quotient of two binary32
  * values rounded once more to binary32 equals the correctly rounded binary32
  * quotient, because 53 >= 2*24 + 2. */
@@ -124,7 +205,7 @@ float orc_div_f32(float x, float s) { return (float)((double)x / (double)s); }
 
 typedef struct {
   const void *k, *v;
-  const float *ks, *vs;
+  const void *ks, *vs;
   int32_t num_blocks, hkv, bs, d, dtype;
 } cache_view;
 
@@ -138,11 +219,32 @@ static void e4m3_table_init(void) {
   e4m3_value_ready = 1;
 }
 
-static double cache_elem(const cache_view *c, const void *base, const float *scale,
+/* Element dd of token slot (phys, off), KV head kvh.  MXFP4: codes
+ * [nb][hkv][bs][d/2] with element 2i in the low and 2i+1 in the high 4 bits
+ * of byte i; scale bytes [nb][hkv][d/32][bs]. */
+static double cache_elem(const cache_view *c, const void *base, const void *scale,
                          int64_t phys, int32_t kvh, int32_t off, int32_t dd) {
-  int64_t idx = ((phys * c->hkv + kvh) * (int64_t)c->bs + off) * (int64_t)c->d + dd;
-  if (c->dtype == ORC_KV_BF16) return orc_bf16_to_double(((const uint16_t *)base)[idx]);
-  return e4m3_value[((const uint8_t *)base)[idx]] * (double)scale[phys * c->hkv + kvh];
+  int64_t row = (phys * c->hkv + kvh) * (int64_t)c->bs + off;
+  if (c->dtype == ORC_KV_BF16) return orc_bf16_to_double(((const uint16_t *)base)[row * c->d + dd]);
+  if (c->dtype == ORC_KV_E4M3)
+    return e4m3_value[((const uint8_t *)base)[row * c->d + dd]] * (double)((const float *)scale)[phys * c->hkv + kvh];
+  uint8_t byte = ((const uint8_t *)base)[row * (c->d / 2) + dd / 2];
+  uint8_t code = (dd & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+  uint8_t sb = ((const uint8_t *)scale)[((phys * c->hkv + kvh) * (c->d / 32) + dd / 32) * (int64_t)c->bs + off];
+  return orc_e2m1_to_double(code) * orc_e8m0_to_double(sb);
+}
+
+/* Encode one token's head vector x[d] into MXFP4 codes and scales at slot
+ * (blk, off), head h, of a cache with the layout above. */
+static void mxfp4_store(uint8_t *codes, uint8_t *scales, int64_t blk, int32_t h, int64_t off, int32_t hkv,
+                        int32_t bs, int32_t d, const uint16_t *x) {
+  uint8_t c[32], sb;
+  uint8_t *row = codes + ((blk * hkv + h) * (int64_t)bs + off) * (d / 2);
+  for (int32_t grp = 0; grp < d / 32; grp++) {
+    orc_mxfp4_encode_group(x + 32 * grp, 32, c, &sb);
+    for (int32_t i = 0; i < 16; i++) row[16 * grp + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+    scales[((blk * hkv + h) * (d / 32) + grp) * (int64_t)bs + off] = sb;
+  }
 }
 
 /* ------------------------------------------------------------------ */
@@ -150,7 +252,7 @@ static double cache_elem(const cache_view *c, const void *base, const float *sca
  * scheduler assigned ([AMPD] §7: the increment's KV is concatenated onto the
  * locally held history; [Agentic] §5.2: the KV write precedes attention).
  * slot = physical_block * block_size + offset; slot < 0 means "skip". */
-int orc_kv_append(void *k_cache, void *v_cache, const float *k_scale, const float *v_scale,
+int orc_kv_append(void *k_cache, void *v_cache, void *k_scale, void *v_scale,
                   int32_t num_blocks, int32_t hkv, int32_t bs, int32_t d, int32_t dtype,
                   const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_mapping,
                   int64_t num_tokens) {
@@ -160,6 +262,11 @@ int orc_kv_append(void *k_cache, void *v_cache, const float *k_scale, const floa
     int64_t blk = slot / bs, off = slot % bs;
     if (blk >= num_blocks) return ORC_ERR_RANGE;
     for (int32_t h = 0; h < hkv; h++) {
+      if (dtype == ORC_KV_MXFP4) {
+        mxfp4_store((uint8_t *)k_cache, (uint8_t *)k_scale, blk, h, off, hkv, bs, d, k_new + (t * hkv + h) * (int64_t)d);
+        mxfp4_store((uint8_t *)v_cache, (uint8_t *)v_scale, blk, h, off, hkv, bs, d, v_new + (t * hkv + h) * (int64_t)d);
+        continue;
+      }
       for (int32_t e = 0; e < d; e++) {
         int64_t src = (t * hkv + h) * (int64_t)d + e;
         int64_t dst = ((blk * hkv + h) * (int64_t)bs + off) * (int64_t)d + e;
@@ -169,8 +276,8 @@ int orc_kv_append(void *k_cache, void *v_cache, const float *k_scale, const floa
         } else {
           float kx = (float)orc_bf16_to_double(k_new[src]);
           float vx = (float)orc_bf16_to_double(v_new[src]);
-          ((uint8_t *)k_cache)[dst] = orc_e4m3_from_float(orc_div_f32(kx, k_scale[blk * hkv + h]));
-          ((uint8_t *)v_cache)[dst] = orc_e4m3_from_float(orc_div_f32(vx, v_scale[blk * hkv + h]));
+          ((uint8_t *)k_cache)[dst] = orc_e4m3_from_float(orc_div_f32(kx, ((const float *)k_scale)[blk * hkv + h]));
+          ((uint8_t *)v_cache)[dst] = orc_e4m3_from_float(orc_div_f32(vx, ((const float *)v_scale)[blk * hkv + h]));
         }
       }
     }
@@ -191,6 +298,33 @@ void orc_e4m3_quantize_pool(const uint16_t *src, const float *scale, uint8_t *ds
       dst[bh * per + e] = orc_e4m3_from_float(orc_div_f32(x, s));
     }
   }
+}
+
+/* MXFP4-encode a whole pool of bf16 values ([nb][hkv][bs][d]): the same
+ * per-token rule as orc_kv_append, into codes [nb][hkv][bs][d/2] and scales
+ * [nb][hkv][d/32][bs]. */
+void orc_mxfp4_quantize_pool(const uint16_t *src, uint8_t *codes, uint8_t *scales, int64_t nb, int32_t hkv,
+                             int32_t bs, int32_t d) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < nb * hkv; bh++)
+    for (int32_t off = 0; off < bs; off++)
+      mxfp4_store(codes, scales, bh / hkv, (int32_t)(bh % hkv), off, hkv, bs, d, src + (bh * bs + off) * (int64_t)d);
+}
+
+/* Values of one sequence's cache through its block-table row, in fp64:
+ * out[p][kvh][e] = element e of K (or V) at position p (the same element
+ * rule attention uses). */
+int orc_gather_values(const void *cache, const void *scale, int32_t dtype, int32_t num_blocks, int32_t hkv,
+                      int32_t bs, int32_t d, const int32_t *bt_row, int64_t ctx, double *out) {
+  e4m3_table_init();
+  cache_view c = {cache, cache, scale, scale, num_blocks, hkv, bs, d, dtype};
+  for (int64_t p = 0; p < ctx; p++) {
+    int32_t phys = bt_row[p / bs];
+    if (phys < 0 || phys >= num_blocks) return ORC_ERR_RANGE;
+    for (int32_t h = 0; h < hkv; h++)
+      for (int32_t e = 0; e < d; e++) out[(p * hkv + h) * (int64_t)d + e] = cache_elem(&c, cache, scale, phys, h, (int32_t)(p % bs), e);
+  }
+  return ORC_OK;
 }
 
 /* Raw gather of one sequence's cache through its block-table row:
@@ -280,7 +414,7 @@ static int check_seq(const cache_view *c, const int32_t *bt_row, int32_t max_blo
  * out:  double [nrows][hq][d];  lse: double [nrows][hq] (may be NULL).
  */
 int orc_attention(const uint16_t *q, const void *k_cache, const void *v_cache,
-                  const float *k_scale, const float *v_scale, int32_t dtype,
+                  const void *k_scale, const void *v_scale, int32_t dtype,
                   int32_t num_blocks, int32_t hkv, int32_t bs, int32_t d,
                   const int32_t *block_tables, int32_t max_blocks,
                   const int32_t *hist, const int32_t *incr, int32_t num_seqs, int32_t hq,
@@ -342,7 +476,7 @@ int orc_attention(const uint16_t *q, const void *k_cache, const void *v_cache,
  * split computation produces.  [Agentic] §4.3.3 merges such partial outputs
  * O_i with their LSE "the online-softmax way". */
 int orc_attention_partial(const uint16_t *qrow, const void *k_cache, const void *v_cache,
-                          const float *k_scale, const float *v_scale, int32_t dtype,
+                          const void *k_scale, const void *v_scale, int32_t dtype,
                           int32_t num_blocks, int32_t hkv, int32_t bs, int32_t d,
                           const int32_t *bt_row, int32_t kvh, int64_t pos, int64_t k_lo,
                           int64_t k_hi, float scale, double *o, double *lse, double *probs) {
