@@ -18,7 +18,8 @@
  * inclusive boundary (a query at absolute position p sees keys 0..p), query
  * head h reads KV head h / (num_q_heads / num_kv_heads), cache layout
  * [num_blocks][num_kv_heads][block_size][head_dim], OCP E4M3 ("e4m3fn") for
- * 8-bit KV with one fp32 scale per (physical block, KV head).
+ * 8-bit KV with one fp32 scale per (physical block, KV head), OCP MXFP4 for
+ * 4-bit KV (E2M1 codes, one E8M0 scale per 32 elements of a token and head).
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless marked HOST.  All tensors are dense
@@ -38,7 +39,8 @@
  *
  * Supported domain: head_dim in {64, 128}; block_size in {16, 64};
  * num_q_heads % num_kv_heads == 0 with group size in {1, 2, 4, 8, 16};
- * q and out bf16; KV bf16 or E4M3.  Element offsets are 64-bit throughout.
+ * q and out bf16; KV bf16, E4M3 or MXFP4 (MXFP4: head_dim 128 only).
+ * Element offsets are 64-bit throughout.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -65,7 +67,7 @@ typedef enum {
   PA_ERR_HIP = 5
 } pa_status;
 
-typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1, PA_KV_MXFP4 = 2 } pa_kv_dtype;
 
 /* The paged KV cache: a pool of physical blocks, each holding block_size
  * consecutive token positions of one sequence for every KV head
@@ -73,18 +75,27 @@ typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
  * needs cdiv(tokens, block_size) blocks; "Scheduler.schedule — 记账与状态":
  * each request holds a list of block ids; blocks may be shared).
  *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim],
- *                     bf16 (2 bytes) or E4M3 codes (1 byte) per element.
- *   k_scale, v_scale  fp32 [num_blocks][num_kv_heads]; stored value =
+ *                     bf16 (2 bytes) or E4M3 codes (1 byte) per element;
+ *                     MXFP4: [num_blocks][num_kv_heads][block_size][head_dim/2]
+ *                     bytes, element 2i in the low and 2i+1 in the high 4 bits
+ *                     of byte i (OCP MX E2M1 codes).
+ *   k_scale, v_scale  E4M3: fp32 [num_blocks][num_kv_heads]; stored value =
  *                     decode(code) * scale; every scale a block in use has is
- *                     a positive, finite, normal fp32 number.  NULL iff
- *                     dtype == PA_KV_BF16.
- * ([V41] "SWA 有界重放" and the kernels section keep KV in FP8 to cut its
- * footprint.) */
+ *                     a positive, finite, normal fp32 number.
+ *                     MXFP4: uint8 E8M0 [num_blocks][num_kv_heads][head_dim/32]
+ *                     [block_size], the scale 2^(byte - 127) (255 = NaN) of 32
+ *                     consecutive elements of one token and head; stored
+ *                     value = E2M1(code) * scale.  kv_append writes them.
+ *                     NULL iff dtype == PA_KV_BF16.
+ * ([V41] "SWA 有界重放" and the kernels section keep KV in FP8, and in FP4
+ * for the long-lived part, to cut its footprint; MXFP4 is OCP's 4-bit format
+ * with power-of-two scales, which gfx950 widens to bf16 exactly in one
+ * instruction per two elements.  MXFP4 needs head_dim 128.) */
 typedef struct {
   void *k_cache;
   void *v_cache;
-  float *k_scale;
-  float *v_scale;
+  void *k_scale;
+  void *v_scale;
   int32_t num_blocks;
   int32_t num_kv_heads;
   int32_t block_size;
@@ -106,8 +117,15 @@ typedef struct {
  *   bf16:  cache[slot / bs][h][slot % bs][:] = new[t][h][:]   (bit copy)
  *   E4M3:  cache[...][e] = E4M3(new[t][h][e] / scale[slot / bs][h]) where the
  *          division is the correctly rounded fp32 quotient and E4M3() rounds
- *          to nearest-even, saturating to +-448 (NaN -> NaN).
- * Only the named slots are written; scales are inputs and never modified.
+ *          to nearest-even, saturating to +-448 (NaN -> NaN).  The scales are
+ *          inputs and never modified.
+ *   MXFP4: per group of 32 elements e = 32j .. 32j+31 of new[t][h]: scale
+ *          byte E = clamp(floor(log2(max |x|)) - 2 + 127, 0, 254) (0 when all
+ *          are zero), code[e] = E2M1(x[e] / 2^(E - 127)) rounded to
+ *          nearest-even and saturating to +-6, sign bit = x's sign bit; a
+ *          group holding a NaN or an infinity gets E = 255 and zero codes.
+ *          Codes and scale bytes of the slot are written.
+ * Only the named slots are written.
  * num_tokens == 0 is a no-op.
  */
 PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
@@ -148,7 +166,9 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  * With an E4M3 cache, K[j] and V[j] are code * scale of their (block, head);
  * the codes widen to bf16 exactly and the scales act in fp32 (the key scale
  * on the score, the value scale on the probability before it is rounded to
- * bf16 for the value product), in prefill and decode alike.
+ * bf16 for the value product), in prefill and decode alike.  With an MXFP4
+ * cache, code * scale widens to bf16 exactly and the arithmetic is the bf16
+ * path's.
  * Neither q nor the caches are written.
  */
 PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
@@ -224,7 +244,10 @@ PA_API const char *pa_last_error(void);
  * tokens in logical order, raw (bf16 or E4M3 bytes, no scaling):
  *   k_out[p][h][:] = k_cache[block_table_row[p / bs]][h][p % bs][:]
  * for p < ctx; same for v_out.  block_table_row is a device pointer;
- * k_out, v_out are [ctx][num_kv_heads][head_dim] elements of the cache type. */
+ * k_out, v_out are [ctx][num_kv_heads][head_dim] elements of the cache type.
+ * MXFP4: k_out, v_out receive the values instead, bf16 [ctx][num_kv_heads]
+ * [head_dim] (code * scale, exact), widened by the attention kernels' own
+ * conversion. */
 PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_row, int32_t ctx,
                           void *k_out, void *v_out, void *stream);
 

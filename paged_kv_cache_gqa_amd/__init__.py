@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = 4, 5
-PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
+PA_KV_BF16, PA_KV_FP8_E4M3, PA_KV_MXFP4 = 0, 1, 2
 TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
 TIMING_KINDS = 4
 
@@ -142,30 +142,42 @@ def _code_dtypes():
 
 
 def make_cache(k_cache, v_cache, k_scale=None, v_scale=None) -> pa_kv_cache:
-    """Describe caches [num_blocks, num_kv_heads, block_size, head_dim]
-    (bf16, or E4M3 codes as uint8 / float8_e4m3fn with fp32
-    [num_blocks, num_kv_heads] scales).  The tensors must outlive every call
-    that uses the returned descriptor."""
+    """Describe caches [num_blocks, num_kv_heads, block_size, head_dim]: bf16;
+    E4M3 codes (uint8 / float8_e4m3fn) with fp32 [num_blocks, num_kv_heads]
+    scales; or MXFP4, codes uint8 [num_blocks, num_kv_heads, block_size,
+    head_dim / 2] with E8M0 scale bytes (uint8 / float8_e8m0fnu)
+    [num_blocks, num_kv_heads, head_dim / 32, block_size].  The scales' dtype
+    tells E4M3 from MXFP4.  The tensors must outlive every call that uses the
+    returned descriptor."""
     import torch
     if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
         _bad("k_cache must be a 4-D tensor [num_blocks, num_kv_heads, block_size, head_dim]")
-    nb, hkv, bs, d = (int(x) for x in k_cache.shape)
-    fp8 = k_cache.dtype in _code_dtypes()
-    dtypes = _code_dtypes() if fp8 else _bf16()
+    nb, hkv, bs, last = (int(x) for x in k_cache.shape)
+    coded = k_cache.dtype in _code_dtypes()
+    e8m0 = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+    fp4 = coded and isinstance(k_scale, torch.Tensor) and k_scale.dtype in e8m0
+    d = 2 * last if fp4 else last
+    dtypes = _code_dtypes() if coded else _bf16()
     ok = [_tensor(k_cache, "k_cache", dtypes),
-          _tensor(v_cache, "v_cache", (k_cache.dtype,), (nb, hkv, bs, d))]
-    if fp8:
+          _tensor(v_cache, "v_cache", (k_cache.dtype,), (nb, hkv, bs, last))]
+    if coded:
         if k_scale is None or v_scale is None:
-            raise PagedAttnError(PA_ERR_NULL_ARG, "an E4M3 cache needs k_scale and v_scale")
-        ok += [_tensor(k_scale, "k_scale", (torch.float32,), (nb, hkv)),
-               _tensor(v_scale, "v_scale", (torch.float32,), (nb, hkv))]
+            raise PagedAttnError(PA_ERR_NULL_ARG, "an E4M3 or MXFP4 cache needs k_scale and v_scale")
+        if fp4:
+            if d % 32:
+                _bad(f"MXFP4 head_dim {d} is not a multiple of 32")
+            ok += [_tensor(k_scale, "k_scale", e8m0, (nb, hkv, d // 32, bs)),
+                   _tensor(v_scale, "v_scale", (k_scale.dtype,), (nb, hkv, d // 32, bs))]
+        else:
+            ok += [_tensor(k_scale, "k_scale", (torch.float32,), (nb, hkv)),
+                   _tensor(v_scale, "v_scale", (torch.float32,), (nb, hkv))]
     elif k_scale is not None or v_scale is not None:
         _bad("a bf16 cache takes no scales")
     _on_device(ok, k_cache.device)
     c = pa_kv_cache(k_cache.data_ptr(), v_cache.data_ptr(),
                     None if k_scale is None else k_scale.data_ptr(),
                     None if v_scale is None else v_scale.data_ptr(),
-                    nb, hkv, bs, d, PA_KV_FP8_E4M3 if fp8 else PA_KV_BF16)
+                    nb, hkv, bs, d, PA_KV_MXFP4 if fp4 else PA_KV_FP8_E4M3 if coded else PA_KV_BF16)
     c.device = k_cache.device
     return c
 
@@ -316,6 +328,7 @@ def pa_debug_gather(cache: pa_kv_cache, block_table_row, ctx, k_out, v_out, stre
     ok = [_tensor(block_table_row, "block_table_row", (torch.int32,), (None,))]
     if int(block_table_row.shape[0]) * cache.block_size < int(ctx):
         _bad(f"block_table_row covers {int(block_table_row.shape[0]) * cache.block_size} tokens, ctx {ctx}")
+    # (MXFP4: the values, bf16)
     dt = _code_dtypes() if cache.dtype == PA_KV_FP8_E4M3 else _bf16()
     shape = (int(ctx), cache.num_kv_heads, cache.head_dim)
     ok += [_tensor(k_out, "k_out", dt, shape), _tensor(v_out, "v_out", dt, shape)]

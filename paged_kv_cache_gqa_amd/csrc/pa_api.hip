@@ -61,13 +61,16 @@ pa_status check_cache(const pa_kv_cache *c) {
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
   if (c->block_size != 16 && c->block_size != 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (16 or 64)", c->block_size);
-  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3)
+  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3 && c->dtype != PA_KV_MXFP4)
     return fail(PA_ERR_UNSUPPORTED, "unknown KV dtype %d", (int)c->dtype);
-  const bool fp8 = c->dtype == PA_KV_FP8_E4M3;
-  if (fp8 && (!c->k_scale || !c->v_scale))
-    return fail(PA_ERR_NULL_ARG, "E4M3 cache needs k_scale and v_scale");
-  if (!fp8 && (c->k_scale || c->v_scale))
+  const bool scaled = c->dtype != PA_KV_BF16;
+  if (scaled && (!c->k_scale || !c->v_scale))
+    return fail(PA_ERR_NULL_ARG, "%s cache needs k_scale and v_scale",
+                c->dtype == PA_KV_MXFP4 ? "MXFP4" : "E4M3");
+  if (!scaled && (c->k_scale || c->v_scale))
     return fail(PA_ERR_BAD_SHAPE, "bf16 cache must not carry scales");
+  if (c->dtype == PA_KV_MXFP4 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "MXFP4 KV needs head_dim 128 (got %d)", c->head_dim);
   return PA_OK;
 }
 
@@ -709,9 +712,9 @@ pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const void *v_n
   a.lbs = a.bs == 16 ? 4 : 6;
   a.d = cache->head_dim;
   a.lcpr = a.d == 64 ? 3 : 4;
-  const bool fp8 = cache->dtype == PA_KV_FP8_E4M3;
+  const int fmt = (int)cache->dtype;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = timed(0, s, [&] { return launch_append(a, fp8, num_tokens, s); });
+  hipError_t e = timed(0, s, [&] { return launch_append(a, fmt, num_tokens, s); });
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return PA_OK;
 }
@@ -826,7 +829,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   a.scale_log2 = scale * 1.44269504088896341f;
   a.out = out;
   a.lse_out = lse_out;
-  const bool fp8 = cache->dtype == PA_KV_FP8_E4M3;
+  const int fmt = (int)cache->dtype;
   const int bs = cache->block_size;
   hipError_t e;
   if (!P.prefill.empty()) {
@@ -836,7 +839,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     ap.part_lse = (float *)(ws + P.off_pl_pre);
     ap.wg_first = P.wg_first.empty() ? nullptr : (const int32_t *)(ws + P.off_wg);
     const int n = P.wg_first.empty() ? (int)P.prefill.size() : (int)P.wg_first.size() - 1;
-    e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fp8, s); });
+    e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
   if (!P.cascade.empty()) {  // one launch: the cascade items, then the decode items
@@ -856,7 +859,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     a.part_o = (float *)(ws + P.off_po_dec);
     a.part_lse = (float *)(ws + P.off_pl_dec);
     const int n = (int)P.decode.size();
-    e = timed(2, s, [&] { return launch_decode(a, n, d, bs, fp8, s); });
+    e = timed(2, s, [&] { return launch_decode(a, n, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "decode attention launch");
   }
   if (!P.merges.empty()) {
@@ -973,8 +976,13 @@ pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_r
   g.v_out = v_out;
   g.hkv = cache->num_kv_heads;
   g.bs = cache->block_size;
-  g.row_bytes = cache->head_dim * (cache->dtype == PA_KV_FP8_E4M3 ? 1 : 2);
-  g.total_chunks = (int64_t)ctx * g.hkv * (g.row_bytes / 16);
+  g.ks = cache->k_scale;
+  g.vs = cache->v_scale;
+  g.fmt = (int)cache->dtype;
+  g.row_bytes = cache->dtype == PA_KV_MXFP4 ? cache->head_dim / 2
+                                            : cache->head_dim * (cache->dtype == PA_KV_FP8_E4M3 ? 1 : 2);
+  // (MXFP4: one thread per 8 elements, i.e. per 4 bytes of codes)
+  g.total_chunks = (int64_t)ctx * g.hkv * (cache->dtype == PA_KV_MXFP4 ? cache->head_dim / 8 : g.row_bytes / 16);
   hipError_t e = launch_gather(g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   return PA_OK;

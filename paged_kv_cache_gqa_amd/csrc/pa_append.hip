@@ -11,7 +11,12 @@
 // thread moves one 16-byte chunk (8 elements) of one (token, KV head) row of
 // K and of V; a token with a negative slot is skipped.  8-bit caches store
 // E4M3(x / scale) with the correctly rounded fp32 quotient, nearest-even
-// rounding and saturation to +-448.
+// rounding and saturation to +-448.  4-bit caches ([V41] kernels section: an
+// FP4 KV cache) are OCP MXFP4: the four threads of a 32-element group find
+// its largest magnitude, whose exponent less 2 (the largest E2M1 exponent),
+// clamped at 2^-127, is the group's E8M0 scale; each element divided by it
+// (exact: a power of two) rounds to E2M1, nearest-even, saturating at 6.  A
+// group holding a NaN or an infinity gets the NaN scale and zero codes.
 #include <algorithm>
 
 #include "pa_device.h"
@@ -19,7 +24,7 @@
 
 namespace pa {
 
-template <bool FP8>
+template <int FMT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   // 32-bit index arithmetic within a launch (the host keeps each launch
   // below 2^31 chunks) and shifts for the power-of-two sizes: the 64-bit
@@ -32,18 +37,52 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int h = (int)(row - tl * (uint32_t)a.hkv);
   const int64_t t = a.tok0 + tl;
   const int64_t slot = a.slots[t];
+  // (the threads of a row share its slot: a 32-element group, four adjacent
+  // lanes of one row, is skipped or kept as a whole)
   if (slot < 0) return;
   const int64_t blk = slot >> a.lbs, off = slot & (a.bs - 1);
   const int64_t src = (t * a.hkv + h) * a.d + ch * 8;                   // element offset
   const int64_t dst = ((blk * a.hkv + h) * a.bs + off) * a.d + ch * 8;  // element offset
   const uint4 kv = gload16_nt((const unsigned char *)a.k_new + src * 2);
   const uint4 vv = gload16_nt((const unsigned char *)a.v_new + src * 2);
-  if constexpr (!FP8) {
+  if constexpr (FMT == kKvBf16) {
     *(uint4 *)((unsigned char *)a.k_cache + dst * 2) = kv;
     *(uint4 *)((unsigned char *)a.v_cache + dst * 2) = vv;
+  } else if constexpr (FMT == kKvMxfp4) {
+    const int64_t sdst = ((blk * a.hkv + h) * (a.d >> 5) + (ch >> 2)) * a.bs + off;  // scale byte
+    auto encode = [&](const uint4 x, unsigned char *codes, unsigned char *scales) {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      float f[8];
+      float amax = 0.f;
+      bool finite = true;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        f[i] = bf16_bits_to_float((w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
+        const float m = __builtin_fabsf(f[i]);
+        finite = finite && m <= 3.4028235e38f;  // false for infinities and NaN
+        amax = fmaxf(amax, m);
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      int fin = finite ? 1 : 0;
+      fin &= __shfl_xor(fin, 1);
+      fin &= __shfl_xor(fin, 2);
+      // the shared exponent: amax's exponent field less 2, at least 0 (a
+      // subnormal or zero amax has field 0)
+      const int ef = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
+      const uint32_t e = fin ? (uint32_t)max(ef - 2, 0) : 0xFFu;
+      const float inv = __builtin_bit_cast(float, (254u - min(e, 253u)) << 23);  // 2^(127 - e), e <= 252
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) packed |= (fin ? e2m1_code(f[i] * inv) : 0u) << (4 * i);
+      *(uint32_t *)(codes + dst / 2) = packed;
+      if ((ch & 3) == 0) scales[sdst] = (unsigned char)e;
+    };
+    encode(kv, (unsigned char *)a.k_cache, (unsigned char *)a.ks);
+    encode(vv, (unsigned char *)a.v_cache, (unsigned char *)a.vs);
   } else {
-    const float ks = a.ks[blk * a.hkv + h];
-    const float vs = a.vs[blk * a.hkv + h];
+    const float ks = ((const float *)a.ks)[blk * a.hkv + h];
+    const float vs = ((const float *)a.vs)[blk * a.hkv + h];
     const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
     const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
     uint32_t ko[2] = {0, 0}, vo[2] = {0, 0};
@@ -97,7 +136,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   *(uint4 *)((unsigned char *)a.v_out + dst) = *(const uint4 *)((const unsigned char *)a.v + src);
 }
 
-hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipStream_t s) {
+hipError_t launch_append(const AppendArgs &a, int fmt, int64_t num_tokens, hipStream_t s) {
   // token pieces of at most 2^30 chunks each
   const int64_t row_chunks = (int64_t)a.hkv << a.lcpr;
   const int64_t piece = std::max<int64_t>(1, ((int64_t)1 << 30) / row_chunks);
@@ -106,20 +145,49 @@ hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipS
     b.tok0 = t0;
     b.nchunks = (uint32_t)(std::min(piece, num_tokens - t0) * row_chunks);
     const unsigned blocks = (b.nchunks + 255) / 256;
-    if (fp8)
-      hipLaunchKernelGGL(append_kernel<true>, dim3(blocks), dim3(256), 0, s, b);
+    if (fmt == kKvE4m3)
+      hipLaunchKernelGGL(append_kernel<kKvE4m3>, dim3(blocks), dim3(256), 0, s, b);
+    else if (fmt == kKvMxfp4)
+      hipLaunchKernelGGL(append_kernel<kKvMxfp4>, dim3(blocks), dim3(256), 0, s, b);
     else
-      hipLaunchKernelGGL(append_kernel<false>, dim3(blocks), dim3(256), 0, s, b);
+      hipLaunchKernelGGL(append_kernel<kKvBf16>, dim3(blocks), dim3(256), 0, s, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+// MXFP4: the values, widened as the attention kernels widen them (bf16
+// [ctx][hkv][d]); one thread per 8 elements: a dword of codes and its
+// group's scale byte.
+__global__ __launch_bounds__(256) void gather_fp4_kernel(GatherArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= a.total_chunks) return;
+  const int d = a.row_bytes * 2;
+  const int cpr = d / 8;
+  const int ch = (int)(gid % cpr);
+  const int64_t th = gid / cpr;
+  const int h = (int)(th % a.hkv);
+  const int64_t p = th / a.hkv;
+  const int64_t blk = a.bt_row[p / a.bs];
+  const int64_t row = (blk * a.hkv + h) * a.bs + p % a.bs;
+  const int64_t sc = ((blk * a.hkv + h) * (d / 32) + ch / 4) * a.bs + p % a.bs;
+  const int64_t dst = (th * d + ch * 8) * 2;
+  const uint32_t kw = *(const uint32_t *)((const unsigned char *)a.k + row * a.row_bytes + ch * 4);
+  const uint32_t vw = *(const uint32_t *)((const unsigned char *)a.v + row * a.row_bytes + ch * 4);
+  const float ks = e8m0_operand(((const unsigned char *)a.ks)[sc]);
+  const float vs = e8m0_operand(((const unsigned char *)a.vs)[sc]);
+  *(bf16x8 *)((unsigned char *)a.k_out + dst) = fp4x8_to_bf16x8(kw, ks);
+  *(bf16x8 *)((unsigned char *)a.v_out + dst) = fp4x8_to_bf16x8(vw, vs);
+}
+
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
   if (a.total_chunks <= 0) return hipSuccess;
   const int64_t blocks = (a.total_chunks + 255) / 256;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (a.fmt == kKvMxfp4)
+    hipLaunchKernelGGL(gather_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

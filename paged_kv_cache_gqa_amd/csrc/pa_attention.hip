@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       for (int j = 0; j < NSC; j++) {
         const int bidx = min((t * kKeyTile + j * BS) / BS, last_blk);
         const int64_t blk = bt[bidx];
-        ksc_n[j] = a.c.ks[blk * hkv + it.kvh];
-        vsc_n[j] = a.c.vs[blk * hkv + it.kvh];
+        ksc_n[j] = ((const float *)a.c.ks)[blk * hkv + it.kvh];
+        vsc_n[j] = ((const float *)a.c.vs)[blk * hkv + it.kvh];
       }
     }
   };
@@ -963,7 +963,9 @@ __global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
 // The four waves of a decode work-group hold softmax states (m in log2
 // units, per-lane partial l, o[d-block]) over disjoint keys of one item's
 // 16 rows; combine them through LDS and write the rows (or the item's partial).
-template <int D, int NW = 4>
+// PAIRED (the MXFP4 kernel): o[2j] holds d = 32j + 2(4 q4 + r), o[2j + 1]
+// the odd d next to it; otherwise o[db] holds d = 16 db + 4 q4 + r.
+template <int D, int NW = 4, bool PAIRED = false>
 __device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it, unsigned char *smem_raw,
                                                float m, float l, const f32x4 (&o)[D / 16]) {
   constexpr int ND = D / 16;
@@ -977,9 +979,19 @@ __device__ __forceinline__ void decode_combine(const AttnArgs &a, const Item &it
   float *red_o = (float *)smem_raw;                  // [NW][16][D]
   float *red_m = red_o + NW * 16 * D;                // [NW][16]
   float *red_l = red_m + NW * 16;                    // [NW][16]
+  if constexpr (PAIRED) {
 #pragma unroll
-  for (int db = 0; db < ND; db++)
-    *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
+    for (int j = 0; j < ND / 2; j++) {
+      const f32x4 lo = o[2 * j], hi = o[2 * j + 1];
+      float *dst = red_o + (wave * 16 + n) * D + 32 * j + 8 * q4;
+      *(f32x4 *)dst = f32x4{lo[0], hi[0], lo[1], hi[1]};
+      *(f32x4 *)(dst + 4) = f32x4{lo[2], hi[2], lo[3], hi[3]};
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+      *(f32x4 *)(red_o + (wave * 16 + n) * D + db * 16 + 4 * q4) = o[db];
+  }
   if (q4 == 0) {
     red_m[wave * 16 + n] = m;
     red_l[wave * 16 + n] = l;
@@ -1102,8 +1114,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
         }
       }
       if constexpr (FP8) {
-        R.ksc[kb] = a.c.ks[blk * hkv + it.kvh];
-        R.vsc[kb] = a.c.vs[blk * hkv + it.kvh];
+        R.ksc[kb] = ((const float *)a.c.ks)[blk * hkv + it.kvh];
+        R.vsc[kb] = ((const float *)a.c.vs)[blk * hkv + it.kvh];
       }
     }
   };
@@ -1800,6 +1812,287 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) 
 }
 
 // =============================================================================
+// Decode for MXFP4 KV, head_dim 128 ([V41] kernels section: a 4-bit KV cache,
+// about half the bytes of 8-bit): wave w takes the 64-key slices w, w+4, ...
+// of the item's range.  A slice's K codes (and V codes) are 4 KB, 64 rows of
+// 64 bytes, moved into the wave's ring by four 1 KB LDS-filling loads of 16
+// rows (one cache block each for block sizes 16 and 64); its K (and V) scale
+// bytes, 256 of them, follow by one-dword-per-lane loads (block 64: the
+// block's [group][key] bytes as they are; block 16: four loads by lanes
+// 0..15, one per block, giving [block][group][16 keys]).  LDS row r holds its
+// logical 16-byte chunk q at position q ^ G(r), G(r) = x0 | ((x0 ^ x1 ^ r4)
+// << 1) with x = (r >> 2) & 3 and r4 = bit 4 of r, which keeps both read
+// patterns below free of bank conflicts.
+//   Scores, per 16-key quarter h: S_h = K_h Q^T on v_mfma_f32_16x16x32_bf16.
+//   The contraction over d is ordered so that lane (n, q4) reads one 16-byte
+//   chunk -- d 32 q4 .. +31 of key 16h + n, a single scale group -- and MFMA
+//   c takes d 32 q4 + 8c .. +7 from it (Q is loaded in the same order); the
+//   codes widen to bf16 with the group's scale, exactly, 2 per instruction.
+//   Values: O^T += V^T P^T over each 32-key half.  A transposing 8-bit read
+//   gives lane (n, q4) byte n of chunk j for the half's keys in P's order;
+//   that byte holds d 32j + 2n and 32j + 2n + 1 of one key, whose scale
+//   group is j, so each key's pair widens with one instruction and the pairs
+//   are regrouped into two A operands: one MFMA over the even d, one over
+//   the odd.  Lane (n, q4) then holds d 32j + 8 q4 .. +7 of row n.
+constexpr int kDec4Slice = 64;                       // keys per wave step
+constexpr int kDec4CodeBytes = kDec4Slice * 64;      // K (or V) codes of one slice, 4 KB
+constexpr int kDec4ScaleBytes = kDec4Slice * 4;      // K (or V) scale bytes of one slice
+constexpr int kDec4StageBytes = 2 * kDec4CodeBytes + 2 * kDec4ScaleBytes;
+
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int ND = D / 16;
+  constexpr int SB = kDec4CodeBytes;
+  constexpr int STB = kDec4StageBytes;
+  constexpr int PER_SLICE = 8 + (BS == 64 ? 2 : 8);  // vector-memory instructions per slice
+  static_assert(BS == 16 || BS == 64, "block size");
+  static_assert(NW * NST * STB >= NW * 16 * (D + 2) * 4, "combine scratch");
+  // (every request of the NST stages outstanding at once fits the 6-bit
+  // vector-memory counter)
+  static_assert(PER_SLICE * NST < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * STB];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  lds_u8 *smem = (lds_u8 *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const Item it = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q4 = lane >> 4;
+  const int tok = n >> a.lg, g = n & (a.group - 1);
+  const bool active = tok < it.nq;
+  const int pos = it.pos0 + tok;
+  const int qh = it.kvh * a.group + g;
+  const int hkv = a.c.hkv;
+  const int kv_lo = it.kv_lo, kv_hi = it.kv_hi;
+
+  // Q in the contraction order of the score product: qf[c] = d 32 q4 + 8c ..
+  bf16x8 qf[4];
+  {
+    const unsigned char *qrow =
+        (const unsigned char *)a.q + (((int64_t)(it.row0 + tok) * a.hq + qh) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      uint4 v = active ? gload16(qrow + (32 * q4 + 8 * c) * 2) : make_uint4(0, 0, 0, 0);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+
+  float m = kNegBig, l = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; i++) o[i] = f32x4{};
+
+  const unsigned char *kc = (const unsigned char *)a.c.k;
+  const unsigned char *vc = (const unsigned char *)a.c.v;
+  const unsigned char *ksc = (const unsigned char *)a.c.ks;
+  const unsigned char *vsc = (const unsigned char *)a.c.vs;
+  const int n_slices = (kv_hi - kv_lo + kDec4Slice - 1) / kDec4Slice;
+  const int nw = n_slices > wave ? (n_slices - wave + NW - 1) / NW : 0;  // this wave's slices
+  const int blk0 = kv_lo / BS;
+  const int last_blk = (kv_hi - 1) / BS;
+  const int lim = min(pos, kv_hi - 1);
+  {  // the item's block ids into LDS (see the bf16 kernel)
+    const int32_t *btr = a.bt + (int64_t)it.seq * a.max_blocks + blk0;
+    for (int i = tid; i <= last_blk - blk0; i += 64 * NW) bt_lds[i] = btr[i];
+  }
+  PA_WAIT_VMCNT(0);
+  __syncthreads();
+  const int lim_min = min(it.pos0, kv_hi - 1);
+
+  auto G = [](int r) {
+    const int x = (r >> 2) & 3;
+    return (x & 1) | ((((x ^ (x >> 1)) ^ (r >> 4)) & 1) << 1);
+  };
+  // code loads: load L fills rows 16L .. 16L+15; lane i writes position
+  // i & 3 of row 16L + (i >> 2) and so fetches that row's chunk (i & 3) ^ G
+  // (G depends on L only through its parity)
+  int voff[2];
+#pragma unroll
+  for (int par = 0; par < 2; par++)
+    voff[par] = (lane >> 2) * 64 + 16 * ((lane & 3) ^ G(16 * par + (lane >> 2)));
+  const uint32_t ring = smem_addr + wave * NST * STB;
+  lds_u8 *ring_p = smem + wave * NST * STB;
+
+  auto slice_key = [&](int k) { return kv_lo + kDec4Slice * (wave + NW * k); };
+  auto block_at = [&](int key) {
+    return __builtin_amdgcn_readfirstlane(bt_lds[min(key / BS, last_blk) - blk0]);
+  };
+  auto desc = [](const unsigned char *p, int nrec) __attribute__((always_inline)) {
+    const uint64_t q = (uint64_t)p;
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)q),
+                   __builtin_amdgcn_readfirstlane((int)((q >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+  };
+  // A request past the range end has a buffer size of zero: it moves no
+  // data (zeros land in LDS) but keeps the per-slice vmcnt accounting.
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int key0 = slice_key(min(k, max(nw - 1, 0)));
+    const bool live = k < nw;
+    const uint32_t st = ring + (k % NST) * STB;
+#pragma unroll
+    for (int L = 0; L < 4; L++) {
+      const int row0 = key0 + 16 * L;
+      const int64_t blk = block_at(row0);
+      const int64_t base = ((blk * hkv + it.kvh) * BS + row0 % BS) * (D / 2);
+      const int nrec = __builtin_amdgcn_readfirstlane(live ? min(max(kv_hi - row0, 0), 16) * (D / 2) : 0);
+      dma_load16_nt(desc(kc + base, nrec), voff[L & 1], st + L * 1024);
+      dma_load16_nt(desc(vc + base, nrec), voff[L & 1], st + SB + L * 1024);
+    }
+    if constexpr (BS == 64) {  // the slice is one block: its [group][64 keys] bytes
+      const int64_t blk = block_at(key0);
+      const int64_t base = (blk * hkv + it.kvh) * (D / 32) * BS;
+      const int nrec = __builtin_amdgcn_readfirstlane(live ? kDec4ScaleBytes : 0);
+      dma_load4(desc(ksc + base, nrec), 4 * lane, st + 2 * SB);
+      dma_load4(desc(vsc + base, nrec), 4 * lane, st + 2 * SB + kDec4ScaleBytes);
+    } else {  // four blocks of [group][16 keys], 64 bytes each
+      if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int64_t blk = block_at(key0 + 16 * j);
+          const int64_t base = (blk * hkv + it.kvh) * (D / 32) * BS;
+          const int nrec = __builtin_amdgcn_readfirstlane(live && key0 + 16 * j < kv_hi ? 64 : 0);
+          dma_load4(desc(ksc + base, nrec), 4 * lane, st + 2 * SB + 64 * j);
+          dma_load4(desc(vsc + base, nrec), 4 * lane, st + 2 * SB + kDec4ScaleBytes + 64 * j);
+        }
+      }
+    }
+  };
+
+  // per-lane LDS offsets.  K: row 16h + n, chunk q4 (position q4 ^ G), and
+  // its scale byte (group q4).  V^T: lane pair (n >> 1) addresses key row vr
+  // of the half (P's order: 4 q4 + i, then 16 + 4 q4 + i), half n & 1 of
+  // chunk j at position j ^ G; the half's scale dwords of group j.
+  auto kofs = [&](int h) { return (16 * h + n) * 64 + 16 * (q4 ^ G(16 * h + n)); };
+  auto ksofs = [&](int h) { return BS == 64 ? 64 * q4 + 16 * h + n : 64 * h + 16 * q4 + n; };
+  const int vr = (n >> 1) < 4 ? 4 * q4 + (n >> 1) : 16 + 4 * q4 + (n >> 1) - 4;
+  auto vofs = [&](int hf) { return (32 * hf + vr) * 64 + 16 * G(32 * hf + vr) + 8 * (n & 1); };
+  auto vsofs = [&](int hf, int j, int part) {  // keys 32 hf + 16 part + 4 q4 .. +3, group j
+    return BS == 64 ? 64 * j + 32 * hf + 16 * part + 4 * q4 : 64 * (2 * hf + part) + 16 * j + 4 * q4;
+  };
+  typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+
+  // Slice k is read from LDS into registers first; its stage is then free
+  // and slice k + NST is requested into it before the arithmetic.
+  auto compute = [&](int k) __attribute__((always_inline)) {
+    const lds_u8 *Ks = ring_p + (k % NST) * STB;
+    const lds_u8 *Vs = Ks + SB;
+    const lds_u8 *KSs = Ks + 2 * SB;
+    const lds_u8 *VSs = KSs + kDec4ScaleBytes;
+    const int key0 = slice_key(k);
+    uint4 kraw[4];
+    uint32_t kse[4];
+    uint2 vraw[2][4];
+    uint32_t vse[2][4][2];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      kraw[h] = lds_load16(Ks + kofs(h));
+      kse[h] = *(KSs + ksofs(h));
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        vraw[hf][j] = lds_read_tr8(Vs + (vofs(hf) ^ (j << 4)));
+#pragma unroll
+        for (int part = 0; part < 2; part++) vse[hf][j][part] = *(lds_u32 *)(VSs + vsofs(hf, j, part));
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's bytes are in registers
+    __builtin_amdgcn_sched_barrier(0);
+    issue(k + NST);
+    if (key0 + kDec4Slice > kv_hi) {
+      // keys past the range: zero codes, but the scale bytes of unwritten
+      // slots may be anything (the NaN scale included), so those keys' V
+      // scales become 2^-127: their values are then 0 and the zero
+      // probabilities they meet add nothing (their scores are masked)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+        for (int part = 0; part < 2; part++) {
+          const int c = min(max(kv_hi - (key0 + 32 * hf + 16 * part + 4 * q4), 0), 4);
+          const uint32_t keep = c >= 4 ? 0xFFFFFFFFu : (1u << (8 * c)) - 1u;
+#pragma unroll
+          for (int j = 0; j < 4; j++) vse[hf][j][part] &= keep;
+        }
+    }
+    f32x4 s[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const float sc = e8m0_operand(kse[h]);
+      const uint32_t w[4] = {kraw[h].x, kraw[h].y, kraw[h].z, kraw[h].w};
+#pragma unroll
+      for (int c = 0; c < 4; c++) s[h] = mfma16x16x32(fp4x8_to_bf16x8(w[c], sc), qf[c], c == 0 ? f32x4{} : s[h]);
+      s[h] *= a.scale_log2;  // base-2 logits
+    }
+    if (key0 + kDec4Slice - 1 > lim_min) {
+#pragma unroll
+      for (int h = 0; h < 4; h++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[h][r] = key0 + 16 * h + 4 * q4 + r <= lim ? s[h][r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 4; h++) mx = fmaxf(mx, fmaxf(fmaxf(s[h][0], s[h][1]), fmaxf(s[h][2], s[h][3])));
+    mx = xor32_max(xor16_max(mx));
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      bf16x8 pb;
+#pragma unroll
+      for (int part = 0; part < 2; part++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const float p = fast_exp2(s[2 * hf + part][r] - m);
+          l += p;
+          pb[4 * part + r] = (__bf16)p;
+        }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        // key i of the half (P's order): byte i of vraw and scale byte i of
+        // the part's dword; it widens to (d 32j + 2n, d 32j + 2n + 1)
+        uint32_t pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const uint32_t w = i < 4 ? vraw[hf][j].x : vraw[hf][j].y;
+          const float sc = e8m0_operand((vse[hf][j][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+          if ((i & 3) == 0) pr[i] = fp4x2_to_bf16x2<0>(w, sc);
+          if ((i & 3) == 1) pr[i] = fp4x2_to_bf16x2<1>(w, sc);
+          if ((i & 3) == 2) pr[i] = fp4x2_to_bf16x2<2>(w, sc);
+          if ((i & 3) == 3) pr[i] = fp4x2_to_bf16x2<3>(w, sc);
+        }
+        const uint4 ev = make_uint4(__builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u),
+                                    __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u),
+                                    __builtin_amdgcn_perm(pr[5], pr[4], 0x05040100u),
+                                    __builtin_amdgcn_perm(pr[7], pr[6], 0x05040100u));
+        const uint4 od = make_uint4(__builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u),
+                                    __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u),
+                                    __builtin_amdgcn_perm(pr[5], pr[4], 0x07060302u),
+                                    __builtin_amdgcn_perm(pr[7], pr[6], 0x07060302u));
+        o[2 * j] = mfma16x16x32(as_bf16x8(ev), pb, o[2 * j]);
+        o[2 * j + 1] = mfma16x16x32(as_bf16x8(od), pb, o[2 * j + 1]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < NST; k++) issue(k);
+  for (int k = 0; k < nw; k++) {
+    PA_WAIT_VMCNT(PER_SLICE * (NST - 1));  // slice k has landed (slices k+1 .. k+NST-1 may be in flight)
+    compute(k);                            // requests slice k + NST into slice k's stage
+  }
+  PA_WAIT_VMCNT(0);
+  decode_combine<D, NW, true>(a, it, smem_raw, m, l, o);
+}
+
+// =============================================================================
 // LSE merge of split items ([Agentic] §4.3.3): for each row,
 // out = sum_i w_i o_i / sum_i w_i with w_i = 2^(lse_i - M), M = max_i lse_i,
 // lse = M + log2(sum_i w_i); parts without keys (lse = -inf) weigh nothing
@@ -2021,12 +2314,25 @@ static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
     return hipErrorInvalidValue;                                                   \
   } while (0)
 
-hipError_t launch_prefill(const AttnArgs &a, int n, int d, int bs, bool fp8, hipStream_t s) {
+hipError_t launch_prefill(const AttnArgs &a, int n, int d, int bs, int fmt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (fmt == kKvMxfp4) return hipErrorInvalidValue;
+  const bool fp8 = fmt == kKvE4m3;
   PA_DISPATCH(launch_prefill_t, a, n, s);
 }
-hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, bool fp8, hipStream_t s) {
+hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, int fmt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (fmt == kKvMxfp4) {
+    if (d != 128) return hipErrorInvalidValue;
+    if (bs == 16)  // 16 requests per slice: three stages keep them within the counter
+      hipLaunchKernelGGL((decode_dma_fp4_kernel<16, 4, 3>), dim3(n), dim3(256), 0, s, a);
+    else if (bs == 64)
+      hipLaunchKernelGGL((decode_dma_fp4_kernel<64, 4, 4>), dim3(n), dim3(256), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  const bool fp8 = fmt == kKvE4m3;
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
 hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,

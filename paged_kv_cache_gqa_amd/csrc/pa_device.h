@@ -158,6 +158,42 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8_hw(uint2 w) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// OCP MXFP4 -> bf16 with gfx950's conversion instruction: byte SEL of w
+// holds two E2M1 codes (the lower-indexed element in the low 4 bits); the
+// scale operand is the float whose bit pattern is e << 23, which the
+// instruction applies as the E8M0 scale 2^(e - 127) (e = 0 and the NaN scale
+// e = 255 included -- checked against the format's definition over every
+// (byte, e) pair).  A code times a power of two is exact in bf16.
+__device__ __forceinline__ float e8m0_operand(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, SEL));
+}
+// eight codes (one dword, elements in order) sharing one scale
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float sc) {
+  return as_bf16x8(make_uint4(fp4x2_to_bf16x2<0>(w, sc), fp4x2_to_bf16x2<1>(w, sc), fp4x2_to_bf16x2<2>(w, sc),
+                              fp4x2_to_bf16x2<3>(w, sc)));
+}
+
+// E2M1 code of a value already divided by its group's scale: nearest of 0,
+// 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even mantissa (rint in the
+// binade's step: 0.5 below 2, 1 below 4, 2 above), magnitudes >= 6 saturate;
+// the sign bit is v's.  The code is the step count plus the binade's offset.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 28) & 8u;
+  const float a = __builtin_fabsf(v);
+  uint32_t c;
+  if (a < 2.f)
+    c = (uint32_t)__builtin_rintf(a * 2.f);
+  else if (a < 4.f)
+    c = (uint32_t)__builtin_rintf(a) + 2u;
+  else if (a < 6.f)
+    c = (uint32_t)__builtin_rintf(a * 0.5f) + 4u;
+  else
+    c = 7u;
+  return sign | c;
+}
+
 // Round a float to E4M3, nearest-even, saturating finite and infinite
 // magnitudes above 448 to 448; NaN -> 0x7F with the input's sign.
 __device__ __forceinline__ uint32_t float_to_e4m3(float x) {

@@ -59,11 +59,14 @@ struct CascadeMember {
 };
 constexpr int kCascadeRows = 64;  // query rows per cascade tile (4 row blocks of 16)
 
+// KV element formats (pa_kv_dtype)
+enum KvFmt : int { kKvBf16 = 0, kKvE4m3 = 1, kKvMxfp4 = 2 };
+
 struct CacheArgs {
   const void *k;
   const void *v;
-  const float *ks;
-  const float *vs;
+  const void *ks;         // E4M3: fp32 [nb][hkv]; MXFP4: E8M0 bytes [nb][hkv][d/32][bs]
+  const void *vs;
   int32_t num_blocks;
   int32_t hkv;
 };
@@ -106,8 +109,8 @@ struct AppendArgs {
   const int64_t *slots;
   void *k_cache;
   void *v_cache;
-  const float *ks;
-  const float *vs;
+  void *ks;               // E4M3: read; MXFP4: written
+  void *vs;
   int64_t tok0;           // first token of this launch
   uint32_t nchunks;       // this launch's tokens * hkv * (d / 8), below 2^31
   int32_t hkv;
@@ -120,13 +123,16 @@ struct AppendArgs {
 struct GatherArgs {
   const void *k;
   const void *v;
+  const void *ks;         // MXFP4: scale bytes (the gather then writes bf16 values)
+  const void *vs;
   const int32_t *bt_row;
   void *k_out;
   void *v_out;
   int64_t total_chunks;   // ctx * hkv * (row bytes / 16)
   int32_t hkv;
   int32_t bs;
-  int32_t row_bytes;      // d * element bytes
+  int32_t row_bytes;      // d * element bytes (MXFP4: d / 2)
+  int32_t fmt;            // KvFmt
 };
 
 constexpr int kRegTileRows = 128;  // query rows (tokens x heads) per tile of prefill_kernel
@@ -138,8 +144,8 @@ constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
 
 // Launchers (defined next to their kernels).
-hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
-hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, bool fp8, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
+hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 // bf16 head_dim 128 decode launch with shared-prefix cascade items first
 // (rows: the largest member count times G among them, at most kCascadeRows)
 hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,
@@ -148,7 +154,7 @@ hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, co
 // n_many) more, with at most many_rows rows each
 hipError_t launch_merge(const MergeArgs &a, int n_few, int n_many, int many_rows, hipStream_t s);
 constexpr int kMergeSerialParts = 16;
-hipError_t launch_append(const AppendArgs &a, bool fp8, int64_t num_tokens, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, int fmt, int64_t num_tokens, hipStream_t s);
 // measurement hooks (pa_peak.hip)
 constexpr int kPeakMfmaGroups = 256;   // one 512-thread work-group per CU
 constexpr int kPeakReadGroups = 256;   // streaming read: one 4-wave work-group per CU

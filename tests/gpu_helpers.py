@@ -13,9 +13,14 @@ from tests.parity import assert_lse, assert_parity  # noqa: F401  (the bars)
 def gpu_caches(batch, host=None):
     """Device caches holding the batch's history in the storage type.
     bf16: the generator's pools themselves.  e4m3: codes from the oracle's
-    encoder (the caller's quantised history), uploaded."""
+    encoder (the caller's quantised history), uploaded; mxfp4: the oracle
+    encoder's codes and scale bytes, uploaded."""
     if batch.spec.kv_dtype == "bf16":
         return batch.k_pool, batch.v_pool, None, None
+    if batch.spec.kv_dtype == "mxfp4":
+        kc, vc, ks, vs, _ = host if host is not None else host_caches(batch)
+        dev = batch.q.device
+        return tuple(torch.from_numpy(x).to(dev) for x in (kc, vc, ks, vs))
     kc, vc, ks, vs, _ = host if host is not None else host_caches(batch)
     dev = batch.q.device
     return (torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),

@@ -18,10 +18,16 @@ def host_caches(batch):
     """Host caches holding the batch's history, in the KV storage type.
 
     bf16: the pool bits.  e4m3: the history encoded by the oracle's codec with
-    the batch's scales (NaN slots become the NaN code)."""
+    the batch's scales (NaN slots become the NaN code).  mxfp4: the history
+    encoded by the oracle's MXFP4 encoder (unwritten slots, NaN in the pool,
+    get the NaN scale and zero codes)."""
     kb, vb = bits16(batch.k_pool), bits16(batch.v_pool)
     if batch.spec.kv_dtype == "bf16":
         return kb.copy(), vb.copy(), None, None, oracle.KV_BF16
+    if batch.spec.kv_dtype == "mxfp4":
+        kc, ks = oracle.mxfp4_quantize_pool(kb)
+        vc, vs = oracle.mxfp4_quantize_pool(vb)
+        return kc, vc, ks, vs, oracle.KV_MXFP4
     ks = batch.k_scale.detach().cpu().numpy().astype(np.float32)
     vs = batch.v_scale.detach().cpu().numpy().astype(np.float32)
     return oracle.quantize_pool(kb, ks), oracle.quantize_pool(vb, vs), ks, vs, oracle.KV_E4M3
@@ -58,6 +64,8 @@ def key_values(caches, bt_row, ctx):
     through the oracle's gather and its codecs (test-side bound computations)."""
     global _E4M3_LUT
     kc, _, ks, _, dt = caches
+    if dt == oracle.KV_MXFP4:
+        return oracle.gather_values(kc, ks, dt, bt_row, ctx)
     raw = oracle.gather(kc, bt_row, ctx)
     if dt == oracle.KV_BF16:
         return bf16_values(raw)

@@ -89,7 +89,7 @@ class Spec:
     block_size: int
     hist: List[int]
     incr: List[int]
-    kv_dtype: str = "bf16"           # "bf16" or "e4m3"
+    kv_dtype: str = "bf16"           # "bf16", "e4m3" or "mxfp4" (the pools hold bf16 values either way)
     shared_prefix_tokens: int = 0    # tokens shared (same physical blocks) by `shared_seqs`
     shared_seqs: List[int] = field(default_factory=list)
     spare_frac: float = 0.01         # extra unreferenced (poisoned) blocks in the pool
@@ -370,6 +370,14 @@ def long_context(hist: int = 1_044_480, incr: int = 4_096, decode_steps: int = 2
     return Spec("long_context", 5, 32, 8, 128, 64, [hist], [incr], kv_dtype="e4m3",
                 scale_tokens=[total], extra_blocks_per_seq=0)
 
+
+
+def long_context_mxfp4(hist: int = 1_044_480, incr: int = 4_096, decode_steps: int = 256) -> Spec:
+    """The 1M-token session with 4-bit KV: OCP MXFP4 (E2M1 codes, one E8M0
+    scale per 32 elements of a token and head), bs 64.  The scales are derived
+    from the values when they are encoded, so the spec carries none."""
+    return Spec("long_context_mxfp4", 5, 32, 8, 128, 64, [hist], [incr], kv_dtype="mxfp4",
+                scale_tokens=[hist + incr + decode_steps], extra_blocks_per_seq=0)
 
 
 def slot_of(batch: Batch, seq: int, pos: int) -> int:
