@@ -213,9 +213,14 @@ typedef struct {
  * the definition above, so the per-element work is a lookup). */
 static double e4m3_value[256];
 static int e4m3_value_ready = 0;
+/* Likewise the 16 E2M1 values and the 256 E8M0 scales (memos of
+ * orc_e2m1_to_double and orc_e8m0_to_double). */
+static double e2m1_value[16], e8m0_value[256];
 static void e4m3_table_init(void) {
   if (e4m3_value_ready) return;
   for (int i = 0; i < 256; i++) e4m3_value[i] = orc_e4m3_to_double((uint8_t)i);
+  for (int i = 0; i < 16; i++) e2m1_value[i] = orc_e2m1_to_double((uint8_t)i);
+  for (int i = 0; i < 256; i++) e8m0_value[i] = orc_e8m0_to_double((uint8_t)i);
   e4m3_value_ready = 1;
 }
 
@@ -231,7 +236,7 @@ static double cache_elem(const cache_view *c, const void *base, const void *scal
   uint8_t byte = ((const uint8_t *)base)[row * (c->d / 2) + dd / 2];
   uint8_t code = (dd & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
   uint8_t sb = ((const uint8_t *)scale)[((phys * c->hkv + kvh) * (c->d / 32) + dd / 32) * (int64_t)c->bs + off];
-  return orc_e2m1_to_double(code) * orc_e8m0_to_double(sb);
+  return e2m1_value[code] * e8m0_value[sb];
 }
 
 /* Encode one token's head vector x[d] into MXFP4 codes and scales at slot

@@ -397,6 +397,12 @@ __device__ __forceinline__ void wg_barrier() {
 // l, which the matrix cores accumulate from those same bf16 values, is kept
 // in units of the current step's value scale and rescaled by s_v(t)/s_v(t-1)
 // when the step changes (divided out at the end).
+// MXFP4 KV ([V41] kernels section: a 4-bit KV cache): a step's K and V codes
+// (64 bytes a key) and scale bytes reach a code ring the same way -- waves
+// 0-3 request the codes (16 key rows each), waves 4-7 the scale bytes (16
+// keys of K or V each) -- and the widening applies each 32-element group's
+// E8M0 scale in the conversion itself: the tiles then hold the values
+// exactly, and the rest is the bf16 path (no scale in the softmax).
 constexpr int kW48Step = 32;                        // keys per step
 // K (or V) of one 32-key step in LDS: 8 blocks of 4 key rows, each block
 // 1,024 bytes of data and 32 of padding (the layout is described at the
@@ -412,9 +418,19 @@ constexpr int kW48CodeBytes = kW48Step * 128;    // E4M3 codes of one step's K (
 constexpr int kW48ScaleSlots = 8;                // E4M3: steps held by the scale ring
 constexpr int kW48ScaleSlotBytes = 1024;         // K half 0, K half 1, V half 0, V half 1: 256 bytes each
 constexpr int kW48Fp8Lds = 4 * kW48TileBytes + kW48CodeStages * 2 * kW48CodeBytes + kW48ScaleSlots * kW48ScaleSlotBytes;
+constexpr int kW48Fp4CodeBytes = kW48Step * 64;  // MXFP4 codes of one step's K (or V)
+constexpr int kW48Fp4ScaleBytes = kW48Step * 4;  // MXFP4 scale bytes of one step's K (or V)
+// a code-ring stage: K codes, V codes, then the scale bytes as K keys 0-15,
+// K keys 16-31, V keys 0-15, V keys 16-31, each [group][16 keys]
+constexpr int kW48Fp4StageBytes = 2 * kW48Fp4CodeBytes + 2 * kW48Fp4ScaleBytes;
+constexpr int kW48Fp4Lds = 4 * kW48TileBytes + kW48CodeStages * kW48Fp4StageBytes;
 
-template <int BS, bool FP8>
+template <int BS, int FMT>
 __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u8 *smem) {
+  constexpr bool FP8 = FMT == kKvE4m3;
+  constexpr bool FP4 = FMT == kKvMxfp4;
+  constexpr bool CODED = FP8 || FP4;  // the tiles are widened from a code ring
+  constexpr int REQ = FP4 ? 1 : 2;    // requests per wave and step
   constexpr int D = 128;
   constexpr int NCQ = D / 32;  // k-steps of the score product
   constexpr int NDB = D / 16;  // d-blocks of the value product
@@ -513,8 +529,8 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // per-step vmcnt accounting.
   constexpr int LGBS = BS == 16 ? 4 : 6;
   static_assert(BS == 16 || BS == 64, "block size");
-  constexpr int ELEM = FP8 ? 1 : 2;
-  const uint32_t blk_bytes = (uint32_t)hkv * BS * D * ELEM;
+  constexpr int KEYB = FP4 ? D / 2 : FP8 ? D : 2 * D;  // bytes of one key row (K or V)
+  const uint32_t blk_bytes = (uint32_t)hkv * BS * KEYB;
   // bf16: this wave's requests fill block `wave` of the step's K and V tiles
   // (key rows 4*wave .. +3): lane l writes byte 16 l of the block, i.e. row
   // (l / 4) % 4, chunk 4 (l / 16) + l % 4.  E4M3: waves 0-3 request K codes,
@@ -522,30 +538,60 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // into the code ring, where row R's 16-byte chunk j sits at position
   // j ^ (4 ((R >> 1) & 1)) (so that the widening reads below are free of bank
   // conflicts): lane l fetches the chunk its LDS position holds.
-  const int voff = FP8 ? (lane >> 3) * 128 + 16 * ((lane & 7) ^ (((lane >> 4) & 1) << 2))
+  // MXFP4: waves 0-3 request the codes of key rows 16 (wave & 1) .. +15 of K
+  // (waves 0, 1) or V (2, 3), 1 KB as stored; waves 4-7 the scale bytes of
+  // those 16 keys of K (4, 5) or V (6, 7): lanes 0-15 fetch the dword of
+  // group lane / 4, keys 4 (lane % 4) .. +3.
+  const int voff = FP4 ? (wave < 4 ? 16 * lane : BS * (lane >> 2) + 4 * (lane & 3))
+                 : FP8 ? (lane >> 3) * 128 + 16 * ((lane & 7) ^ (((lane >> 4) & 1) << 2))
                        : ((lane >> 2) & 3) * 256 + (4 * (lane >> 4) + (lane & 3)) * 16;
   const int qw = wave & 3;
-  const unsigned char *mine = FP8 && wave >= 4 ? vc : kc;
-  const uint64_t kc_head = (uint64_t)(kc + (int64_t)kvh * BS * D * ELEM);
-  const uint64_t vc_head = (uint64_t)(vc + (int64_t)kvh * BS * D * ELEM);
-  const uint64_t my_head = (uint64_t)(mine + (int64_t)kvh * BS * D * ELEM);
-  int rpos = t_begin * kW48Step + (FP8 ? 8 * qw : 4 * wave);  // first key row of this wave's next request
+  const bool fp4_v = ((wave >> 1) & 1) != 0;  // MXFP4: this wave requests V (codes or scales)
+  const unsigned char *mine = FP4 ? (fp4_v ? vc : kc) : FP8 && wave >= 4 ? vc : kc;
+  const uint64_t kc_head = (uint64_t)(kc + (int64_t)kvh * BS * KEYB);
+  const uint64_t vc_head = (uint64_t)(vc + (int64_t)kvh * BS * KEYB);
+  const uint64_t my_head = (uint64_t)(mine + (int64_t)kvh * BS * KEYB);
+  // first key row of this wave's next request
+  int rpos = t_begin * kW48Step + (FP4 ? 16 * (wave & 1) : FP8 ? 8 * qw : 4 * wave);
   uint32_t st_off = 0;                                        // its ring stage, in bytes
   int blk_next = block_of(rpos);
-  constexpr int RING = FP8 ? 4 * TILEB : 0;  // E4M3: the code ring follows the four bf16 tiles
+  constexpr int RING = CODED ? 4 * TILEB : 0;  // the code ring follows the four bf16 tiles
   constexpr int SCB = RING + NCS * 2 * CB;   // E4M3: then the scale ring
   // E4M3: with its codes, each wave requests the scale of the block its rows
   // lie in (K waves the K scale, V waves the V scale) into the step's slot
   // of the scale ring (the 16-key half of its rows: (wave % 4) / 2); every
   // lane reads the same 4 bytes.  Two requests per wave and step.
   const uint64_t sc_head = (uint64_t)(FP8 && wave >= 4 ? a.c.vs : a.c.ks) + (uint64_t)kvh * 4;
+  // MXFP4 scale bytes of this wave's KV head: [block][hkv][group][BS]
+  const uint64_t sc4_head = (uint64_t)(fp4_v ? a.c.vs : a.c.ks) + (uint64_t)kvh * (D / 32) * BS;
+  const uint32_t sc4_blk = (uint32_t)hkv * (D / 32) * BS;
+  const uint32_t fp4_dst = wave < 4 ? (fp4_v ? kW48Fp4CodeBytes : 0) + (wave & 1) * 1024
+                                    : 2 * kW48Fp4CodeBytes + (2 * (fp4_v ? 1 : 0) + (wave & 1)) * 64;
   const uint32_t sc_lane0 = SCB + (wave >= 4 ? 512 : 0) + (qw >> 1) * 256;
   uint32_t sc_off = 0;
   const int zero = 0;
   auto issue = [&]() __attribute__((always_inline)) {
     const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(blk_next);
-    const uint64_t off = (uint64_t)blk * blk_bytes + (uint32_t)((rpos & (BS - 1)) * (D * ELEM));
-    if constexpr (FP8) {
+    const uint64_t off = (uint64_t)blk * blk_bytes + (uint32_t)((rpos & (BS - 1)) * KEYB);
+    if constexpr (FP4) {
+      const uint32_t dst = smem_addr + RING + st_off + fp4_dst;
+      if (wave < 4) {
+        const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 16) * KEYB);
+        const uint64_t ga = my_head + off;
+        const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ga),
+                           __builtin_amdgcn_readfirstlane((int)((ga >> 32) & 0xFFFF)), nrec, kRsrcFlags};
+        dma_load16(r, voff, dst);
+      } else {
+        // the block's scale bytes from its first key of the request on (keys
+        // past the range are made harmless by the widening)
+        const uint64_t sa = sc4_head + (uint64_t)blk * sc4_blk + (uint32_t)(rpos & (BS - 1));
+        const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)sa),
+                           __builtin_amdgcn_readfirstlane((int)((sa >> 32) & 0xFFFF)),
+                           (D / 32) * BS - (rpos & (BS - 1)), kRsrcFlags};
+        if (lane < 16) dma_load4(r, voff, dst);
+      }
+      st_off = st_off + kW48Fp4StageBytes == NCS * kW48Fp4StageBytes ? 0 : st_off + kW48Fp4StageBytes;
+    } else if constexpr (FP8) {
       const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 8) * D);
       const uint64_t ga = my_head + off;
       const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ga),
@@ -577,11 +623,11 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   static_assert((NST & (NST - 1)) == 0 && (NCS & (NCS - 1)) == 0, "ring stages: a power of two");
   // bf16 tiles of step t: the DMA ring (bf16) or the widened double buffers (E4M3)
   auto ktile = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8) return (const lds_u8 *)(smem + (t & 1) * TILEB);
+    if constexpr (CODED) return (const lds_u8 *)(smem + (t & 1) * TILEB);
     else return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB);
   };
   auto vtile = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8) return (const lds_u8 *)(smem + 2 * TILEB + (t & 1) * TILEB);
+    if constexpr (CODED) return (const lds_u8 *)(smem + 2 * TILEB + (t & 1) * TILEB);
     else return (const lds_u8 *)(smem + ((t - t_begin) % NST) * STAGEB + TILEB);
   };
   // E4M3 widening: wave w converts block w (key rows 4w .. 4w+3) of a step's
@@ -598,8 +644,33 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   auto widen_dst = [&](int t, bool v) __attribute__((always_inline)) {
     return smem + (v ? 2 * TILEB : 0) + (t & 1) * TILEB + w_wr;
   };
+  // MXFP4: the same lane takes the 4 code bytes of d 8q .. 8q+7 of row
+  // wrow (4 rows of 64 bytes per wave: 256 contiguous bytes) and the scale
+  // byte of group q / 4; a key past the range end (codes zero, its slot's
+  // scale byte possibly anything, NaN included) widens with scale 2^-127 so
+  // that its values are zeros.
+  const int f4_rd = wrow * 64 + 4 * wq;
+  const int f4_sc = 2 * kW48Fp4CodeBytes + (wrow >> 4) * 64 + (wq >> 2) * 16 + (wrow & 15);
+  auto f4_stage = [&](int t) __attribute__((always_inline)) {
+    return (const lds_u8 *)(smem + RING + ((t - t_begin) & (NCS - 1)) * kW48Fp4StageBytes);
+  };
+  auto f4_read = [&](int t, bool v, uint32_t &w, uint32_t &e) __attribute__((always_inline)) {
+    const lds_u8 *stg = f4_stage(t);
+    w = *(const __attribute__((address_space(3))) uint32_t *)(stg + (v ? kW48Fp4CodeBytes : 0) + f4_rd);
+    e = *(stg + f4_sc + (v ? 128 : 0));
+  };
+  auto f4_convert = [&](int t, uint32_t w, uint32_t e) __attribute__((always_inline)) {
+    const uint32_t es = t * kW48Step + wrow < kv_hi ? e : 0u;
+    return __builtin_bit_cast(uint4, fp4x8_to_bf16x8(w, e8m0_operand(es)));
+  };
   auto widen = [&](int t, bool v) __attribute__((always_inline)) {
-    lds_store16(widen_dst(t, v), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(lds_load8(widen_src(t, v)))));
+    if constexpr (FP4) {
+      uint32_t w, e;
+      f4_read(t, v, w, e);
+      lds_store16(widen_dst(t, v), f4_convert(t, w, e));
+    } else {
+      lds_store16(widen_dst(t, v), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(lds_load8(widen_src(t, v)))));
+    }
   };
 
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
@@ -810,15 +881,15 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
 
   // prologue.  bf16: NST-1 steps requested, step t0 waited.  E4M3: NCS steps
   // requested, t0 and t0+1 waited, then K(t0), V(t0), K(t0+1) widened.
-  if constexpr (FP8) {
+  if constexpr (CODED) {
 #pragma unroll
     for (int k = 0; k < NCS; k++) issue();
-    PA_WAIT_VMCNT(2 * (NCS - 2));
+    PA_WAIT_VMCNT(REQ * (NCS - 2));
     wg_barrier();
     widen(t_begin, false);
     widen(t_begin, true);
     widen(t_begin + 1, false);  // (past the range end: a tile nothing reads)
-    read_scales(t_begin);
+    if constexpr (FP8) read_scales(t_begin);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the widened tiles are written
     wg_barrier();
   } else {
@@ -838,8 +909,8 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // barrier of step t finds group 0 about to start its matrix-core phase and
   // group 1 its vector phase.
   auto open_step = [&]() __attribute__((always_inline)) {
-    if constexpr (FP8) {
-      PA_WAIT_VMCNT(2 * (NCS - 3));
+    if constexpr (CODED) {
+      PA_WAIT_VMCNT(REQ * (NCS - 3));
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's widened chunks are written
     } else {
       PA_WAIT_VMCNT(2 * (NST - 3));
@@ -850,14 +921,21 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // out first, the conversions and writes follow the softmax.  (Past the
   // range end these touch only tiles nothing reads: no branch needed.)
   uint2 wk = {}, wv = {};
+  uint32_t ek = 0, ev = 0;
   auto widen_read = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      f4_read(t + 2, false, wk.x, ek);
+      f4_read(t + 1, true, wv.x, ev);
+    } else if constexpr (FP8) {
       wk = lds_load8(widen_src(t + 2, false));
       wv = lds_load8(widen_src(t + 1, true));
     }
   };
   auto widen_write = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      lds_store16(widen_dst(t + 2, false), f4_convert(t + 2, wk.x, ek));
+      lds_store16(widen_dst(t + 1, true), f4_convert(t + 1, wv.x, ev));
+    } else if constexpr (FP8) {
       lds_store16(widen_dst(t + 2, false), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(wk)));
       lds_store16(widen_dst(t + 1, true), __builtin_bit_cast(uint4, e4m3x8_to_bf16x8_hw(wv)));
     }
@@ -948,15 +1026,15 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   }
 }
 
-template <int BS, bool FP8>
+template <int BS, int FMT>
 __global__ __launch_bounds__(512, 1) void prefill_w48_kernel(AttnArgs a) {
-  constexpr int RING = FP8 ? kW48Fp8Lds : kW48Stages * 2 * kW48TileBytes;
+  constexpr int RING = FMT == kKvE4m3 ? kW48Fp8Lds : FMT == kKvMxfp4 ? kW48Fp4Lds : kW48Stages * 2 * kW48TileBytes;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[RING];
   const int first = a.wg_first ? a.wg_first[blockIdx.x] : (int)blockIdx.x;
   const int last = a.wg_first ? a.wg_first[blockIdx.x + 1] : (int)blockIdx.x + 1;
   for (int i = first; i < last; i++) {
     if (i > first) __syncthreads();  // LDS of the previous item no longer read or written
-    w48_item<BS, FP8>(a, a.items[i], (lds_u8 *)smem_raw);
+    w48_item<BS, FMT>(a, a.items[i], (lds_u8 *)smem_raw);
   }
 }
 
@@ -2267,7 +2345,7 @@ template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (D == 128) {
     if (a.tile_rows == kW48TileRows) {
-      hipLaunchKernelGGL((prefill_w48_kernel<BS, FP8>), dim3(n), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((prefill_w48_kernel<BS, FP8 ? kKvE4m3 : kKvBf16>), dim3(n), dim3(512), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -2316,7 +2394,16 @@ static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
 
 hipError_t launch_prefill(const AttnArgs &a, int n, int d, int bs, int fmt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (fmt == kKvMxfp4) return hipErrorInvalidValue;
+  if (fmt == kKvMxfp4) {  // head_dim 128, the 384-row kernel only
+    if (d != 128 || a.tile_rows != kW48TileRows) return hipErrorInvalidValue;
+    if (bs == 16)
+      hipLaunchKernelGGL((prefill_w48_kernel<16, kKvMxfp4>), dim3(n), dim3(512), 0, s, a);
+    else if (bs == 64)
+      hipLaunchKernelGGL((prefill_w48_kernel<64, kKvMxfp4>), dim3(n), dim3(512), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const bool fp8 = fmt == kKvE4m3;
   PA_DISPATCH(launch_prefill_t, a, n, s);
 }

@@ -91,10 +91,10 @@ def plan_tiles(palib, spec):
     """(first row, tokens) of every prefill tile the library's planner makes
     for this step, from its work list (pa_debug_plan): the tile height is the
     kernel's, so boundary rows are sampled where tiles really meet."""
-    fp8 = spec.kv_dtype == "e4m3"
-    c = palib.pa_kv_cache(0x1000, 0x1000, 0x1000 if fp8 else None, 0x1000 if fp8 else None, 1,
-                          spec.num_kv_heads, spec.block_size, spec.head_dim,
-                          palib.PA_KV_FP8_E4M3 if fp8 else palib.PA_KV_BF16)
+    coded = spec.kv_dtype != "bf16"
+    kind = {"bf16": palib.PA_KV_BF16, "e4m3": palib.PA_KV_FP8_E4M3, "mxfp4": palib.PA_KV_MXFP4}[spec.kv_dtype]
+    c = palib.pa_kv_cache(0x1000, 0x1000, 0x1000 if coded else None, 0x1000 if coded else None, 1,
+                          spec.num_kv_heads, spec.block_size, spec.head_dim, kind)
     items, counts = palib.pa_debug_plan(spec.hist, spec.incr, spec.num_q_heads, c)
     pre = items[:counts[0]]
     return sorted({(int(r), int(n)) for r, n in zip(pre[:, 2], pre[:, 4])})

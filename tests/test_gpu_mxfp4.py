@@ -193,3 +193,54 @@ def test_long_context_decode(palib, needled):
     refd, _ = oracle.attention(bits16(q), kc, vc, ks, vs, dt, b.block_tables, [pos], [1], 32, spec.scale)
     ndd = [(0, b.decode_needles[1][0])] if 1 in b.decode_needles else []
     assert_parity(outd, refd, False, "long_context_mxfp4 decode step 1", needles=ndd)
+
+
+# ---------------------------------------------------------------------------
+# attention: prefill tiles (the 384-row kernel with MXFP4 widening), mixed steps
+PREFILL_CASES = {
+    "initial_bs16": _spec([0], [1000]),
+    "incremental_bs16": _spec([2000, 37], [700, 400]),
+    "incremental_bs64": _spec([4100], [900], bs=64),
+    "ragged_g8": _spec([333, 0], [150, 97], hq=32, hkv=4),
+    "g1": _spec([1200], [300], hq=8, hkv=8),
+    "g16_bs64": _spec([640], [130], hq=32, hkv=2, bs=64),
+    "mixed": _spec([5000, 900, 12_000, 0, 77], [600, 1, 1, 300, 1]),
+    "long_split": _spec([60_000], [400], bs=64),
+    "q_std3": _spec([3000], [500], q_std=3.0),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_prefill_parity(palib, name):
+    print(f"[case] mxfp4 prefill {name}", flush=True)
+    check_against_oracle(palib, PREFILL_CASES[name], what=f"mxfp4 prefill {name}")
+
+
+@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
+def test_long_context_prefill(palib, needled):
+    """The 4,096-token incremental prefill over the 1,044,480-token MXFP4
+    history (block 64): sampled rows at the planner's tile boundaries, the
+    cache after the quantising append byte for byte."""
+    from tests.test_gpu_fullsize import local_needles, plan_tiles, tile_boundary_rows
+    spec = W.long_context_mxfp4()
+    tiles = plan_tiles(palib, spec)
+    rows = tile_boundary_rows(tiles, 0, spec.incr[0], np.random.default_rng(4), k=2)
+    if needled:
+        spec = W.with_needles(spec, needles=[(0, r) for r in rows[::2]])
+    print(f"[case] long_context_mxfp4 prefill needled={needled} rows={rows}", flush=True)
+    b = W.make_batch(spec, DEV)
+    host = host_caches(b)
+    caches = gpu_caches(b, host)
+    c = palib.make_cache(*caches)
+    palib.kv_append(c, b.k_new, b.v_new, b.slot_mapping)
+    out, _ = forward(palib, b, c)
+    kc, vc, ks, vs, dt = host
+    oracle.kv_append(kc, vc, ks, vs, dt, bits16(b.k_new), bits16(b.v_new), b.slot_mapping.cpu().numpy())
+    torch.cuda.synchronize()
+    for g, h in zip(caches, (kc, vc, ks, vs)):
+        assert torch.equal(g.cpu(), torch.from_numpy(h))
+    t = time.time()
+    ref, _ = oracle.attention(bits16(b.q), kc, vc, ks, vs, dt, b.block_tables, b.hist, b.incr, 32, spec.scale,
+                              rows=rows)
+    print(f"[oracle] prefill rows in {time.time() - t:.1f}s", flush=True)
+    assert_parity(out[rows], ref, False, "long_context_mxfp4 prefill", needles=local_needles(b, rows))
