@@ -42,6 +42,11 @@ def prefill_flops(hist, incr, hq, d):
 
 
 def kv_bytes_per_token(spec):
+    """K and V bytes of one token, all KV heads: bf16 2 per element, E4M3 1
+    (its per-(block, head) scales are under 0.1%), MXFP4 half a byte plus
+    one scale byte per 32 elements."""
+    if spec.kv_dtype == "mxfp4":
+        return 2 * spec.num_kv_heads * (spec.head_dim // 2 + spec.head_dim // 32)
     elem = 1 if spec.kv_dtype == "e4m3" else 2
     return 2 * spec.num_kv_heads * spec.head_dim * elem
 
@@ -84,6 +89,24 @@ class Runner:
             b.k_pool = b.v_pool = None
             torch.cuda.empty_cache()
             self.cache = pa.make_cache(self.k_codes, self.v_codes, b.k_scale, b.v_scale)
+        elif spec.kv_dtype == "mxfp4":
+            # the history encoded by the library's own quantising kv_append,
+            # a block range at a time (unwritten slots, NaN in the pool, get
+            # the NaN scale and zero codes)
+            nb, hkv, bs, d = b.k_pool.shape
+            self.k_codes = torch.empty((nb, hkv, bs, d // 2), dtype=torch.uint8, device=dev)
+            self.v_codes = torch.empty_like(self.k_codes)
+            self.k_sc = torch.empty((nb, hkv, d // 32, bs), dtype=torch.uint8, device=dev)
+            self.v_sc = torch.empty_like(self.k_sc)
+            self.cache = pa.make_cache(self.k_codes, self.v_codes, self.k_sc, self.v_sc)
+            for i in range(0, nb, 4096):
+                j = min(nb, i + 4096)
+                kt = b.k_pool[i:j].permute(0, 2, 1, 3).reshape((j - i) * bs, hkv, d).contiguous()
+                vt = b.v_pool[i:j].permute(0, 2, 1, 3).reshape((j - i) * bs, hkv, d).contiguous()
+                pa.kv_append(self.cache, kt, vt, torch.arange(i * bs, j * bs, dtype=torch.int64, device=dev))
+            torch.cuda.synchronize()
+            b.k_pool = b.v_pool = None
+            torch.cuda.empty_cache()
         else:
             self.cache = pa.make_cache(b.k_pool, b.v_pool)
         self.bt = torch.from_numpy(b.block_tables).to(dev)
@@ -170,7 +193,8 @@ def report_prefill(pa, torch, spec, dev, steps, warmup, label, runner=None):
          "roofline": {"bound": "mfma", "achieved": round(fl / (k_ms * 1e-3) / 1e12, 2),
                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(fl / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                      "kernel": "prefill_w48_kernel<%d>" % spec.block_size}}
+                      "kernel": "prefill_w48_kernel<%d, %d>" % (
+                          spec.block_size, {"bf16": 0, "e4m3": 1, "mxfp4": 2}[spec.kv_dtype])}}
     if runner is None:
         del r
         torch.cuda.empty_cache()
@@ -242,8 +266,10 @@ def report_decode_steps(pa, torch, r, dev, label, nsteps=256, warmup=16):
             "roofline": {"bound": "hbm", "achieved": round(byts / (dk_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("decode_long_e4m3_bytes"),
-                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_fp8_kernel<64, 8, 2>"}}
+                         "traffic": measured_traffic(f"decode_long_{spec.kv_dtype}_bytes"),
+                         "algorithmic_bytes": int(byts),
+                         "kernel": {"e4m3": "decode_dma_fp8_kernel<64, 8, 2>",
+                                    "mxfp4": "decode_dma_fp4_kernel<64, 8, 2>"}.get(spec.kv_dtype)}}
 
 
 def report_decode(pa, torch, spec, dev, steps, warmup, label, kernel=None, traffic_key=None):
@@ -535,16 +561,23 @@ KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_attention.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_append.hip",
                   "paged_kv_cache_gqa_amd/csrc/pa_api.hip"]  # the planner sets the access order
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, false>(pa::AttnArgs)"
-PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, true>(pa::AttnArgs)"
+# (the prefill and append kernels' last template argument is the KV format:
+# 0 bf16, 1 E4M3, 2 MXFP4)
+PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, 0>(pa::AttnArgs)"
+PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, 1>(pa::AttnArgs)"
+PREFILL_FP4_KERNEL = "void pa::prefill_w48_kernel<64, 2>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
-APPEND_KERNEL = "void pa::append_kernel<false>(pa::AppendArgs)"
+DECODE_FP4_KERNEL = "void pa::decode_dma_fp4_kernel<64, 8, 2>(pa::AttnArgs)"
+APPEND_KERNEL = "void pa::append_kernel<0>(pa::AppendArgs)"
 # (--only workload, kernel, summary name, key in TRAFFIC_FILE)
 PROFILED = [("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k", "prefill_incremental_bytes"),
             ("incremental_128k", PREFILL_KERNEL, "incremental_131k_to_133.8k", "prefill_incremental_128k_bytes"),
             ("decode", DECODE_KERNEL, "decode_batch_64x142k", "decode_batch_bytes"),
             ("long_decode", DECODE_FP8_KERNEL, "decode_e4m3_context_1m", "decode_long_e4m3_bytes"),
+            ("long_decode_mxfp4", DECODE_FP4_KERNEL, "decode_mxfp4_context_1m", "decode_long_mxfp4_bytes"),
+            ("long_prefill", PREFILL_FP8_KERNEL, "prefill_e4m3_1m_plus_4096", "prefill_long_e4m3_bytes"),
+            ("long_prefill_mxfp4", PREFILL_FP4_KERNEL, "prefill_mxfp4_1m_plus_4096", "prefill_long_mxfp4_bytes"),
             ("kv_append_1m", APPEND_KERNEL, "kv_append_1m_bf16", "kv_append_1m_bytes"),
             ("mixed", PREFILL_KERNEL, "mixed_step_prefill_part", "prefill_mixed_bytes"),
             ("mixed", DECODE_KERNEL, "mixed_step_decode_part", "decode_mixed_bytes")]
@@ -554,7 +587,9 @@ def only_spec(W, name):
     """The workload of bench.py --only NAME."""
     return {"incremental": lambda: W.incremental(), "decode": lambda: W.decode_batch(),
             "incremental_128k": lambda: W.incremental(131_072, 2_700, "incremental_128k"),
-            "long_decode": lambda: W.long_context(1_048_575, 1), "mixed": lambda: W.mixed()}[name]()
+            "long_decode": lambda: W.long_context(1_048_575, 1), "mixed": lambda: W.mixed(),
+            "long_decode_mxfp4": lambda: W.long_context_mxfp4(1_048_575, 1),
+            "long_prefill": lambda: W.long_context(), "long_prefill_mxfp4": lambda: W.long_context_mxfp4()}[name]()
 
 
 def algorithmic_work(W, name, kernel=None):
@@ -566,7 +601,7 @@ def algorithmic_work(W, name, kernel=None):
         fl, dfl, byts = mixed_parts(spec)
         return (dfl, byts) if kernel == DECODE_KERNEL else (fl, 0)
     fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
-    return fl, decode_bytes(spec) if name in ("decode", "long_decode") else prefill_bytes(spec)
+    return fl, decode_bytes(spec) if name in ("decode", "long_decode", "long_decode_mxfp4") else prefill_bytes(spec)
 
 
 def kernel_source_hash():
@@ -746,7 +781,7 @@ def main():
                     help="skip the measured MFMA and HBM-read ceilings")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m",
-                                       "mixed"],
+                                       "mixed", "long_decode_mxfp4", "long_prefill", "long_prefill_mxfp4"],
                     help="run one workload (for profiling); prints its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (HBM counter calibration)")
@@ -817,7 +852,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill_incremental_bytes"),
-                     "kernel": "prefill_w48_kernel<16, false>",
+                     "kernel": "prefill_w48_kernel<16, 0>",
                      "kernel_ms": round(k_ms, 4)},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
     }
@@ -863,7 +898,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pfl / (pk_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_incremental_128k_bytes"),
-                         "kernel": "prefill_w48_kernel<16, false>", "kernel_ms": round(pk_ms, 4)},
+                         "kernel": "prefill_w48_kernel<16, 0>", "kernel_ms": round(pk_ms, 4)},
         }
         del r
         torch.cuda.empty_cache()
@@ -896,6 +931,17 @@ def main():
             "long_context: the 256 decode steps after the prefill (contexts 1,048,577 to "
             "1,048,832), each appending one token, E4M3 KV, block 64")
         del lr
+        torch.cuda.empty_cache()
+        fspec = W.long_context_mxfp4()
+        fr = Runner(pa, torch, fspec, dev)
+        rep["long_context_prefill_mxfp4"] = report_prefill(
+            pa, torch, fspec, dev, max(3, args.steps // 4), rw,
+            "the same session with 4-bit KV: OCP MXFP4 (E2M1 codes, one E8M0 scale per 32 elements "
+            "of a token and head), block 64", runner=fr)
+        rep["long_context_decode_mxfp4"] = report_decode_steps(
+            pa, torch, fr, dev,
+            "the 256 decode steps after that prefill, MXFP4 KV, block 64")
+        del fr
         torch.cuda.empty_cache()
         rep["kv_append_45700"] = report_append(pa, torch, dev, 45_700, 20,
                                                "kv_append of 45,700 bf16 tokens (initial prefill)")

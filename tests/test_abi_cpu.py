@@ -380,3 +380,30 @@ def test_noalloc_rejects_steps_beyond_its_scratch(palib):
                                            n.ctypes.data_as(C.c_void_p), 512, 32, 0.088, FAKE, None, None)
     assert st == pa.PA_ERR_WORKSPACE_TOO_SMALL
     assert "scratch" in pa.pa_last_error()
+
+
+def test_mxfp4_cache_checks(palib):
+    """MXFP4 descriptors: head_dim 128 only, both scale arrays required; the
+    binding tells MXFP4 from E4M3 by the scales' dtype and shape."""
+    import torch
+    pa = palib
+    mx = pa.PA_KV_MXFP4
+    assert pa.lib.kv_append(C.byref(cache(pa, dtype=mx, k_scale=FAKE, v_scale=FAKE, head_dim=64)),
+                            FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert pa.lib.kv_append(C.byref(cache(pa, dtype=mx, k_scale=None, v_scale=FAKE)),
+                            FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_NULL_ARG
+    assert pa.lib.kv_append(C.byref(cache(pa, dtype=mx, k_scale=FAKE, v_scale=FAKE)),
+                            None, None, None, 0, None) == pa.PA_OK
+    assert pa.lib.kv_append(C.byref(cache(pa, dtype=3, k_scale=FAKE, v_scale=FAKE)),
+                            FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    codes = torch.zeros((4, 2, 16, 64), dtype=torch.uint8)   # head_dim 128, two codes a byte
+    sc = torch.zeros((4, 2, 4, 16), dtype=torch.uint8)       # [nb][hkv][d/32][bs]
+    _expect_bad(pa, lambda: pa.make_cache(codes, codes, sc, sc[:, :, :3]), "shape")
+    _expect_bad(pa, lambda: pa.make_cache(codes, codes, sc, torch.zeros((4, 2, 4, 16), dtype=torch.int8)), "dtype")
+    _expect_bad(pa, lambda: pa.make_cache(codes, codes, sc.transpose(2, 3).contiguous(), sc), "shape")
+    _expect_bad(pa, lambda: pa.make_cache(codes, codes, sc, sc), "GPU tensor")
+    # the planner sizes an MXFP4 step like a bf16 one (same tiles and partials)
+    hist, incr = np.array([5000, 100], np.int32), np.array([700, 1], np.int32)
+    bf = pa.pa_workspace_size(hist, incr, 32, cache(pa))
+    f4 = pa.pa_workspace_size(hist, incr, 32, cache(pa, dtype=mx, k_scale=FAKE, v_scale=FAKE))
+    assert bf == f4 > 0
