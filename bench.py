@@ -128,8 +128,20 @@ class Runner:
         self.ws = self.torch.empty(need, dtype=self.torch.uint8, device=self.ws.device)
         self.cascade = True
 
+    def use_one_launch(self):
+        """Run steps through paged_attn_step (kv_append and the attention in
+        one persistent launch)."""
+        spec, b, pa = self.spec, self.b, self.pa
+        need = pa.step_workspace_size(b.hist, b.incr, spec.num_q_heads, self.cache, self.bt, spec.scale)
+        self.ws = self.torch.empty(need, dtype=self.torch.uint8, device=self.ws.device)
+        self.one_launch = True
+
     def step(self):
         b, pa = self.b, self.pa
+        if getattr(self, "one_launch", False):
+            pa.paged_attn_step(self.cache, b.k_new, b.v_new, self.slots, b.q, self.bt, b.hist, b.incr,
+                               self.spec.scale, self.out, self.ws, stream=self.stream)
+            return
         pa.kv_append(self.cache, b.k_new, b.v_new, self.slots, stream=self.stream)
         if getattr(self, "cascade", False):
             pa.paged_attn_forward_cascade(b.q, self.cache, self.bt, b.hist, b.incr, self.spec.scale,
@@ -170,7 +182,7 @@ class Runner:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         kern = {}
-        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge")):
+        for kind, name in ((0, "kv_append"), (1, "prefill"), (2, "decode"), (3, "merge"), (4, "step")):
             tot, cnt = pa.pa_timing_read(kind)
             if cnt:
                 kern[name] = (tot / cnt, cnt / steps)   # avg ms per launch, launches per step
@@ -305,6 +317,19 @@ def mixed_parts(spec):
     uniq = sum(spec.hist[i] + 1 for i in dec) - max(0, len(shared) - 1) * spec.shared_prefix_tokens
     byts = uniq * kvb + 2 * len(dec) * spec.num_q_heads * spec.head_dim * 2
     return fl, dfl, byts
+
+
+def report_mixed_one_launch(pa, torch, spec, dev, steps, warmup, label):
+    """The mixed step through paged_attn_step: one persistent launch (after
+    the work-list copy) for the append, both attention parts and the merges."""
+    r = Runner(pa, torch, spec, dev)
+    r.use_one_launch()
+    ms, kern = r.timed(steps, warmup)
+    fl, dfl, byts = mixed_parts(spec)
+    k_ms = kern["step"][0] * kern["step"][1]
+    return {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
+            "step_kernel_ms": round(k_ms, 4),
+            "note": "prefill and decode parts share the launch: no per-part rates"}
 
 
 def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False):
@@ -920,6 +945,10 @@ def main():
             pa, torch, W.mixed(), dev, rs, rw,
             "the same mixed step through paged_attn_forward_cascade, the 8 sub-agents declared as a "
             "group over their shared 10,000 tokens", cascade=True)
+        rep["mixed_step_one_launch"] = report_mixed_one_launch(
+            pa, torch, W.mixed(), dev, rs, rw,
+            "the same mixed step through paged_attn_step: kv_append, both attention parts and the merges "
+            "in one persistent launch with device-side task claiming")
         lspec = W.long_context()
         lr = Runner(pa, torch, lspec, dev)
         rep["long_context_prefill_e4m3"] = report_prefill(

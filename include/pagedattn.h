@@ -251,12 +251,52 @@ PA_API const char *pa_last_error(void);
 PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_row, int32_t ctx,
                           void *k_out, void *v_out, void *stream);
 
+/*
+ * paged_attn_step -- kv_append and paged_attn_forward of one step in ONE
+ * kernel launch (after the work-list copy).
+ *
+ * [Agentic] §5.1-§5.2: a decode layer runs as persistent kernels, one block
+ * per SM, whose stages are task tables the blocks claim by index, and the KV
+ * write precedes the attention that reads it.  Here one work-group per
+ * compute unit claims, with device-scope atomics on counters in the
+ * workspace: the append of the step's new tokens in chunks, then (once every
+ * append chunk has finished) the prefill work of the persistent plan from
+ * its own XCD's queue, then the decode items; a split tile's partials are
+ * merged by the work-group that writes its last part (no merge launch).
+ *
+ * Arguments are those of kv_append followed by those of paged_attn_forward,
+ * with num_tokens = total_q: k_new, v_new [total_q][num_kv_heads][head_dim]
+ * and slot_mapping [total_q] are the new tokens of the query rows, in the
+ * same order.  The results equal kv_append followed by paged_attn_forward's
+ * within the attention tolerance (the decode items run with eight waves and
+ * the merge sums in another order, so the bits may differ).
+ *   workspace       NULL: *workspace_bytes is set to the bytes this step
+ *                   needs (nothing else happens); otherwise at least that
+ *                   many bytes, 256-byte aligned, contents need no
+ *                   initialisation.
+ * Supported: bf16 KV with head_dim 128 (PA_ERR_UNSUPPORTED otherwise).
+ */
+PA_API pa_status paged_attn_step(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                                 const int64_t *slot_mapping, const void *q, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *hist_lens, const int32_t *incr_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, float scale, void *out, float *lse_out,
+                                 void *workspace, size_t *workspace_bytes, void *stream);
+
+/* Test hook: after a paged_attn_step on `workspace` (same lengths), copies
+ * its flag word to HOST *flags_out and synchronises `stream`.  Bit 0 set
+ * means a bounded device-side wait gave up (never expected; the step's
+ * results are then not to be trusted). */
+PA_API pa_status pa_debug_step_flags(const void *workspace, const pa_kv_cache *cache, const int32_t *hist_lens,
+                                     const int32_t *incr_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     uint32_t *flags_out, void *stream);
+
 /* Per-kernel timing for measurement.  When enabled (nonzero), each launch
  * records HIP events on the call's stream around the kernel; the durations
  * accumulate until read.  pa_timing_read(kind, &ms, &count) returns, for
  * kind 0 = kv_append, 1 = prefill attention, 2 = decode attention
  * (holding the shared-prefix cascade items of paged_attn_forward_cascade,
- * which run in the same launch), 3 = LSE merge, the summed
+ * which run in the same launch), 3 = LSE merge, 4 = the one launch of
+ * paged_attn_step, the summed
  * milliseconds and launch count since the last reset (it synchronises on the
  * recorded events), then resets that kind. */
 PA_API pa_status pa_timing_enable(int enable);

@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK, PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = 4, 5
 PA_KV_BF16, PA_KV_FP8_E4M3, PA_KV_MXFP4 = 0, 1, 2
-TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE = 0, 1, 2, 3
-TIMING_KINDS = 4
+TIMING_APPEND, TIMING_PREFILL, TIMING_DECODE, TIMING_MERGE, TIMING_STEP = 0, 1, 2, 3, 4
+TIMING_KINDS = 5
 
 # Every symbol the header declares.
 EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_error",
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
            "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read", "pa_device_shape",
-           "pa_debug_xcc_ids", "paged_attn_forward_noalloc", "paged_attn_forward_cascade")
+           "pa_debug_xcc_ids", "paged_attn_forward_noalloc", "paged_attn_forward_cascade",
+           "paged_attn_step", "pa_debug_step_flags")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
@@ -67,7 +68,10 @@ def _load():
     L.paged_attn_forward_noalloc.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P]
     L.paged_attn_forward_cascade.argtypes = [P, pc, P, i32, P, P, i32, i32, C.c_float, P, P, P, P, i32, P,
                                              C.POINTER(sz), P]
-    for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "paged_attn_forward_cascade", "pa_debug_gather", "pa_timing_enable",
+    L.paged_attn_step.argtypes = [pc, P, P, P, P, P, i32, P, P, i32, i32, C.c_float, P, P, P, C.POINTER(sz), P]
+    L.pa_debug_step_flags.argtypes = [P, pc, P, P, i32, i32, C.POINTER(C.c_uint32), P]
+    for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "paged_attn_forward_cascade",
+              "paged_attn_step", "pa_debug_step_flags", "pa_debug_gather", "pa_timing_enable",
               "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
               "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids"):
         getattr(L, f).restype = C.c_int
@@ -259,6 +263,59 @@ def cascade_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache
         n.ctypes.data_as(C.c_void_p), len(h), int(num_q_heads), float(scale), None, None,
         go.ctypes.data_as(C.c_void_p), gl.ctypes.data_as(C.c_void_p), len(gl), None, C.byref(need), None))
     return int(need.value)
+
+
+def step_workspace_size(hist_lens, incr_lens, num_q_heads, cache: pa_kv_cache, block_tables, scale) -> int:
+    """Workspace bytes paged_attn_step needs for this step."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    need = C.c_size_t(0)
+    _check(lib.paged_attn_step(C.byref(cache), None, None, None, None, None, int(block_tables.shape[1]),
+                               h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h),
+                               int(num_q_heads), float(scale), None, None, None, C.byref(need), None))
+    return int(need.value)
+
+
+def paged_attn_step(cache: pa_kv_cache, k_new, v_new, slot_mapping, q, block_tables, hist_lens, incr_lens,
+                    scale, out, workspace, lse_out=None, stream=None):
+    """kv_append of the step's new tokens and paged_attn_forward in one launch."""
+    import torch
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    if h.shape != n.shape or h.ndim != 1:
+        _bad("hist_lens and incr_lens must be 1-D of equal length")
+    dev = getattr(cache, "device", None)
+    total_q = int(n.astype(np.int64).sum())
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        _bad("q must be a 3-D tensor [total_q, num_q_heads, head_dim]")
+    hq = int(q.shape[1])
+    kv_shape = (total_q, cache.num_kv_heads, cache.head_dim)
+    ok = [_tensor(q, "q", _bf16(), (total_q, hq, cache.head_dim)),
+          _tensor(out, "out", _bf16(), (total_q, hq, cache.head_dim)),
+          _tensor(k_new, "k_new", _bf16(), kv_shape), _tensor(v_new, "v_new", _bf16(), kv_shape),
+          _tensor(slot_mapping, "slot_mapping", (torch.int64,), (total_q,))]
+    if lse_out is not None:
+        ok.append(_tensor(lse_out, "lse_out", (torch.float32,), (total_q, hq)))
+    ok.append(_tensor(block_tables, "block_tables", (torch.int32,), (None, None)))
+    if int(block_tables.shape[0]) < len(h):
+        _bad(f"block_tables has {int(block_tables.shape[0])} rows for {len(h)} sequences")
+    if not isinstance(workspace, torch.Tensor):
+        _bad("workspace must be a torch.Tensor")
+    ok.append(_tensor(workspace, "workspace", (workspace.dtype,)))
+    _on_device(ok, dev)
+    cap = C.c_size_t(int(workspace.numel() * workspace.element_size()))
+    _check(lib.paged_attn_step(
+        C.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(block_tables),
+        int(block_tables.shape[1]), h.ctypes.data_as(C.c_void_p), n.ctypes.data_as(C.c_void_p), len(h), hq,
+        float(scale), _ptr(out), _ptr(lse_out), _ptr(workspace), C.byref(cap), _stream_ptr(stream)))
+
+
+def pa_debug_step_flags(workspace, cache: pa_kv_cache, hist_lens, incr_lens, num_q_heads, stream=None) -> int:
+    """Flag word of the last paged_attn_step on `workspace` (bit 0: a bounded wait gave up)."""
+    h, n = _host_i32(hist_lens), _host_i32(incr_lens)
+    f = C.c_uint32(0)
+    _check(lib.pa_debug_step_flags(_ptr(workspace), C.byref(cache), h.ctypes.data_as(C.c_void_p),
+                                   n.ctypes.data_as(C.c_void_p), len(h), int(num_q_heads), C.byref(f),
+                                   _stream_ptr(stream)))
+    return int(f.value)
 
 
 def paged_attn_forward_cascade(q, cache: pa_kv_cache, block_tables, hist_lens, incr_lens, scale, out,

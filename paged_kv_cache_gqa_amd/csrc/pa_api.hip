@@ -139,8 +139,13 @@ struct Plan {
   std::vector<CascadeItem> cascade;
   std::vector<CascadeMember> members;
   int32_t cascade_rows = 0;
+  // one-launch step: prefill ranges per XCD queue, the merge record of
+  // each partial slot, the task counters
+  std::vector<int32_t> step_queue, step_queue_off, step_pre_merge, step_dec_merge;
+  int32_t step_xcds = 1, step_ranges = 0;
+  size_t n_ctr = 0;
   size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, off_cascade = 0, off_members = 0,
-         plan_bytes = 0;
+         off_sq = 0, off_sqo = 0, off_spm = 0, off_sdm = 0, off_ctr = 0, plan_bytes = 0;
   size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
 };
 
@@ -158,6 +163,22 @@ struct Groups {
   const int32_t *group_of = nullptr;
   const int32_t *group_len = nullptr;
   int32_t num_groups = 0;
+};
+
+// Prefill ranges per compute unit in the one-launch step's plan (more,
+// shorter ranges let work-groups that finish early take more of them; with
+// ranges of equal length that gained nothing: 4 per CU measured 12.6 ms
+// against 12.3 ms for the mixed step, the extra partials and merges costing
+// more than the balance won).
+#ifndef PA_STEP_RANGES_PER_CU
+#define PA_STEP_RANGES_PER_CU 1
+#endif
+constexpr int32_t kStepRangesPerCu = PA_STEP_RANGES_PER_CU;
+
+// The step's new tokens for the one-launch step (paged_attn_step).
+struct StepIn {
+  const void *k_new = nullptr, *v_new = nullptr;
+  const int64_t *slots = nullptr;
 };
 
 // Balanced cut of [0, keys) into n ranges whose inner boundaries are
@@ -206,7 +227,7 @@ constexpr int kGroupPieces = PA_GROUP_PIECES;
 constexpr bool kPlanLpt = PA_PLAN_LPT;
 
 void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_rows, const MachineShape &M,
-                     Plan &P) {
+                     Plan &P, int32_t ranges_per_cu = 1) {
   std::vector<int32_t> pre;  // prefill tiles
   int32_t max_steps = 0;
   int64_t W = 0;
@@ -218,7 +239,8 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
     W += (int64_t)steps * hkv;
   }
   if (W == 0) return;
-  const int32_t nwg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(M.cus, W / kMinGroupKeyTiles));
+  const int32_t nwg =
+      (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)M.cus * ranges_per_cu, W / kMinGroupKeyTiles));
   // chunk length (in steps) so that a work-group's range spans about
   // kGroupPieces (tile, chunk) pieces
   const int64_t units = (int64_t)pre.size() * hkv;
@@ -309,7 +331,7 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
 }
 
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const pa_kv_cache *c,
-               int32_t group, Plan &P, const Groups *groups = nullptr) {
+               int32_t group, Plan &P, const Groups *groups = nullptr, bool step = false) {
   const int32_t hkv = c->num_kv_heads, d = c->head_dim, tile_rows = prefill_tile_rows(c);
   const MachineShape M = machine_shape();
   const int64_t decode_target_items = (int64_t)kDecodeItemsPerCU * M.cus;
@@ -368,7 +390,7 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
 
   const bool persistent = tile_rows == kDmaTileRows;
   if (persistent)
-    plan_persistent(tiles, hkv, tile_rows, M, P);
+    plan_persistent(tiles, hkv, tile_rows, M, P, step ? kStepRangesPerCu : 1);
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
   // cascade members: the first partial slot of tile i's KV head kvh (its
@@ -447,6 +469,30 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
   std::stable_partition(P.merges.begin(), P.merges.end(),
                         [](const Merge &m) { return m.nparts <= kMergeSerialParts; });
 
+  if (step) {
+    // prefill ranges: the persistent plan's work-group ranges (or one item
+    // each); range w was cut for XCD w % xcds, so XCD x's queue holds the
+    // ranges w = x, x + xcds, ...
+    if (P.wg_first.empty() && !P.prefill.empty())
+      for (int32_t i = 0; i <= (int32_t)P.prefill.size(); i++) P.wg_first.push_back(i);
+    P.step_ranges = P.wg_first.empty() ? 0 : (int32_t)P.wg_first.size() - 1;
+    const int32_t xq = std::min(M.xcds, kMaxXcds);
+    P.step_xcds = P.step_ranges > 0 && P.step_ranges % xq == 0 ? xq : 1;
+    P.step_queue_off.assign(kMaxXcds + 1, 0);
+    for (int32_t x = 0; x < P.step_xcds; x++) {
+      P.step_queue_off[x] = (int32_t)P.step_queue.size();
+      for (int32_t w = x; w < P.step_ranges; w += P.step_xcds) P.step_queue.push_back(w);
+    }
+    for (int32_t x = P.step_xcds; x <= kMaxXcds; x++) P.step_queue_off[x] = (int32_t)P.step_queue.size();
+    P.step_pre_merge.assign((size_t)P.n_part_prefill, -1);
+    P.step_dec_merge.assign((size_t)P.n_part_decode, -1);
+    for (size_t m = 0; m < P.merges.size(); m++) {
+      auto &v = P.merges[m].is_decode ? P.step_dec_merge : P.step_pre_merge;
+      for (int32_t i = 0; i < P.merges[m].nparts; i++) v[(size_t)P.merges[m].part0 + i] = (int32_t)m;
+    }
+    P.n_ctr = (size_t)kCtrMerge + P.merges.size();
+  }
+
   size_t off = 0;
   P.off_prefill = off;
   off = align256(off + P.prefill.size() * sizeof(Item));
@@ -460,6 +506,16 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
   off = align256(off + P.cascade.size() * sizeof(CascadeItem));
   P.off_members = off;
   off = align256(off + P.members.size() * sizeof(CascadeMember));
+  P.off_sq = off;
+  off = align256(off + P.step_queue.size() * sizeof(int32_t));
+  P.off_sqo = off;
+  off = align256(off + P.step_queue_off.size() * sizeof(int32_t));
+  P.off_spm = off;
+  off = align256(off + P.step_pre_merge.size() * sizeof(int32_t));
+  P.off_sdm = off;
+  off = align256(off + P.step_dec_merge.size() * sizeof(int32_t));
+  P.off_ctr = off;
+  off = align256(off + P.n_ctr * sizeof(uint32_t));  // zeros in the staged copy
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -603,7 +659,7 @@ pa_status scratch_address(unsigned char **out) {
 
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
-constexpr int kKinds = 4;
+constexpr int kKinds = 5;
 std::mutex g_time_mu;
 bool g_timing = false;
 struct TimedLaunch {
@@ -742,7 +798,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
                   int32_t max_blocks_per_seq, const int32_t *hist_lens, const int32_t *incr_lens,
                   int32_t num_seqs, int32_t num_q_heads, float scale, void *out, float *lse_out,
                   void *workspace, size_t workspace_bytes, void *stream, bool no_alloc,
-                  const Groups *groups = nullptr, size_t *size_query = nullptr) {
+                  const Groups *groups = nullptr, size_t *size_query = nullptr, const StepIn *step = nullptr) {
   pa_status st = check_cache(cache);
   if (st) return st;
   if (max_blocks_per_seq < 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq < 0");
@@ -764,17 +820,23 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
       if (groups->group_of[s] < -1 || groups->group_of[s] >= groups->num_groups)
         return fail(PA_ERR_BAD_SHAPE, "sequence %d: group %d out of range", s, groups->group_of[s]);
   }
+  if (step && (cache->dtype != PA_KV_BF16 || cache->head_dim != 128))
+    return fail(PA_ERR_UNSUPPORTED, "the one-launch step takes bf16 KV with head_dim 128");
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
   if (size_query) {
-    make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups);
+    make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups, step != nullptr);
     *size_query = std::max<size_t>(P.total, 256);
     return PA_OK;
   }
   if (total_q == 0) return PA_OK;
   if (!q || !out || !block_tables) return fail(PA_ERR_NULL_ARG, "q/out/block_tables is NULL");
-  make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups);
+  if (step && (!step->k_new || !step->v_new || !step->slots))
+    return fail(PA_ERR_NULL_ARG, "k_new/v_new/slot_mapping is NULL");
+  if (step && total_q * hkv * (d / 8) >= ((int64_t)1 << 31))
+    return fail(PA_ERR_BAD_SHAPE, "too many new tokens for one step (%lld)", (long long)total_q);
+  make_plan(hist_lens, incr_lens, num_seqs, cache, group, P, groups, step != nullptr);
   if (no_alloc) {
     if (P.total > (size_t)PA_NOALLOC_SCRATCH_BYTES)
       return fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -803,6 +865,13 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     memcpy(host.data() + P.off_cascade, P.cascade.data(), P.cascade.size() * sizeof(CascadeItem));
     memcpy(host.data() + P.off_members, P.members.data(), P.members.size() * sizeof(CascadeMember));
   }
+  auto put = [&](size_t off, const std::vector<int32_t> &v) {
+    if (!v.empty()) memcpy(host.data() + off, v.data(), v.size() * sizeof(int32_t));
+  };
+  put(P.off_sq, P.step_queue);
+  put(P.off_sqo, P.step_queue_off);
+  put(P.off_spm, P.step_pre_merge);
+  put(P.off_sdm, P.step_dec_merge);  // (the counters stay zero)
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   if (no_alloc) {
@@ -832,6 +901,56 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   const int fmt = (int)cache->dtype;
   const int bs = cache->block_size;
   hipError_t e;
+  MergeArgs m{};
+  m.merges = (const Merge *)(ws + P.off_merges);
+  m.part_o_prefill = (const float *)(ws + P.off_po_pre);
+  m.part_lse_prefill = (const float *)(ws + P.off_pl_pre);
+  m.part_o_decode = (const float *)(ws + P.off_po_dec);
+  m.part_lse_decode = (const float *)(ws + P.off_pl_dec);
+  m.out = out;
+  m.lse_out = lse_out;
+  m.hq = num_q_heads;
+  m.group = group;
+  m.lg = a.lg;
+  m.d = d;
+  if (step) {
+    StepArgs sa{};
+    sa.pre = a;
+    sa.pre.items = (const Item *)(ws + P.off_prefill);
+    sa.pre.part_o = (float *)(ws + P.off_po_pre);
+    sa.pre.part_lse = (float *)(ws + P.off_pl_pre);
+    sa.dec = a;
+    sa.dec.items = (const Item *)(ws + P.off_decode);
+    sa.dec.part_o = (float *)(ws + P.off_po_dec);
+    sa.dec.part_lse = (float *)(ws + P.off_pl_dec);
+    sa.app.k_new = step->k_new;
+    sa.app.v_new = step->v_new;
+    sa.app.slots = step->slots;
+    sa.app.k_cache = cache->k_cache;
+    sa.app.v_cache = cache->v_cache;
+    sa.app.hkv = hkv;
+    sa.app.bs = bs;
+    sa.app.lbs = bs == 16 ? 4 : 6;
+    sa.app.d = d;
+    sa.app.lcpr = d == 64 ? 3 : 4;
+    sa.app.tok0 = 0;
+    sa.app.nchunks = (uint32_t)(total_q * hkv * (d / 8));
+    sa.mg = m;
+    sa.wg_first = (const int32_t *)(ws + P.off_wg);
+    sa.pre_queue = (const int32_t *)(ws + P.off_sq);
+    sa.pre_queue_off = (const int32_t *)(ws + P.off_sqo);
+    sa.pre_part_merge = (const int32_t *)(ws + P.off_spm);
+    sa.dec_part_merge = (const int32_t *)(ws + P.off_sdm);
+    sa.ctr = (uint32_t *)(ws + P.off_ctr);
+    sa.n_append_tasks = (int32_t)((sa.app.nchunks + kStepAppendChunks - 1) / kStepAppendChunks);
+    sa.n_decode = (int32_t)P.decode.size();
+    sa.xcds = P.step_xcds;
+    const int64_t tasks = (int64_t)sa.n_append_tasks + P.step_ranges + sa.n_decode;
+    const int groups_n = (int)std::max<int64_t>(1, std::min<int64_t>(machine_shape().cus, tasks));
+    e = timed(4, s, [&] { return launch_step(sa, groups_n, bs, s); });
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    return PA_OK;
+  }
   if (!P.prefill.empty()) {
     AttnArgs ap = a;
     ap.items = (const Item *)(ws + P.off_prefill);
@@ -863,18 +982,6 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     if (e != hipSuccess) return hip_fail(e, "decode attention launch");
   }
   if (!P.merges.empty()) {
-    MergeArgs m{};
-    m.merges = (const Merge *)(ws + P.off_merges);
-    m.part_o_prefill = (const float *)(ws + P.off_po_pre);
-    m.part_lse_prefill = (const float *)(ws + P.off_pl_pre);
-    m.part_o_decode = (const float *)(ws + P.off_po_dec);
-    m.part_lse_decode = (const float *)(ws + P.off_pl_dec);
-    m.out = out;
-    m.lse_out = lse_out;
-    m.hq = num_q_heads;
-    m.group = group;
-    m.lg = a.lg;
-    m.d = d;
     int n_few = 0, many_rows = 0;
     for (const Merge &mg : P.merges) {
       if (mg.nparts <= kMergeSerialParts) n_few++;
@@ -916,6 +1023,39 @@ pa_status paged_attn_forward_cascade(const void *q, const pa_kv_cache *cache,
   return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs,
                  num_q_heads, scale, out, lse_out, workspace, *workspace_bytes, stream, false, &g,
                  workspace ? nullptr : workspace_bytes);
+}
+
+pa_status paged_attn_step(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                          const int64_t *slot_mapping, const void *q, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *hist_lens, const int32_t *incr_lens,
+                          int32_t num_seqs, int32_t num_q_heads, float scale, void *out, float *lse_out,
+                          void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return fail(PA_ERR_NULL_ARG, "workspace_bytes is NULL");
+  StepIn in;
+  in.k_new = k_new;
+  in.v_new = v_new;
+  in.slots = slot_mapping;
+  return forward(q, cache, block_tables, max_blocks_per_seq, hist_lens, incr_lens, num_seqs, num_q_heads,
+                 scale, out, lse_out, workspace, *workspace_bytes, stream, false, nullptr,
+                 workspace ? nullptr : workspace_bytes, &in);
+}
+
+pa_status pa_debug_step_flags(const void *workspace, const pa_kv_cache *cache, const int32_t *hist_lens,
+                              const int32_t *incr_lens, int32_t num_seqs, int32_t num_q_heads,
+                              uint32_t *flags_out, void *stream) {
+  pa_status st = check_cache(cache);
+  if (st) return st;
+  int64_t total_q = 0;
+  st = check_lengths(hist_lens, incr_lens, num_seqs, num_q_heads, cache, 0, false, &total_q);
+  if (st) return st;
+  if (!workspace || !flags_out) return fail(PA_ERR_NULL_ARG, "workspace/flags_out is NULL");
+  Plan P;
+  make_plan(hist_lens, incr_lens, num_seqs, cache, num_q_heads / cache->num_kv_heads, P, nullptr, true);
+  hipError_t e = hipMemcpyAsync(flags_out, (const unsigned char *)workspace + P.off_ctr + kCtrFlags * 4, 4,
+                                hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "flags copy");
+  return PA_OK;
 }
 
 pa_status paged_attn_forward_noalloc(const void *q, const pa_kv_cache *cache,

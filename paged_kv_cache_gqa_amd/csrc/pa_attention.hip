@@ -30,6 +30,7 @@
 //   decode_dma_kernel<BS, NW, NST>, decode_dma_fp8_kernel<BS, NW, NST>
 //                                  LDS-DMA decode, bf16 and E4M3 (head_dim 128)
 //   merge_kernel, merge_many_kernel  LSE merge of split items
+#include "pa_append.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -2343,6 +2344,182 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a, int first)
 }
 
 // =============================================================================
+// =============================================================================
+// One launch per step ([Agentic] §5.1-§5.2: a decode layer runs as two
+// persistent kernels, one block per SM, whose stages are task tables the
+// blocks claim by index, and the KV write comes before the attention that
+// reads it).  Here one grid of one 8-wave work-group per CU runs the whole
+// step: each work-group claims tasks from counters in the workspace with
+// vector atomics (one lane), in this order --
+//   1. kv_append chunks of the step's new tokens;
+//   2. (once) wait until every append task has finished: the attention below
+//      reads those tokens, and append tasks wait on nothing, so the wait
+//      ends (bounded all the same: past the bound a flag is set);
+//   3. prefill ranges of the persistent plan from its own XCD's queue (the
+//      planner puts one KV head's ranges on one XCD for L2 reuse), then the
+//      other XCDs' queues;
+//   4. decode items (eight waves, two stages).
+// A split tile's partials are merged by the work-group that writes its last
+// part: after its partial stores, one lane releases them at device scope and
+// counts the part in; the one that completes the count acquires and merges
+// (so a step has no merge launch).  Memory ordering: every wave waits for
+// its own stores (vmcnt 0) before the barrier, the counting lane then
+// releases at device scope (its XCD's L2 written back), and the merging
+// work-group's device-scope acquire (caches invalidated) precedes its reads
+// of other work-groups' partials.
+enum : int { kTaskAppend = 1, kTaskPrefill = 2, kTaskDecode = 3 };
+
+// The in-work-group LSE merge of one record: wave w takes rows w, w + 8, ...;
+// the lanes hold the part weights (64 parts at a time) and d = lane, lane +
+// 64 of the output.
+__device__ __forceinline__ void step_merge(const MergeArgs &a, const Merge mt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows = mt.nq << a.lg;
+  const float *po = mt.is_decode ? a.part_o_decode : a.part_o_prefill;
+  const float *pl = mt.is_decode ? a.part_lse_decode : a.part_lse_prefill;
+  const int rpp = mt.rows_per_part, np = mt.nparts, d = a.d;
+  for (int r = wave; r < rows; r += kStepThreads / 64) {
+    float M = -INFINITY;
+    for (int i0 = 0; i0 < np; i0 += 64)
+      if (i0 + lane < np) M = fmaxf(M, pl[(int64_t)(mt.part0 + i0 + lane) * rpp + r]);
+    M = wave_max(M);
+    float S = 0.f, O0 = 0.f, O1 = 0.f;
+    for (int i0 = 0; i0 < np; i0 += 64) {
+      const float li = i0 + lane < np ? pl[(int64_t)(mt.part0 + i0 + lane) * rpp + r] : -INFINITY;
+      const float w = (M > -INFINITY && li > -INFINITY) ? fast_exp2(li - M) : 0.f;
+      S += wave_sum(w);
+      const int nn = min(64, np - i0);
+      for (int i = 0; i < nn; i++) {
+        const float wi = __shfl(w, i);
+        const float *orow = po + ((int64_t)(mt.part0 + i0 + i) * rpp + r) * d;
+        O0 += wi * orow[lane];
+        if (d > 64) O1 += wi * orow[lane + 64];
+      }
+    }
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    const int64_t orow = (int64_t)(mt.row0 + (r >> a.lg)) * a.hq + mt.kvh * a.group + (r & (a.group - 1));
+    ((__bf16 *)a.out)[orow * d + lane] = (__bf16)(O0 * inv);
+    if (d > 64) ((__bf16 *)a.out)[orow * d + lane + 64] = (__bf16)(O1 * inv);
+    if (lane == 0 && a.lse_out) a.lse_out[orow] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+  }
+}
+
+// Thread 0's claim: the next task, encoded (kind << 28) | index, or -1.
+// (Claiming decode items first on half the XCDs, so that fewer compute
+// units stream the decode part while the rest compute prefill, measured
+// slower: 12.5-12.6 ms against 12.3-12.4 ms for the mixed step.)
+__device__ __forceinline__ int step_claim(const StepArgs &s, int &phase, uint32_t xcc, bool &waited,
+                                          bool &dec_empty) {
+  uint32_t *c = s.ctr;
+  if (phase == 0) {
+    const uint32_t i = atomicAdd(&c[kCtrAppendNext], 1u);
+    if (i < (uint32_t)s.n_append_tasks) return (kTaskAppend << 28) | (int)i;
+    phase = 1;
+  }
+  if (!waited) {
+    for (int it = 0; __hip_atomic_load(&c[kCtrAppendDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                     (uint32_t)s.n_append_tasks;
+         it++) {
+      if (it > (1 << 24)) {  // never expected: give up rather than hang
+        atomicOr(&c[kCtrFlags], 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    waited = true;
+  }
+  while (phase <= s.xcds) {  // phase p: the prefill queue of XCD (xcc + p - 1) % xcds
+    const int q = (int)((xcc + (uint32_t)phase - 1) % (uint32_t)s.xcds);
+    const int n = s.pre_queue_off[q + 1] - s.pre_queue_off[q];
+    if (n > 0) {
+      const uint32_t i = atomicAdd(&c[kCtrPrefillNext + q], 1u);
+      if (i < (uint32_t)n) return (kTaskPrefill << 28) | s.pre_queue[s.pre_queue_off[q] + (int)i];
+    }
+    phase++;
+  }
+  if (dec_empty) return -1;
+  const uint32_t i = atomicAdd(&c[kCtrDecodeNext], 1u);
+  if (i < (uint32_t)s.n_decode) return (kTaskDecode << 28) | (int)i;
+  dec_empty = true;
+  return -1;
+}
+
+template <int BS>
+__global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
+  // the decode ring (8 waves x 2 stages of K and V slices); the 384-row
+  // prefill's ring and the decode combine scratch lie inside it
+  constexpr int DEC_LDS = 8 * 2 * 2 * kDecSliceBytes;
+  static_assert(DEC_LDS >= kW48Stages * 2 * kW48TileBytes, "prefill ring");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[DEC_LDS];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  __shared__ int task_s, merge_s;
+  const int tid = threadIdx.x;
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  xcc %= (uint32_t)s.xcds;
+  int phase = 0;
+  bool waited = false, dec_empty = false;
+  // after a task's partial stores: count the part in; the last one merges
+  auto part_done = [&](int merge) __attribute__((always_inline)) {
+    PA_WAIT_VMCNT(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t old = atomicAdd(&s.ctr[kCtrMerge + merge], 1u);
+      const bool last = old + 1 == (uint32_t)s.mg.merges[merge].nparts;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      merge_s = last ? merge : -1;
+    }
+    __syncthreads();
+    if (merge_s >= 0) step_merge(s.mg, s.mg.merges[merge_s]);
+  };
+  for (;;) {
+    if (tid == 0) task_s = step_claim(s, phase, xcc, waited, dec_empty);
+    __syncthreads();
+    const int t = task_s;
+    __syncthreads();  // (task_s is rewritten by the next claim)
+    if (t < 0) break;
+    const int kind = t >> 28, idx = t & 0x0FFFFFFF;
+    if (kind == kTaskAppend) {
+      const uint32_t c0 = (uint32_t)idx * kStepAppendChunks;
+#pragma unroll 1
+      for (uint32_t gid = c0 + tid; gid < min(c0 + kStepAppendChunks, s.app.nchunks); gid += kStepThreads)
+        append_chunk<kKvBf16>(s.app, gid);
+      PA_WAIT_VMCNT(0);
+      __syncthreads();
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        atomicAdd(&s.ctr[kCtrAppendDone], 1u);
+      }
+    } else if (kind == kTaskPrefill) {
+      for (int i = s.wg_first[idx]; i < s.wg_first[idx + 1]; i++) {
+        const Item it = s.pre.items[i];
+        w48_item<BS, kKvBf16>(s.pre, it, (lds_u8 *)smem_raw);
+        if (it.part >= 0)
+          part_done(s.pre_part_merge[it.part]);
+        else
+          __syncthreads();  // LDS of this item no longer read or written
+      }
+    } else {
+      const Item it = s.dec.items[idx];
+      decode_dma_item<BS, 8, 2>(s.dec, it, smem_raw, bt_lds);
+      if (it.part >= 0) part_done(s.dec_part_merge[it.part]);
+    }
+  }
+}
+
+hipError_t launch_step(const StepArgs &a, int n_groups, int bs, hipStream_t s) {
+  if (n_groups <= 0) return hipSuccess;
+  if (bs == 16)
+    hipLaunchKernelGGL((step_kernel<16>), dim3(n_groups), dim3(kStepThreads), 0, s, a);
+  else if (bs == 64)
+    hipLaunchKernelGGL((step_kernel<64>), dim3(n_groups), dim3(kStepThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <int D, int BS, bool FP8>
 static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (D == 128) {

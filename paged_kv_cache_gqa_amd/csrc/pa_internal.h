@@ -144,6 +144,37 @@ constexpr int kDecodeRows = 16;    // query rows per decode tile
 constexpr int kKeyTile = 64;       // keys per inner-loop tile
 
 // Launchers (defined next to their kernels).
+// One launch per step: persistent work-groups claim tasks -- kv_append token
+// chunks, prefill ranges (per-XCD queues), decode items -- by vector atomics
+// on counters in the workspace; the last writer of a split tile's partials
+// merges them.  Counters (uint32, zeroed by the work-list copy):
+constexpr int kCtrAppendNext = 0;   // next append task
+constexpr int kCtrAppendDone = 1;   // append tasks finished
+constexpr int kCtrDecodeNext = 2;   // next decode item
+constexpr int kCtrFlags = 3;        // bit 0: a bounded wait gave up (never expected)
+constexpr int kCtrPrefillNext = 4;  // [kMaxXcds] next range of each XCD's prefill queue
+constexpr int kMaxXcds = 8;
+constexpr int kCtrMerge = kCtrPrefillNext + kMaxXcds;  // [n_merges] partials written per merge record
+constexpr int kStepThreads = 512;
+constexpr int kStepAppendChunks = 8 * kStepThreads;  // 16-byte append chunks per append task
+
+struct StepArgs {
+  AttnArgs pre;                  // prefill items and partial arrays
+  AttnArgs dec;                  // decode items and partial arrays
+  AppendArgs app;                // the step's new tokens (tok0 = 0, nchunks = all)
+  MergeArgs mg;                  // merge records over both partial arrays
+  const int32_t *wg_first;       // prefill range r: items [wg_first[r], wg_first[r+1])
+  const int32_t *pre_queue;      // range ids, XCD queue by XCD queue
+  const int32_t *pre_queue_off;  // [kMaxXcds + 1]
+  const int32_t *pre_part_merge; // merge record of each prefill partial slot
+  const int32_t *dec_part_merge; // ... of each decode partial slot
+  uint32_t *ctr;
+  int32_t n_append_tasks;
+  int32_t n_decode;
+  int32_t xcds;                  // queues in use (1 .. kMaxXcds)
+};
+
+hipError_t launch_step(const StepArgs &a, int n_groups, int bs, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 // bf16 head_dim 128 decode launch with shared-prefix cascade items first

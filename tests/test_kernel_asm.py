@@ -114,13 +114,16 @@ def _loop_depths(asm, name):
 
 
 def test_no_scratch_in_loops_and_no_packed_fp32(attention_asm):
-    """Spills are tolerated only outside loops and in the 384-row kernel's
-    per-item code (the loop over a work-group's items, depth 1); the key-step
-    loops, where the time goes, must run from registers."""
+    """Spills are tolerated only outside loops and in per-item code: the
+    384-row kernel's loop over a work-group's items (depth 1), and the
+    one-launch step kernel's task loop and the items within a task (depths 1
+    and 2); the key-step loops, where the time goes, must run from registers
+    (the step kernel's inner loops are the same item code, checked in the
+    standalone kernels)."""
     for name in _functions(attention_asm):
-        item_loop = "prefill_w48_kernel" in name
+        item_depth = 1 if "prefill_w48_kernel" in name else 2 if "step_kernel" in name else 0
         for depth, line in _loop_depths(attention_asm, name):
             op = line.split()[0]
             if op.startswith("scratch_"):
-                assert depth == 0 or (item_loop and depth == 1), f"{name} spills in a loop: {line}"
+                assert depth <= item_depth, f"{name} spills in a loop: {line}"
             assert op not in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"), f"{name}: {line}"
