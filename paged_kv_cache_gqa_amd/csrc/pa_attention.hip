@@ -431,7 +431,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   constexpr bool FP8 = FMT == kKvE4m3;
   constexpr bool FP4 = FMT == kKvMxfp4;
   constexpr bool CODED = FP8 || FP4;  // the tiles are widened from a code ring
-  constexpr int REQ = FP4 ? 1 : 2;    // requests per wave and step
+  constexpr int REQ = FP4 ? 1 : 2;    // requests per wave and step (E4M3: of the scale-loading waves)
   constexpr int D = 128;
   constexpr int NCQ = D / 32;  // k-steps of the score product
   constexpr int NDB = D / 16;  // d-blocks of the value product
@@ -558,10 +558,12 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   int blk_next = block_of(rpos);
   constexpr int RING = CODED ? 4 * TILEB : 0;  // the code ring follows the four bf16 tiles
   constexpr int SCB = RING + NCS * 2 * CB;   // E4M3: then the scale ring
-  // E4M3: with its codes, each wave requests the scale of the block its rows
-  // lie in (K waves the K scale, V waves the V scale) into the step's slot
-  // of the scale ring (the 16-key half of its rows: (wave % 4) / 2); every
-  // lane reads the same 4 bytes.  Two requests per wave and step.
+  // E4M3: with its codes, one wave per scale the step needs also requests
+  // it into the step's slot of the scale ring: waves 0 (K) and 4 (V), and
+  // for block 16, whose two 16-key halves lie in different blocks, waves 2
+  // and 6 for the second half (the half of a wave's rows is (wave % 4) / 2);
+  // every lane reads the same 4 bytes.  Those waves make two requests a
+  // step, the others one.
   const uint64_t sc_head = (uint64_t)(FP8 && wave >= 4 ? a.c.vs : a.c.ks) + (uint64_t)kvh * 4;
   // MXFP4 scale bytes of this wave's KV head: [block][hkv][group][BS]
   const uint64_t sc4_head = (uint64_t)(fp4_v ? a.c.vs : a.c.ks) + (uint64_t)kvh * (D / 32) * BS;
@@ -569,6 +571,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   const uint32_t fp4_dst = wave < 4 ? (fp4_v ? kW48Fp4CodeBytes : 0) + (wave & 1) * 1024
                                     : 2 * kW48Fp4CodeBytes + (2 * (fp4_v ? 1 : 0) + (wave & 1)) * 64;
   const uint32_t sc_lane0 = SCB + (wave >= 4 ? 512 : 0) + (qw >> 1) * 256;
+  const bool sc_loader = FP8 && (SPLIT ? (qw & 1) == 0 : qw == 0);
   uint32_t sc_off = 0;
   const int zero = 0;
   auto issue = [&]() __attribute__((always_inline)) {
@@ -599,10 +602,12 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
                          __builtin_amdgcn_readfirstlane((int)((ga >> 32) & 0xFFFF)), nrec, kRsrcFlags};
       dma_load16(r, voff, smem_addr + RING + st_off + (wave >= 4 ? CB : 0) + qw * 1024);
       st_off = st_off + 2 * CB == NCS * 2 * CB ? 0 : st_off + 2 * CB;
-      const uint64_t sa = sc_head + (uint64_t)blk * ((uint32_t)hkv * 4);
-      const i32x4_t rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)sa),
-                          __builtin_amdgcn_readfirstlane((int)((sa >> 32) & 0xFFFF)), 4, kRsrcFlags};
-      dma_load4(rs, zero, smem_addr + sc_lane0 + sc_off);
+      if (sc_loader) {
+        const uint64_t sa = sc_head + (uint64_t)blk * ((uint32_t)hkv * 4);
+        const i32x4_t rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)sa),
+                            __builtin_amdgcn_readfirstlane((int)((sa >> 32) & 0xFFFF)), 4, kRsrcFlags};
+        dma_load4(rs, zero, smem_addr + sc_lane0 + sc_off);
+      }
       sc_off = (sc_off + kW48ScaleSlotBytes) & (kW48ScaleSlots * kW48ScaleSlotBytes - 1);
     } else {
       const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 4) * (D * 2));
@@ -885,7 +890,10 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   if constexpr (CODED) {
 #pragma unroll
     for (int k = 0; k < NCS; k++) issue();
-    PA_WAIT_VMCNT(REQ * (NCS - 2));
+    if (FP8 && !sc_loader)
+      PA_WAIT_VMCNT(NCS - 2);
+    else
+      PA_WAIT_VMCNT(REQ * (NCS - 2));
     wg_barrier();
     widen(t_begin, false);
     widen(t_begin, true);
@@ -911,7 +919,10 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // group 1 its vector phase.
   auto open_step = [&]() __attribute__((always_inline)) {
     if constexpr (CODED) {
-      PA_WAIT_VMCNT(REQ * (NCS - 3));
+      if (FP8 && !sc_loader)
+        PA_WAIT_VMCNT(NCS - 3);
+      else
+        PA_WAIT_VMCNT(REQ * (NCS - 3));
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's widened chunks are written
     } else {
       PA_WAIT_VMCNT(2 * (NST - 3));
