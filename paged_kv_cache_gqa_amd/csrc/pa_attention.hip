@@ -414,7 +414,7 @@ constexpr int kW48TileBytes = 8 * kW48BlockBytes;
 #define PA_W48_STAGES 4
 #endif
 constexpr int kW48Stages = PA_W48_STAGES;
-constexpr int kW48CodeStages = 4;                // E4M3: stages of the code ring
+constexpr int kW48CodeStages = 8;                // E4M3 and MXFP4: stages of the code ring (8 against 4: 57.3 -> 55.0 ms for the 1M-token E4M3 prefill)
 constexpr int kW48CodeBytes = kW48Step * 128;    // E4M3 codes of one step's K (or V)
 constexpr int kW48ScaleSlots = 8;                // E4M3: steps held by the scale ring
 constexpr int kW48ScaleSlotBytes = 1024;         // K half 0, K half 1, V half 0, V half 1: 256 bytes each
