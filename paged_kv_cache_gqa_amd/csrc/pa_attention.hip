@@ -499,7 +499,9 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   // the length of an item (the planner never cuts an item for length).
   typedef const __attribute__((address_space(4))) int32_t cint;
   const cint *btr = (const cint *)(a.bt + (int64_t)it.seq * a.max_blocks);
-  auto block_of = [&](int key) __attribute__((always_inline)) { return btr[min(key / BS, last_blk)]; };
+  auto block_of = [&](int key) __attribute__((always_inline)) {
+    return btr[(uint32_t)min((int)((uint32_t)key / BS), last_blk)];  // (key >= 0: an unsigned shift)
+  };
 
   // LDS tile of one step (32 keys, 256 bytes each): key row k lies in block
   // k / 4 (blocks kW48BlockBytes apart: 1 KB of data + 32 bytes), and within
@@ -525,9 +527,11 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
 
   // K/V requests walk the item's steps in order, so their positions are
   // running counters.  Items start on a step boundary (the planner cuts key
-  // ranges in multiples of 64 keys), so rpos >= kv_lo.  A request past the
-  // range end has a buffer size of zero: it moves no data but keeps the
-  // per-step vmcnt accounting.
+  // ranges in multiples of 64 keys), so rpos >= kv_lo.  A request's buffer
+  // size is the bytes of the range's rows left from its first row on (no
+  // upper clamp: its lanes never address past the request's own rows), so
+  // rows past the range end read as zeros, and a request past the end has
+  // size zero: it moves no data but keeps the per-step vmcnt accounting.
   constexpr int LGBS = BS == 16 ? 4 : 6;
   static_assert(BS == 16 || BS == 64, "block size");
   constexpr int KEYB = FP4 ? D / 2 : FP8 ? D : 2 * D;  // bytes of one key row (K or V)
@@ -580,7 +584,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
     if constexpr (FP4) {
       const uint32_t dst = smem_addr + RING + st_off + fp4_dst;
       if (wave < 4) {
-        const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 16) * KEYB);
+        const int nrec = __builtin_amdgcn_readfirstlane(max(kv_hi - rpos, 0) * KEYB);
         const uint64_t ga = my_head + off;
         const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ga),
                            __builtin_amdgcn_readfirstlane((int)((ga >> 32) & 0xFFFF)), nrec, kRsrcFlags};
@@ -596,7 +600,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
       }
       st_off = st_off + kW48Fp4StageBytes == NCS * kW48Fp4StageBytes ? 0 : st_off + kW48Fp4StageBytes;
     } else if constexpr (FP8) {
-      const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 8) * D);
+      const int nrec = __builtin_amdgcn_readfirstlane(max(kv_hi - rpos, 0) * D);
       const uint64_t ga = my_head + off;
       const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)ga),
                          __builtin_amdgcn_readfirstlane((int)((ga >> 32) & 0xFFFF)), nrec, kRsrcFlags};
@@ -610,7 +614,7 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
       }
       sc_off = (sc_off + kW48ScaleSlotBytes) & (kW48ScaleSlots * kW48ScaleSlotBytes - 1);
     } else {
-      const int nrec = __builtin_amdgcn_readfirstlane(min(max(kv_hi - rpos, 0), 4) * (D * 2));
+      const int nrec = __builtin_amdgcn_readfirstlane(max(kv_hi - rpos, 0) * (D * 2));
       const uint32_t st = smem_addr + st_off;
       const uint64_t ka = kc_head + off, va = vc_head + off;
       // (readfirstlane keeps the descriptor in SGPRs, as the asm operand needs)
@@ -784,7 +788,11 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
 #pragma unroll
         for (int rb = 0; rb < RB; rb++) o[NDB][rb][0] *= rv;
       }
-      if ((((t + 1) * kW48Step) & (BS - 1)) == 0) read_scales(t + 1);
+      // (every step, although only a block's first step uses them: read
+      // conditionally, the values had to be copied out at the branch's join,
+      // which made the phase wait for its outstanding LDS and scalar loads
+      // right there instead of at its end)
+      read_scales(t + 1);
       mul[0] = mul[1] = mul_k;
     } else if constexpr (FP8) {
       float rv[2];
