@@ -684,60 +684,99 @@ __device__ __forceinline__ void w48_item(const AttnArgs &a, const Item it, lds_u
   };
 
   // Matrix-core phase: O += V(t)^T P(t)^T (24 MFMAs, 16 transposing reads),
-  // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads), reads kept ~10 ahead.
+  // then S(t+1) = K(t+1) Q^T (24 MFMAs, 8 reads): the first three V
+  // fragments' reads; per three MFMAs (one fragment's worth) the reads of the
+  // fragment three ahead -- V during the value product's first 15 MFMAs, K
+  // during its last 9 and the score product's first 3, in the order the score
+  // product uses them -- so about three fragments are in flight at any time.
+  // bf16 and E4M3 pin that order with scheduling barriers between the groups
+  // (left to the scheduler, K fragments were at times requested in the
+  // reverse of their use, into the registers the value product frees last,
+  // and the score product's first MFMAs waited for them: pinned, ~1%
+  // faster); MXFP4 measured 7% slower pinned and leaves the placement of the
+  // same groups to the scheduler.
   auto gemm = [&](auto with_qk_tag, const lds_u8 *Vb, const lds_u8 *Kb) __attribute__((always_inline)) {
     constexpr bool with_qk = decltype(with_qk_tag)::value;
+    static_assert(NDB == 8 && NCQ == 4 && RB == 3, "the phase's read order is laid out for d 128, 48 rows");
     bf16x8 vf[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; db++) {
+    bf16x8 kf[NCQ][2];
+    auto read_v = [&](int db) __attribute__((always_inline)) {
       const bf16x4 h0 = lds_read_tr(Vb + vofs(db));
       const bf16x4 h1 = lds_read_tr(Vb + KB16 + vofs(db));
       vf[db] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    };
+    auto read_k = [&](int i) __attribute__((always_inline)) {
+      kf[i >> 1][i & 1] = as_bf16x8(lds_load16(Kb + (i & 1) * KB16 + kofs(i >> 1)));
+    };
+    if constexpr (FP4) {
 #pragma unroll
-    for (int db = 0; db < NDB; db++)
+      for (int db = 0; db < NDB; db++) read_v(db);
 #pragma unroll
-      for (int rb = 0; rb < RB; rb++) o[db][rb] = mfma16x16x32(vf[db], pb[rb], o[db][rb]);
+      for (int db = 0; db < NDB; db++)
 #pragma unroll
-    for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
-    if constexpr (with_qk) {
-      bf16x8 kf[NCQ][2];
+        for (int rb = 0; rb < RB; rb++) o[db][rb] = mfma16x16x32(vf[db], pb[rb], o[db][rb]);
 #pragma unroll
-      for (int c = 0; c < NCQ; c++)
+      for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
+      if constexpr (with_qk) {
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) kf[c][kb] = as_bf16x8(lds_load16(Kb + kb * KB16 + kofs(c)));
+        for (int i = 0; i < 2 * NCQ; i++) read_k(i);
 #pragma unroll
-      for (int c = 0; c < NCQ; c++)
+        for (int c = 0; c < NCQ; c++)
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+          for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-          for (int rb = 0; rb < RB; rb++)
-            S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} : S[kb][rb]);
-      // order: the first three V fragments' reads; then per three MFMAs
-      // (one fragment's worth) the reads of the fragment three ahead -- V
-      // reads during the value product's first 15 MFMAs, K reads during its
-      // last 9 and the score product's first 6 -- so about three fragments
-      // are in flight at any time
+            for (int rb = 0; rb < RB; rb++)
+              S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} : S[kb][rb]);
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
+      for (int i = 0; i < (with_qk ? 8 : 5); i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      if constexpr (with_qk) {
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 2; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 21, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 21, 0);
     } else {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      read_v(0);
+      read_v(1);
+      read_v(2);
 #pragma unroll
-      for (int i = 0; i < 5; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int db = 0; db < NDB; db++) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) o[db][rb] = mfma16x16x32(vf[db], pb[rb], o[db][rb]);
+        if (db + 3 < NDB) {
+          read_v(db + 3);
+        } else if constexpr (with_qk) {
+          read_k(2 * (db - 5));
+          read_k(2 * (db - 5) + 1);
+        }
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) o[NDB][rb] = mfma16x16x32(ones, pb[rb], o[NDB][rb]);
+      if constexpr (with_qk) {
+        read_k(6);
+#pragma unroll
+        for (int c = 0; c < NCQ; c++)
+#pragma unroll
+          for (int kb = 0; kb < 2; kb++) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rb = 0; rb < RB; rb++)
+              S[kb][rb] = mfma16x16x32(kf[c][kb], qf[rb][c], c == 0 ? f32x4{} : S[kb][rb]);
+            if (c == 0 && kb == 0) read_k(7);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto qk_only = [&](const lds_u8 *Kb) __attribute__((always_inline)) {
