@@ -332,25 +332,44 @@ def report_mixed_one_launch(pa, torch, spec, dev, steps, warmup, label):
             "note": "prefill and decode parts share the launch: no per-part rates"}
 
 
-def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False):
-    """One call holding 4 incremental prefills and 48 decodes: the prefill
-    part in TFLOP/s over its kernel, the decode part in GB/s over its kernels
-    (the decode launch holds the shared-prefix cascade items when the
-    sub-agents are declared as a group; the shared prefix's blocks are counted
-    once either way)."""
-    r = Runner(pa, torch, spec, dev)
-    if cascade:
-        r.use_cascade()
-    ms, kern = r.timed(steps, warmup)
+def report_mixed(pa, torch, spec, dev, steps, warmup, label, cascade=False, overlap=None):
+    """One call holding 4 incremental prefills and 48 decodes.  Launched one
+    after the other (overlap=0, or the cascade entry point): the prefill part
+    in TFLOP/s over its kernel, the decode part in GB/s over its kernel (the
+    decode launch holds the shared-prefix cascade items when the sub-agents
+    are declared as a group; the shared prefix's blocks are counted once
+    either way).  Co-scheduled (the planner's choice): the decode's first
+    launch runs beside the prefill on a few CUs, so per-kernel rates overlap;
+    the parts' rates are given over the whole step instead."""
+    if overlap is not None:
+        pa.pa_debug_overlap_cus(overlap)
+    try:
+        r = Runner(pa, torch, spec, dev)
+        if cascade:
+            r.use_cascade()
+        ms, kern = r.timed(steps, warmup)
+        groups = pa.pa_debug_plan_groups(spec.hist, spec.incr, spec.num_q_heads, r.cache)
+    finally:
+        if overlap is not None:
+            pa.pa_debug_overlap_cus(-1)
     fl, _, byts = mixed_parts(spec)
     p_ms = kern["prefill"][0] * kern["prefill"][1]
-    d_ms = kern["decode"][0] * kern["decode"][1]
-    d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern),
-         "prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
-         "prefill_frac": round(fl / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-         "decode_GB/s_kernel": round(byts / (d_ms * 1e-3) / 1e9, 1),
-         "decode_frac": round(byts / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-         "decode_unique_bytes": int(byts)}
+    d = {"workload": label, "ms_per_step": round(ms, 4), "kernels_ms": _kern(kern)}
+    if kern["decode"][1] > 1.5:  # co-scheduled: one decode launch beside the prefill, one after
+        cus = pa.pa_device_shape()[0]
+        n_pre = len(groups) - 1
+        d.update({"co_scheduled": {"prefill_cus": n_pre, "decode_cus_beside_prefill": cus - n_pre},
+                  "prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
+                  "prefill_TFLOP/s_over_step": round(fl / (ms * 1e-3) / 1e12, 2),
+                  "decode_GB/s_over_step": round(byts / (ms * 1e-3) / 1e9, 1),
+                  "decode_unique_bytes": int(byts)})
+    else:
+        d_ms = kern["decode"][0] * kern["decode"][1]
+        d.update({"prefill_TFLOP/s_kernel": round(fl / (p_ms * 1e-3) / 1e12, 2),
+                  "prefill_frac": round(fl / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "decode_GB/s_kernel": round(byts / (d_ms * 1e-3) / 1e9, 1),
+                  "decode_frac": round(byts / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "decode_unique_bytes": int(byts)})
     del r
     torch.cuda.empty_cache()
     return d
@@ -604,8 +623,8 @@ PROFILED = [("incremental", PREFILL_KERNEL, "incremental_45.7k_to_48.4k", "prefi
             ("long_prefill", PREFILL_FP8_KERNEL, "prefill_e4m3_1m_plus_4096", "prefill_long_e4m3_bytes"),
             ("long_prefill_mxfp4", PREFILL_FP4_KERNEL, "prefill_mxfp4_1m_plus_4096", "prefill_long_mxfp4_bytes"),
             ("kv_append_1m", APPEND_KERNEL, "kv_append_1m_bf16", "kv_append_1m_bytes"),
-            ("mixed", PREFILL_KERNEL, "mixed_step_prefill_part", "prefill_mixed_bytes"),
-            ("mixed", DECODE_KERNEL, "mixed_step_decode_part", "decode_mixed_bytes")]
+            ("mixed_sequential", PREFILL_KERNEL, "mixed_step_prefill_part", "prefill_mixed_bytes"),
+            ("mixed_sequential", DECODE_KERNEL, "mixed_step_decode_part", "decode_mixed_bytes")]
 
 
 def only_spec(W, name):
@@ -613,6 +632,7 @@ def only_spec(W, name):
     return {"incremental": lambda: W.incremental(), "decode": lambda: W.decode_batch(),
             "incremental_128k": lambda: W.incremental(131_072, 2_700, "incremental_128k"),
             "long_decode": lambda: W.long_context(1_048_575, 1), "mixed": lambda: W.mixed(),
+            "mixed_sequential": lambda: W.mixed(),
             "long_decode_mxfp4": lambda: W.long_context_mxfp4(1_048_575, 1),
             "long_prefill": lambda: W.long_context(), "long_prefill_mxfp4": lambda: W.long_context_mxfp4()}[name]()
 
@@ -622,7 +642,7 @@ def algorithmic_work(W, name, kernel=None):
     if name == "kv_append_1m":
         return 0, 2 * 1_048_576 * 8 * 128 * 2 * 2 + 1_048_576 * 8
     spec = only_spec(W, name)
-    if name == "mixed":
+    if name in ("mixed", "mixed_sequential"):
         fl, dfl, byts = mixed_parts(spec)
         return (dfl, byts) if kernel == DECODE_KERNEL else (fl, 0)
     fl = prefill_flops(spec.hist, spec.incr, spec.num_q_heads, spec.head_dim)
@@ -806,7 +826,8 @@ def main():
                     help="skip the measured MFMA and HBM-read ceilings")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["incremental", "decode", "incremental_128k", "long_decode", "kv_append_1m",
-                                       "mixed", "long_decode_mxfp4", "long_prefill", "long_prefill_mxfp4"],
+                                       "mixed", "mixed_sequential", "long_decode_mxfp4", "long_prefill",
+                                       "long_prefill_mxfp4"],
                     help="run one workload (for profiling); prints its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (HBM counter calibration)")
@@ -843,6 +864,8 @@ def main():
         return
     if args.only:
         spec = only_spec(W, args.only)
+        if args.only == "mixed_sequential":  # the prefill and decode launches one after the other
+            pa.pa_debug_overlap_cus(0)
         r = Runner(pa, torch, spec, dev)
         ms, kern = r.timed(args.steps, args.warmup)
         print(json.dumps({"workload": args.only, "ms_per_step": round(ms, 4),
@@ -940,7 +963,12 @@ def main():
         rep["mixed_step"] = report_mixed(
             pa, torch, W.mixed(), dev, rs, rw,
             "mixed: 4 incremental prefills (lognormal histories, median 100K) + 48 decodes "
-            "(8 over a shared 10,000-token prefix), 32 q / 8 KV, d 128, block 16, bf16, one call")
+            "(8 over a shared 10,000-token prefix), 32 q / 8 KV, d 128, block 16, bf16, one call "
+            "(the decode co-scheduled beside the prefill as the planner chooses)")
+        rep["mixed_step_sequential"] = report_mixed(
+            pa, torch, W.mixed(), dev, rs, rw,
+            "the same mixed step with the prefill and decode launches one after the other",
+            overlap=0)
         rep["mixed_step_cascade"] = report_mixed(
             pa, torch, W.mixed(), dev, rs, rw,
             "the same mixed step through paged_attn_forward_cascade, the 8 sub-agents declared as a "

@@ -170,6 +170,14 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  * cache, code * scale widens to bf16 exactly and the arithmetic is the bf16
  * path's.
  * Neither q nor the caches are written.
+ * Streams: everything is ordered after the work already on `stream`, and
+ * work enqueued on `stream` afterwards is ordered after all of it.  A step
+ * that holds both prefill and decode rows (bf16 KV, head_dim 128) may run
+ * its decode partly on a second, library-owned stream per device, forked
+ * from `stream` by an event and joined back to it before the merges, so the
+ * decode streams from HBM on a few CUs while the prefill occupies the others
+ * ([Agentic] §5.1-5.2: the decode's tasks taken from a table by persistent
+ * work-groups).  Calls from several host threads serialise that section.
  */
 PA_API pa_status paged_attn_forward(const void *q, const pa_kv_cache *cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -312,6 +320,16 @@ PA_API pa_status pa_timing_read(int kind, double *ms, int64_t *count);
 PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_lens,
                                int32_t num_seqs, int32_t num_q_heads, const pa_kv_cache *cache,
                                int32_t *items_out, int32_t items_cap, int32_t *counts_out);
+
+/* Test and measurement hook for the co-scheduled mixed step (see
+ * paged_attn_forward): n < 0 (the default) lets the planner choose how many
+ * CUs to take from the prefill for the decode; n > 0 forces that many
+ * (rounded down to a multiple of the XCD count, at most half the CUs); n = 0
+ * runs the launches one after the other.  A prefill too small to hold every
+ * CU leaves the others to the decode whenever co-scheduling is on.  Applies
+ * to every later plan that qualifies (pa_workspace_size and the debug plans
+ * alike); process-wide. */
+PA_API pa_status pa_debug_overlap_cus(int32_t n);
 
 /* Test hook for the persistent prefill launch: when the plan for these HOST
  * lengths runs the persistent 384-row kernel (head_dim 128, bf16 or E4M3 KV)

@@ -26,7 +26,7 @@ EXPORTS = ("kv_append", "paged_attn_forward", "pa_workspace_size", "pa_last_erro
            "pa_debug_gather", "pa_timing_enable", "pa_timing_read", "pa_debug_plan",
            "pa_debug_plan_groups", "pa_peak_mfma", "pa_peak_read", "pa_device_shape",
            "pa_debug_xcc_ids", "paged_attn_forward_noalloc", "paged_attn_forward_cascade",
-           "paged_attn_step", "pa_debug_step_flags")
+           "paged_attn_step", "pa_debug_step_flags", "pa_debug_overlap_cus")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
@@ -70,10 +70,11 @@ def _load():
                                              C.POINTER(sz), P]
     L.paged_attn_step.argtypes = [pc, P, P, P, P, P, i32, P, P, i32, i32, C.c_float, P, P, P, C.POINTER(sz), P]
     L.pa_debug_step_flags.argtypes = [P, pc, P, P, i32, i32, C.POINTER(C.c_uint32), P]
+    L.pa_debug_overlap_cus.argtypes = [i32]
     for f in ("kv_append", "paged_attn_forward", "paged_attn_forward_noalloc", "paged_attn_forward_cascade",
               "paged_attn_step", "pa_debug_step_flags", "pa_debug_gather", "pa_timing_enable",
               "pa_timing_read", "pa_debug_plan", "pa_debug_plan_groups", "pa_peak_mfma",
-              "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids"):
+              "pa_peak_read", "pa_device_shape", "pa_debug_xcc_ids", "pa_debug_overlap_cus"):
         getattr(L, f).restype = C.c_int
     return L
 
@@ -412,6 +413,12 @@ def pa_peak_read(buf, out, stream=None):
     """Enqueue a streaming read of the device buffer buf (out: int32 [PEAK_READ_THREADS])."""
     _check(lib.pa_peak_read(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(out),
                             _stream_ptr(stream)))
+
+
+def pa_debug_overlap_cus(n):
+    """CUs that stream decode items beside the prefill in later plans: n < 0
+    the planner's choice (default), n >= 0 forced (0: no co-scheduling)."""
+    _check(lib.pa_debug_overlap_cus(int(n)))
 
 
 def pa_device_shape():

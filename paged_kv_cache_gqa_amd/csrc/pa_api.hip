@@ -9,10 +9,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -82,19 +84,20 @@ pa_status check_cache(const pa_kv_cache *c) {
 // cut into 128-row prefill tiles.  Key ranges are split so that there are
 // enough similar-sized items to fill every compute unit; split items write
 // partials merged by LSE ([Agentic] §4.3.3).
-#ifndef PA_DEC_ITEMS_PER_CU
-#define PA_DEC_ITEMS_PER_CU 4
-#endif
-constexpr int kDecodeItemsPerCU = PA_DEC_ITEMS_PER_CU;
+constexpr int kDecodeItemsPerCU[] = {1, 2, 4};  // candidate decode cuts (decode_chunk)
 constexpr int kDecodeMinChunk = 2048;
+constexpr int kDecodeItemStartKeys = 512;  // an item's start-up, in keys streamed
 constexpr int kPrefillItemsPerCU = 8;
 
 // The machine the plan is cut for: compute units and XCDs (chiplets, each
 // with its own L2) of the current device, queried once per device.  Without a
 // device (the host-only planning hooks on a machine with no GPU) the MI355X's
 // 256 CUs in 8 XCDs are assumed.  Work-group ids are dispatched round-robin
-// over the XCDs (work-group w runs on XCD w mod num_xcds); pa_debug_xcc_ids
-// lets a test check that on the GPU.
+// over the XCDs (work-group w runs on XCD (w + k) mod num_xcds, k fixed per
+// launch: 0 for a launch alone on the GPU, possibly not while another
+// stream's launch is being dispatched); pa_debug_xcc_ids lets a test check
+// that on the GPU.  The plans rely only on the work-groups of one residue
+// class sharing an XCD.
 struct MachineShape {
   int32_t cus = 256;
   int32_t xcds = 8;
@@ -144,8 +147,11 @@ struct Plan {
   std::vector<int32_t> step_queue, step_queue_off, step_pre_merge, step_dec_merge;
   int32_t step_xcds = 1, step_ranges = 0;
   size_t n_ctr = 0;
+  // co-scheduled mixed step: CUs that stream decode items beside the
+  // persistent prefill launch (0: the launches run one after the other)
+  int32_t overlap_cus = 0;
   size_t off_prefill = 0, off_decode = 0, off_merges = 0, off_wg = 0, off_cascade = 0, off_members = 0,
-         off_sq = 0, off_sqo = 0, off_spm = 0, off_sdm = 0, off_ctr = 0, plan_bytes = 0;
+         off_sq = 0, off_sqo = 0, off_spm = 0, off_sdm = 0, off_ctr = 0, off_claim = 0, plan_bytes = 0;
   size_t off_po_pre = 0, off_pl_pre = 0, off_po_dec = 0, off_pl_dec = 0, total = 0;
 };
 
@@ -330,11 +336,102 @@ void plan_persistent(const std::vector<Tile> &tiles, int32_t hkv, int32_t tile_r
   P.wg_first[nwg] = (int32_t)P.prefill.size();
 }
 
+// Key length of decode items.  Fewer, longer items pay an item's start-up
+// (its block ids staged, the first loads in flight) less often; more, shorter
+// ones balance better.  Among the cuts for 1, 2 and 4 items per CU (at least
+// kDecodeMinChunk, at most kMaxDecItemKeys keys), the one with the shortest
+// predicted makespan is taken: the items are dispatched longest first, each
+// to the CU that frees first (one decode work-group per CU), and an item
+// costs its keys plus kDecodeItemStartKeys.  (A single 1M-token sequence:
+// 256 items of 32K keys instead of 1,024 of 8K, 6% faster for 4-bit KV.)
+int64_t decode_chunk(const std::vector<Tile> &tiles, int32_t hkv, int32_t cus, int64_t wd) {
+  int64_t best_chunk = kMaxDecItemKeys, best_span = -1;
+  std::vector<std::pair<int32_t, int32_t>> ranges;
+  std::vector<int64_t> cost;
+  for (const int k : kDecodeItemsPerCU) {
+    const int64_t chunk = std::min<int64_t>(
+        kMaxDecItemKeys, std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), (int64_t)k * cus)));
+    cost.clear();
+    for (const Tile &t : tiles) {
+      if (!t.decode) continue;
+      cut(t.keys, (int32_t)std::min<int64_t>(cdiv64(t.keys, chunk), INT32_MAX), ranges);
+      for (const auto &r : ranges)
+        for (int32_t h = 0; h < hkv; h++) cost.push_back((int64_t)(r.second - r.first) + kDecodeItemStartKeys);
+    }
+    std::sort(cost.begin(), cost.end(), std::greater<int64_t>());
+    // list scheduling: a min-heap of the CUs' finishing times
+    std::vector<int64_t> cu(std::min<size_t>((size_t)cus, cost.size()), 0);
+    int64_t span = 0;
+    for (size_t i = 0; i < cost.size(); i++) {
+      if (i < cu.size()) {
+        cu[i] = cost[i];
+        if (i + 1 == cu.size()) std::make_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+      } else {
+        std::pop_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+        cu.back() += cost[i];
+        std::push_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+      }
+    }
+    for (const int64_t f : cu) span = std::max(span, f);
+    if (best_span < 0 || span < best_span) best_span = span, best_chunk = chunk;
+  }
+  return best_chunk;
+}
+
+// Co-scheduling a mixed step's decode with its prefill.  The 384-row prefill
+// keeps every CU's matrix cores busy but draws little from HBM; the decode
+// streams from HBM and computes little.  A CU streams more than its 1/256
+// share of the chip's bandwidth when few CUs stream (measured with the
+// LDS-filling read alone: 59 GB/s per CU with 32 CUs, 55 with 64, 48 with
+// 128, 28 with all 256; the decode items beside the prefill: ~38 GB/s per
+// CU), so a few CUs given to the decode while the others prefill stream most
+// of it before the prefill ends.  The candidates are multiples of the XCD
+// count (an equal number per XCD, so the prefill's ranges stay balanced per
+// XCD) up to half the CUs; the time of each is predicted as the prefill on
+// the remaining CUs plus the decode bytes those few CUs could not stream
+// meanwhile, streamed afterwards by the whole chip; the shortest wins (0: no
+// co-scheduling).  Unit costs, MI355X: a 384-row tile's 64-key step of one
+// KV head takes a CU ~2.47 us; the decode streams ~38 GB/s per CU beside the
+// prefill and ~6.5 TB/s over the whole chip.  (The mixed step of 4
+// incremental prefills and 48 decodes: 12.55 ms one after the other, 11.7 ms
+// with 48 to 64 decode CUs.)
+constexpr double kCoPrefillStepSec = 2.47e-6;
+constexpr double kCoDecodeCuBytesPerSec = 38e9;
+constexpr double kCoDecodeChipBytesPerSec = 6.5e12;
+std::atomic<int32_t> g_overlap_force{-1};  // pa_debug_overlap_cus: < 0 the model's choice
+
+// Returns the CUs taken from the prefill's share (-1: no co-scheduling).  A
+// prefill too small to fill every CU (at least kMinGroupKeyTiles steps per
+// work-group) leaves the rest to the decode at no cost.
+int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int32_t hkv, int32_t d, const MachineShape &M) {
+  int64_t units = 0, dec_bytes = 0;
+  for (const Tile &t : tiles) {
+    if (t.decode)
+      dec_bytes += (int64_t)t.keys * hkv * d * 2 * 2;
+    else
+      units += cdiv64(t.keys, kKeyTile) * hkv;
+  }
+  if (units == 0 || dec_bytes == 0 || M.xcds <= 0 || M.cus % M.xcds != 0) return -1;
+  const int32_t forced = g_overlap_force.load();
+  if (forced == 0) return -1;
+  if (forced > 0) return std::min(forced / M.xcds, M.cus / M.xcds / 2) * M.xcds;
+  const int64_t pre_max = std::max<int64_t>(1, units / kMinGroupKeyTiles);
+  int32_t best = 0;
+  double best_t = -1.0;
+  for (int32_t n = 0; n <= M.cus / 2; n += M.xcds) {
+    const int64_t pre = std::min<int64_t>(M.cus - n, pre_max);
+    const double tp = (double)units * kCoPrefillStepSec / (double)pre;
+    const double left = std::max(0.0, (double)dec_bytes - (double)(M.cus - pre) * kCoDecodeCuBytesPerSec * tp);
+    const double t = tp + left / kCoDecodeChipBytesPerSec;
+    if (best_t < 0.0 || t < best_t) best_t = t, best = n;
+  }
+  return best;
+}
+
 void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const pa_kv_cache *c,
                int32_t group, Plan &P, const Groups *groups = nullptr, bool step = false) {
   const int32_t hkv = c->num_kv_heads, d = c->head_dim, tile_rows = prefill_tile_rows(c);
   const MachineShape M = machine_shape();
-  const int64_t decode_target_items = (int64_t)kDecodeItemsPerCU * M.cus;
   const int64_t prefill_target_items = (int64_t)kPrefillItemsPerCU * M.cus;
   const int32_t dec_tokens = kDecodeRows / group;  // >= 1 for group <= 16
   const int32_t pre_tokens = tile_rows / group;
@@ -382,15 +479,23 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
       np0 += hkv;
     }
   }
-  const int64_t dchunk = std::min<int64_t>(
-      kMaxDecItemKeys, std::max<int64_t>(kDecodeMinChunk, cdiv64(std::max<int64_t>(wd, 1), decode_target_items)));
+  const int64_t dchunk = decode_chunk(tiles, hkv, M.cus, wd);
   int64_t pchunk = INT32_MAX;
   if (np0 > 0 && np0 < prefill_target_items)
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, prefill_target_items));
 
   const bool persistent = tile_rows == kDmaTileRows;
-  if (persistent)
-    plan_persistent(tiles, hkv, tile_rows, M, P, step ? kStepRangesPerCu : 1);
+  // co-scheduling: bf16 KV at head_dim 128 (the LDS-DMA prefill and decode),
+  // neither the one-launch step nor shared-prefix groups
+  const int32_t co = persistent && !step && group_tiles.empty() && c->dtype == PA_KV_BF16
+                         ? choose_overlap_cus(tiles, hkv, d, M) : -1;
+  if (persistent) {
+    MachineShape Mp = M;
+    Mp.cus -= std::max(co, 0);
+    plan_persistent(tiles, hkv, tile_rows, Mp, P, step ? kStepRangesPerCu : 1);
+    // the decode takes every CU the prefill launch does not hold
+    if (co >= 0 && !P.wg_first.empty()) P.overlap_cus = std::max(0, M.cus - ((int32_t)P.wg_first.size() - 1));
+  }
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
   // cascade members: the first partial slot of tile i's KV head kvh (its
@@ -516,6 +621,8 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
   off = align256(off + P.step_dec_merge.size() * sizeof(int32_t));
   P.off_ctr = off;
   off = align256(off + P.n_ctr * sizeof(uint32_t));  // zeros in the staged copy
+  P.off_claim = off;
+  off = align256(off + (P.overlap_cus > 0 ? sizeof(uint32_t) : 0));  // decode claim counter, zero
   P.plan_bytes = off;
   P.off_po_pre = off;
   off = align256(off + (size_t)P.n_part_prefill * tile_rows * d * sizeof(float));
@@ -654,6 +761,39 @@ pa_status scratch_address(unsigned char **out) {
   if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
   g_scratch.push_back({dev, (unsigned char *)p});
   *out = (unsigned char *)p;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The second stream of a co-scheduled mixed step: one per device, created on
+// first use (default priority, non-blocking), with the two events that fork
+// it from the call's stream and join it back.  A call holds g_co_mu from the
+// fork to the join, so calls from several host threads do not interleave on
+// the shared events.
+struct CoStream {
+  int device;
+  hipStream_t s2;
+  hipEvent_t fork, join;
+};
+std::mutex g_co_mu;
+std::vector<CoStream> g_co;
+
+pa_status co_stream(CoStream *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  for (const auto &c : g_co)
+    if (c.device == dev) {
+      *out = c;
+      return PA_OK;
+    }
+  CoStream c{dev, nullptr, nullptr, nullptr};
+  e = hipStreamCreateWithFlags(&c.s2, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "co-scheduling stream");
+  g_co.push_back(c);
+  *out = c;
   return PA_OK;
 }
 
@@ -951,7 +1091,45 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     if (e != hipSuccess) return hip_fail(e, "step launch");
     return PA_OK;
   }
-  if (!P.prefill.empty()) {
+  if (P.overlap_cus > 0 && !no_alloc) {
+    // Co-scheduled mixed step: the persistent prefill (its ranges cut for
+    // the CUs it leaves to the decode) on the call's stream; beside it, on
+    // the second stream, overlap_cus work-groups claim decode items from the
+    // list; after the prefill, work-groups on the CUs it frees claim the
+    // rest.  Each CU holds one work-group of either kernel (registers and
+    // LDS), and work-groups are dispatched round-robin over the XCDs, so the
+    // decode takes overlap_cus / xcds CUs of every XCD.  The merges follow
+    // the join.  (The no-allocation entry point runs the same plan's
+    // launches one after the other: same items, same results.)
+    AttnArgs ap = a;
+    ap.items = (const Item *)(ws + P.off_prefill);
+    ap.part_o = (float *)(ws + P.off_po_pre);
+    ap.part_lse = (float *)(ws + P.off_pl_pre);
+    ap.wg_first = (const int32_t *)(ws + P.off_wg);
+    const int n_pre = (int)P.wg_first.size() - 1;
+    AttnArgs ad = a;
+    ad.items = (const Item *)(ws + P.off_decode);
+    ad.wg_first = nullptr;
+    ad.part_o = (float *)(ws + P.off_po_dec);
+    ad.part_lse = (float *)(ws + P.off_pl_dec);
+    uint32_t *ctr = (uint32_t *)(ws + P.off_claim);
+    const int n_dec = (int)P.decode.size();
+    const int tail = std::max(1, machine_shape().cus - P.overlap_cus);
+    CoStream co;
+    std::lock_guard<std::mutex> lk(g_co_mu);
+    st = co_stream(&co);
+    if (st) return st;
+    if ((e = hipEventRecord(co.fork, s)) != hipSuccess) return hip_fail(e, "fork event");
+    if ((e = hipStreamWaitEvent(co.s2, co.fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    e = timed(1, s, [&] { return launch_prefill(ap, n_pre, d, bs, fmt, s); });
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    e = timed(2, co.s2, [&] { return launch_decode_claim(ad, ctr, n_dec, P.overlap_cus, bs, co.s2); });
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch (beside the prefill)");
+    e = timed(2, s, [&] { return launch_decode_claim(ad, ctr, n_dec, tail, bs, s); });
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch (after the prefill)");
+    if ((e = hipEventRecord(co.join, co.s2)) != hipSuccess) return hip_fail(e, "join event");
+    if ((e = hipStreamWaitEvent(s, co.join, 0)) != hipSuccess) return hip_fail(e, "join wait");
+  } else if (!P.prefill.empty()) {
     AttnArgs ap = a;
     ap.items = (const Item *)(ws + P.off_prefill);
     ap.part_o = (float *)(ws + P.off_po_pre);
@@ -961,7 +1139,9 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
-  if (!P.cascade.empty()) {  // one launch: the cascade items, then the decode items
+  if (P.overlap_cus > 0 && !no_alloc) {
+    // (the decode ran above)
+  } else if (!P.cascade.empty()) {  // one launch: the cascade items, then the decode items
     a.items = (const Item *)(ws + P.off_decode);
     a.wg_first = nullptr;
     a.part_o = (float *)(ws + P.off_po_dec);
@@ -1125,6 +1305,11 @@ pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_table_r
   g.total_chunks = (int64_t)ctx * g.hkv * (cache->dtype == PA_KV_MXFP4 ? cache->head_dim / 8 : g.row_bytes / 16);
   hipError_t e = launch_gather(g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return PA_OK;
+}
+
+pa_status pa_debug_overlap_cus(int32_t n) {
+  g_overlap_force.store(n < 0 ? -1 : n);
   return PA_OK;
 }
 

@@ -12,7 +12,11 @@ namespace pa {
 // power-of-two sizes: the 64-bit divisions this replaces cost more
 // instructions than the copy itself.  The four threads of a 32-element group
 // are adjacent lanes (MXFP4 reduces its largest magnitude across them).
-template <int FMT>
+// NT: bf16 rows are stored non-temporally (the kv_append kernel: the rows
+// are read back by a later kernel, if at all; 1.7% faster at 1M tokens than
+// ordinary stores); the one-launch step kernel, whose attention reads them
+// back within the launch, stores them ordinarily.
+template <int FMT, bool NT = false>
 __device__ __forceinline__ void append_chunk(const AppendArgs &a, uint32_t gid) {
   const uint32_t ch = gid & ((1u << a.lcpr) - 1);
   const uint32_t row = gid >> a.lcpr;  // (token, KV head) row of this launch
@@ -29,8 +33,13 @@ __device__ __forceinline__ void append_chunk(const AppendArgs &a, uint32_t gid) 
   const uint4 kv = gload16_nt((const unsigned char *)a.k_new + src * 2);
   const uint4 vv = gload16_nt((const unsigned char *)a.v_new + src * 2);
   if constexpr (FMT == kKvBf16) {
-    *(uint4 *)((unsigned char *)a.k_cache + dst * 2) = kv;
-    *(uint4 *)((unsigned char *)a.v_cache + dst * 2) = vv;
+    if constexpr (NT) {
+      __builtin_nontemporal_store(u32x4{kv.x, kv.y, kv.z, kv.w}, (u32x4 *)((unsigned char *)a.k_cache + dst * 2));
+      __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, (u32x4 *)((unsigned char *)a.v_cache + dst * 2));
+    } else {
+      *(uint4 *)((unsigned char *)a.k_cache + dst * 2) = kv;
+      *(uint4 *)((unsigned char *)a.v_cache + dst * 2) = vv;
+    }
   } else if constexpr (FMT == kKvMxfp4) {
     const int64_t sdst = ((blk * a.hkv + h) * (a.d >> 5) + (ch >> 2)) * a.bs + off;  // scale byte
     auto encode = [&](const uint4 x, unsigned char *codes, unsigned char *scales) {

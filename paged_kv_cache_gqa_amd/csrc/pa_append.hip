@@ -29,7 +29,7 @@ template <int FMT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
   if (gid >= a.nchunks) return;
-  append_chunk<FMT>(a, gid);
+  append_chunk<FMT, true>(a, gid);
 }
 
 // Work-list copy from a pinned host buffer into the workspace (bytes is a

@@ -1544,6 +1544,31 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
   decode_dma_item<BS, NW, NST>(a, a.items[blockIdx.x], smem_raw, bt_lds);
 }
 
+// The same decode items taken from a shared list instead of one per
+// work-group: a persistent grid whose work-groups claim item indexes from a
+// counter in the workspace (zeroed by the work-list copy; one vector atomic
+// by one lane per claim) until the list is exhausted.  The forward call
+// launches it twice over the same list and counter -- on a few CUs beside a
+// prefill launch that holds the others, and after that prefill on the CUs it
+// frees -- so a mixed step's decode streams from HBM while its prefill keeps
+// the matrix cores busy ([Agentic] §5.1-5.2: persistent work-groups taking
+// tasks from a table by index).  Items are listed longest first.
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_claim_kernel(AttnArgs a, uint32_t *ctr, int n_items) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  __shared__ int claim_s;
+  for (;;) {
+    if (threadIdx.x == 0) claim_s = (int)atomicAdd(ctr, 1u);
+    __syncthreads();
+    const int i = claim_s;
+    __syncthreads();  // (claim_s is rewritten by the next claim)
+    if (i >= n_items) break;
+    decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
+    __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
+  }
+}
+
 // =============================================================================
 // Shared-prefix cascade for bf16 KV, head_dim 128: the decode rows of the
 // members of a prefix group (up to 64 rows: NRB blocks of 16, G rows per
@@ -2661,6 +2686,18 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, int fmt, hipSt
   }
   const bool fp8 = fmt == kKvE4m3;
   PA_DISPATCH(launch_decode_t, a, n, s);
+}
+hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_items, int groups, int bs, hipStream_t s) {
+  if (n_items <= 0 || groups <= 0) return hipSuccess;
+  if (bs == 16)
+    hipLaunchKernelGGL((decode_claim_kernel<16, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(groups), dim3(64 * PA_DEC_WAVES), 0,
+                       s, a, ctr, n_items);
+  else if (bs == 64)
+    hipLaunchKernelGGL((decode_claim_kernel<64, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(groups), dim3(64 * PA_DEC_WAVES), 0,
+                       s, a, ctr, n_items);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,
                                  int n_cascade, int n_decode, int rows, int bs, hipStream_t s) {

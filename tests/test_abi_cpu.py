@@ -195,6 +195,39 @@ def test_planner_balances_persistent_prefill(palib):
     assert 1 <= len(first) - 1 < 256
 
 
+def test_planner_coschedules_mixed_steps(palib):
+    """A bf16 head-dim-128 step with prefill and decode rows: the planner
+    leaves a multiple of the XCD count of CUs (up to half) to the decode
+    beside the prefill, cuts the prefill's ranges for the rest (balanced), and
+    still covers the causal pattern exactly; steps with one kind of row, other
+    KV types and the forced settings behave as documented."""
+    import workloads as W
+    cus, xcds = palib.pa_device_shape()
+    m = W.mixed()
+    c = cache(palib, num_kv_heads=8, head_dim=128, block_size=16)
+    first = check_balance(palib, m.hist, m.incr, 32, 8)
+    n_dec = cus - (len(first) - 1)
+    assert 0 < n_dec <= cus // 2 and n_dec % xcds == 0, n_dec
+    check_cover(palib, m.hist, m.incr, 32, 8)
+    size_auto = palib.pa_workspace_size(m.hist, m.incr, 32, c)
+    try:
+        for force, want in ((0, cus), (20, cus - 16), (64, cus - 64), (1000, cus - cus // 2)):
+            palib.pa_debug_overlap_cus(force)
+            assert len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, c)) - 1 == want, force
+            check_balance(palib, m.hist, m.incr, 32, 8)
+            check_cover(palib, m.hist, m.incr, 32, 8)
+            assert palib.pa_workspace_size(m.hist, m.incr, 32, c) > 0
+    finally:
+        palib.pa_debug_overlap_cus(-1)
+    assert palib.pa_workspace_size(m.hist, m.incr, 32, c) == size_auto
+    # prefill only, decode only: nothing to co-schedule
+    assert len(palib.pa_debug_plan_groups([45_700], [2_700], 32, c)) - 1 == cus
+    # E4M3 KV: the launches one after the other
+    e4 = cache(palib, num_kv_heads=8, head_dim=128, block_size=64, dtype=palib.PA_KV_FP8_E4M3,
+               k_scale=FAKE, v_scale=FAKE)
+    assert len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, e4)) - 1 == cus
+
+
 def test_planner_covers_causal_pattern_exactly(palib):
     check_cover(palib, [256], [32], 4, 1, d=64)                  # tiny workload
     check_cover(palib, [0, 45_700, 3], [45_7, 2_700, 1], 32, 8)  # mixed classes

@@ -122,15 +122,15 @@ def local_needles(b, rows):
 PREFILL = [W.incremental(), W.initial(), W.incremental(131_072, 2_700, "incremental_128k")]
 
 
-@pytest.mark.parametrize("needled", [False, True], ids=["plain", "needles"])
-@pytest.mark.parametrize("spec", PREFILL, ids=["incremental_45.7k_to_48.4k", "initial_45.7k",
-                                               "incremental_128k"])
+# (an initial prefill has no history to hold a needle: plain only)
+@pytest.mark.parametrize("spec,needled", [(PREFILL[0], False), (PREFILL[0], True), (PREFILL[1], False),
+                                          (PREFILL[2], False), (PREFILL[2], True)],
+                         ids=["incremental_45.7k_to_48.4k-plain", "incremental_45.7k_to_48.4k-needles",
+                              "initial_45.7k-plain", "incremental_128k-plain", "incremental_128k-needles"])
 def test_single_session_prefill(palib, spec, needled):
     tiles = plan_tiles(palib, spec)
     rows = tile_boundary_rows(tiles, 0, spec.incr[0], np.random.default_rng(1))
     if needled:
-        if spec.hist[0] == 0:
-            pytest.skip("no history to hold a needle")
         spec = W.with_needles(spec, needles=[(0, r) for r in rows[::2]])
     print(f"[case] {spec.name} hist={spec.hist} incr={spec.incr} needled={needled} "
           f"tiles={len(tiles)} rows={rows}", flush=True)
