@@ -611,6 +611,7 @@ PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, 0>(pa::AttnArgs)"
 PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, 1>(pa::AttnArgs)"
 PREFILL_FP4_KERNEL = "void pa::prefill_w48_kernel<64, 2>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
+DECODE_CLAIM_KERNEL = "void pa::decode_claim_kernel<16, 4, 4>(pa::AttnArgs, unsigned int*, int)"
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
 DECODE_FP4_KERNEL = "void pa::decode_dma_fp4_kernel<64, 8, 2>(pa::AttnArgs)"
 APPEND_KERNEL = "void pa::append_kernel<0>(pa::AppendArgs)"
@@ -727,6 +728,8 @@ def summarize_profiles(out):
         fh.write("  " + PROFILE_CMDS["ktrace"] + "\n\n")
         _stats_table(fh, load("ktrace", "kernel_stats"))
         fh.write(f"\nKernel sources sha256[:16] = {src}\n")
+    if os.path.isdir(os.path.join(out, "ktrace_mixed")):
+        summarize_coscheduled(out, src)
     if os.path.isdir(os.path.join(out, "pmcx")):
         summarize_design_counters(out, src)
     with open(TRAFFIC_FILE, "w") as fh:
@@ -735,6 +738,58 @@ def summarize_profiles(out):
         for key, v in traffic.items():
             fh.write(f"{key}={v:.0f}\n")
     print(f"wrote profiles for source {src}")
+
+
+def summarize_coscheduled(out, src):
+    """profiles/decode_claim_kernel_16_4_4__mixed_step_coscheduled.txt: the
+    mixed step as the planner runs it, from a kernel trace of bench.py --only
+    mixed: per timed step, when the prefill and the two decode launches ran
+    (the first beside the prefill on a second queue, the second after it)."""
+    import csv
+    import glob
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(out, "ktrace_mixed", "*kernel_trace.csv"))[0])))
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(out, "ktrace_mixed", "*kernel_stats.csv"))[0])))
+
+    def t(r, k):
+        return int(r[k + "_Timestamp"])
+
+    pre = [r for r in rows if r["Kernel_Name"] == PREFILL_KERNEL][-10:]
+    claims = [r for r in rows if r["Kernel_Name"] == DECODE_CLAIM_KERNEL]
+    fn = os.path.join(ROOT, "profiles", "decode_claim_kernel_16_4_4__mixed_step_coscheduled.txt")
+    with open(fn, "w") as fh:
+        fh.write(f"Kernels: {PREFILL_KERNEL} and {DECODE_CLAIM_KERNEL}\n"
+                 "Workload: mixed step, co-scheduled as the planner chooses (bench.py --only mixed)\n\n"
+                 "Command (run from /tmp with TMPDIR=/tmp; OUT = output dir, REPO = repo root):\n"
+                 "  " + PROFILE_CMDS["ktrace_only"].format(w="mixed") + "\n"
+                 "  python3 REPO/bench.py --summarize-profiles OUT\n\n"
+                 "rocprofv3 --kernel-trace --stats (kernel_stats.csv rows of this run):\n")
+        _stats_table(fh, stats)
+        fh.write("\nThe last 10 steps (kernel_trace.csv), ms from the prefill's start:\n"
+                 "  prefill [start, end] (queue) | decode beside it [start, end] (queue) | "
+                 "decode after it [start, end] | prefill start to last decode end\n")
+        spans, pdur, bdur = [], [], []
+        for p in pre:
+            p0, p1 = t(p, "Start"), t(p, "End")
+            beside = [c for c in claims if t(c, "Start") < p1 and t(c, "End") > p0]
+            after = [c for c in claims if t(c, "Start") >= p1 and t(c, "Start") - p1 < 2_000_000]
+            if not beside or not after:
+                continue
+            b, a = beside[0], after[0]
+
+            def ms(x):
+                return (x - p0) / 1e6
+
+            end = max(p1, t(b, "End"), t(a, "End"))
+            spans.append(ms(end))
+            pdur.append(ms(p1))
+            bdur.append((t(b, "End") - t(b, "Start")) / 1e6)
+            fh.write(f"  [0, {ms(p1):.3f}] ({p['Queue_Id']}) | [{ms(t(b, 'Start')):.3f}, {ms(t(b, 'End')):.3f}] "
+                     f"({b['Queue_Id']}) | [{ms(t(a, 'Start')):.3f}, {ms(t(a, 'End')):.3f}] | {ms(end):.3f}\n")
+        if spans:
+            fh.write(f"\nAverages over {len(spans)} steps: prefill {sum(pdur) / len(pdur):.3f} ms, decode beside "
+                     f"it {sum(bdur) / len(bdur):.3f} ms, prefill start to last decode end "
+                     f"{sum(spans) / len(spans):.3f} ms\n")
+        fh.write(f"\nKernel sources sha256[:16] = {src}\n")
 
 
 def summarize_design_counters(out, src):
