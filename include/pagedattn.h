@@ -232,7 +232,12 @@ PA_API pa_status paged_attn_forward_cascade(const void *q, const pa_kv_cache *ca
  * with PA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (use
  * paged_attn_forward with a workspace).  Calls that overlap on one device
  * share the array and race; calls ordered on one stream are safe.  The
- * scratch keeps the last call's contents; no call relies on them.
+ * scratch keeps the last call's contents; no call relies on them.  The work
+ * list is copied from a host buffer that lives only for the call, so a call
+ * recorded by stream capture must not be replayed as a graph (each eager
+ * call, the intended use here, copies its own list).  A co-scheduled mixed
+ * step (see paged_attn_forward) runs its launches one after the other here,
+ * on `stream` alone, with the same results.
  */
 PA_API pa_status paged_attn_forward_noalloc(const void *q, const pa_kv_cache *cache,
                                             const int32_t *block_tables, int32_t max_blocks_per_seq,
