@@ -393,8 +393,8 @@ int64_t decode_chunk(const std::vector<Tile> &tiles, int32_t hkv, int32_t cus, i
 // co-scheduling).  Unit costs, MI355X: a 384-row tile's 64-key step of one
 // KV head takes a CU ~2.47 us; the decode streams ~38 GB/s per CU beside the
 // prefill and ~6.5 TB/s over the whole chip.  (The mixed step of 4
-// incremental prefills and 48 decodes: 12.55 ms one after the other, 11.7 ms
-// with 48 to 64 decode CUs.)
+// incremental prefills and 48 decodes: 12.55 ms one after the other; 11.5 ms
+// with the 56 decode CUs the model picks, 11.7-12.0 ms with 32 to 48 or 64.)
 constexpr double kCoPrefillStepSec = 2.47e-6;
 constexpr double kCoDecodeCuBytesPerSec = 38e9;
 constexpr double kCoDecodeChipBytesPerSec = 6.5e12;
@@ -791,7 +791,12 @@ pa_status co_stream(CoStream *out) {
   e = hipStreamCreateWithFlags(&c.s2, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming);
-  if (e != hipSuccess) return hip_fail(e, "co-scheduling stream");
+  if (e != hipSuccess) {
+    if (c.join) (void)hipEventDestroy(c.join);
+    if (c.fork) (void)hipEventDestroy(c.fork);
+    if (c.s2) (void)hipStreamDestroy(c.s2);
+    return hip_fail(e, "co-scheduling stream");
+  }
   g_co.push_back(c);
   *out = c;
   return PA_OK;
