@@ -403,11 +403,14 @@ std::atomic<int32_t> g_overlap_force{-1};  // pa_debug_overlap_cus: < 0 the mode
 // Returns the CUs taken from the prefill's share (-1: no co-scheduling).  A
 // prefill too small to fill every CU (at least kMinGroupKeyTiles steps per
 // work-group) leaves the rest to the decode at no cost.
-int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int32_t hkv, int32_t d, const MachineShape &M) {
-  int64_t units = 0, dec_bytes = 0;
+// shared_keys: the keys the cascade items read once for all members of
+// their groups (members' own keys count from the end of the shared prefix).
+int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int64_t shared_keys, int32_t hkv, int32_t d,
+                           const MachineShape &M) {
+  int64_t units = 0, dec_bytes = shared_keys * hkv * d * 2 * 2;
   for (const Tile &t : tiles) {
     if (t.decode)
-      dec_bytes += (int64_t)t.keys * hkv * d * 2 * 2;
+      dec_bytes += (int64_t)(t.keys - t.shared) * hkv * d * 2 * 2;
     else
       units += cdiv64(t.keys, kKeyTile) * hkv;
   }
@@ -486,9 +489,12 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
 
   const bool persistent = tile_rows == kDmaTileRows;
   // co-scheduling: bf16 KV at head_dim 128 (the LDS-DMA prefill and decode),
-  // neither the one-launch step nor shared-prefix groups
-  const int32_t co = persistent && !step && group_tiles.empty() && c->dtype == PA_KV_BF16
-                         ? choose_overlap_cus(tiles, hkv, d, M) : -1;
+  // not the one-launch step
+  int64_t shared_keys = 0;
+  for (const auto &v : group_tiles)
+    if (!v.empty()) shared_keys += tiles[v[0]].shared;
+  const int32_t co = persistent && !step && c->dtype == PA_KV_BF16
+                         ? choose_overlap_cus(tiles, shared_keys, hkv, d, M) : -1;
   if (persistent) {
     MachineShape Mp = M;
     Mp.cus -= std::max(co, 0);
@@ -1099,9 +1105,9 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   if (P.overlap_cus > 0 && !no_alloc) {
     // Co-scheduled mixed step: the persistent prefill (its ranges cut for
     // the CUs it leaves to the decode) on the call's stream; beside it, on
-    // the second stream, overlap_cus work-groups claim decode items from the
-    // list; after the prefill, work-groups on the CUs it frees claim the
-    // rest.  Each CU holds one work-group of either kernel (registers and
+    // the second stream, overlap_cus work-groups claim the decode launch's
+    // items (shared-prefix cascade items first, if any) from the list; after
+    // the prefill, work-groups on the CUs it frees claim the rest.  Each CU holds one work-group of either kernel (registers and
     // LDS), and work-groups are dispatched round-robin over the XCDs, so the
     // decode takes overlap_cus / xcds CUs of every XCD.  The merges follow
     // the join.  (The no-allocation entry point runs the same plan's
@@ -1119,6 +1125,9 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     ad.part_lse = (float *)(ws + P.off_pl_dec);
     uint32_t *ctr = (uint32_t *)(ws + P.off_claim);
     const int n_dec = (int)P.decode.size();
+    const CascadeItem *citems = (const CascadeItem *)(ws + P.off_cascade);
+    const CascadeMember *members = (const CascadeMember *)(ws + P.off_members);
+    const int n_casc = (int)P.cascade.size();
     const int tail = std::max(1, machine_shape().cus - P.overlap_cus);
     CoStream co;
     std::lock_guard<std::mutex> lk(g_co_mu);
@@ -1128,9 +1137,13 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     if ((e = hipStreamWaitEvent(co.s2, co.fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
     e = timed(1, s, [&] { return launch_prefill(ap, n_pre, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-    e = timed(2, co.s2, [&] { return launch_decode_claim(ad, ctr, n_dec, P.overlap_cus, bs, co.s2); });
+    e = timed(2, co.s2, [&] {
+      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, P.overlap_cus, bs, co.s2);
+    });
     if (e != hipSuccess) return hip_fail(e, "decode attention launch (beside the prefill)");
-    e = timed(2, s, [&] { return launch_decode_claim(ad, ctr, n_dec, tail, bs, s); });
+    e = timed(2, s, [&] {
+      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, tail, bs, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "decode attention launch (after the prefill)");
     if ((e = hipEventRecord(co.join, co.s2)) != hipSuccess) return hip_fail(e, "join event");
     if ((e = hipStreamWaitEvent(s, co.join, 0)) != hipSuccess) return hip_fail(e, "join wait");

@@ -1544,31 +1544,6 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
   decode_dma_item<BS, NW, NST>(a, a.items[blockIdx.x], smem_raw, bt_lds);
 }
 
-// The same decode items taken from a shared list instead of one per
-// work-group: a persistent grid whose work-groups claim item indexes from a
-// counter in the workspace (zeroed by the work-list copy; one vector atomic
-// by one lane per claim) until the list is exhausted.  The forward call
-// launches it twice over the same list and counter -- on a few CUs beside a
-// prefill launch that holds the others, and after that prefill on the CUs it
-// frees -- so a mixed step's decode streams from HBM while its prefill keeps
-// the matrix cores busy ([Agentic] §5.1-5.2: persistent work-groups taking
-// tasks from a table by index).  Items are listed longest first.
-template <int BS, int NW, int NST>
-__global__ __launch_bounds__(64 * NW, 1) void decode_claim_kernel(AttnArgs a, uint32_t *ctr, int n_items) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
-  __shared__ int claim_s;
-  for (;;) {
-    if (threadIdx.x == 0) claim_s = (int)atomicAdd(ctr, 1u);
-    __syncthreads();
-    const int i = claim_s;
-    __syncthreads();  // (claim_s is rewritten by the next claim)
-    if (i >= n_items) break;
-    decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
-    __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
-  }
-}
-
 // =============================================================================
 // Shared-prefix cascade for bf16 KV, head_dim 128: the decode rows of the
 // members of a prefix group (up to 64 rows: NRB blocks of 16, G rows per
@@ -1769,6 +1744,42 @@ __global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, cons
     cascade_item<BS, NRB>(a, citems[blockIdx.x], members, smem_raw, bt_lds);
   else
     decode_dma_item<BS, 4, kDecStages>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
+}
+
+// The decode launch's items (the cascade items, if any, then the decode
+// items) taken from a shared list instead of one per work-group: a
+// persistent grid whose work-groups claim item indexes from a counter in the
+// workspace (zeroed by the work-list copy; one vector atomic by one lane per
+// claim) until the list is exhausted.  The forward call launches it twice
+// over the same list and counter -- on a few CUs beside a prefill launch that
+// holds the others, and after that prefill on the CUs it frees -- so a mixed
+// step's decode streams from HBM while its prefill keeps the matrix cores
+// busy ([Agentic] §5.1-5.2: persistent work-groups taking tasks from a table
+// by index).  Items are listed longest first (cascade items first).  NRB = 0:
+// no cascade items.
+template <int BS, int NRB>
+__global__ __launch_bounds__(256, 1) void decode_claim_kernel(AttnArgs a, uint32_t *ctr, int n_items,
+                                                              const CascadeItem *citems,
+                                                              const CascadeMember *members, int n_cascade) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kDecStages * 2 * kDecSliceBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  __shared__ int claim_s;
+  for (;;) {
+    if (threadIdx.x == 0) claim_s = (int)atomicAdd(ctr, 1u);
+    __syncthreads();
+    const int i = claim_s;
+    __syncthreads();  // (claim_s is rewritten by the next claim)
+    if (i >= n_items) break;
+    if constexpr (NRB > 0) {
+      if (i < n_cascade)
+        cascade_item<BS, NRB>(a, citems[i], members, smem_raw, bt_lds);
+      else
+        decode_dma_item<BS, 4, kDecStages>(a, a.items[i - n_cascade], smem_raw, bt_lds);
+    } else {
+      decode_dma_item<BS, 4, kDecStages>(a, a.items[i], smem_raw, bt_lds);
+    }
+    __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
+  }
 }
 
 // =============================================================================
@@ -2687,16 +2698,28 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, int fmt, hipSt
   const bool fp8 = fmt == kKvE4m3;
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
-hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_items, int groups, int bs, hipStream_t s) {
-  if (n_items <= 0 || groups <= 0) return hipSuccess;
-  if (bs == 16)
-    hipLaunchKernelGGL((decode_claim_kernel<16, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(groups), dim3(64 * PA_DEC_WAVES), 0,
-                       s, a, ctr, n_items);
-  else if (bs == 64)
-    hipLaunchKernelGGL((decode_claim_kernel<64, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(groups), dim3(64 * PA_DEC_WAVES), 0,
-                       s, a, ctr, n_items);
-  else
-    return hipErrorInvalidValue;
+hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_decode, const CascadeItem *citems,
+                               const CascadeMember *members, int n_cascade, int rows, int groups, int bs,
+                               hipStream_t s) {
+  const int n = n_cascade + n_decode;
+  if (n <= 0 || groups <= 0) return hipSuccess;
+  if ((n_cascade > 0 && (rows <= 0 || rows > kCascadeRows)) || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
+  static_assert(PA_DEC_WAVES == 4, "the claiming decode launch runs 4-wave work-groups");
+#define PA_CLAIM(B, R)                                                                                        \
+  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(256), 0, s, a, ctr, n, citems, members, \
+                     n_cascade)
+  if (bs == 16) {
+    if (n_cascade == 0) PA_CLAIM(16, 0);
+    else if (rows <= 16) PA_CLAIM(16, 1);
+    else if (rows <= 32) PA_CLAIM(16, 2);
+    else PA_CLAIM(16, 4);
+  } else {
+    if (n_cascade == 0) PA_CLAIM(64, 0);
+    else if (rows <= 16) PA_CLAIM(64, 1);
+    else if (rows <= 32) PA_CLAIM(64, 2);
+    else PA_CLAIM(64, 4);
+  }
+#undef PA_CLAIM
   return hipGetLastError();
 }
 hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, const CascadeMember *members,

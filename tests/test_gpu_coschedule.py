@@ -103,3 +103,45 @@ def test_small_prefill_leaves_cus_to_the_decode(palib):
     assert_lse(lse, ref_lse, lse_bounds(b, after), spec.name)
     out0, _ = _forced(palib, b, c, 0)
     assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+
+
+def test_coscheduled_cascade(palib):
+    """paged_attn_forward_cascade co-schedules too: the cascade items (the
+    shared prefix read once for its members) and the decode items are
+    claimed beside the prefill.  Sub-agents over a 4,096-token shared prefix,
+    other decodes and an increment long enough to fill every CU: forced 0
+    and 64 CUs and the planner's choice, every decode row bitwise equal
+    across the modes, sampled rows within the bars against the oracle."""
+    from tests.test_gpu_cascade import cascade_step
+    big = 2000
+    hist = [20_000, 9000, 7000, 12_000, 5000, 30_000, 8000, 6000]
+    incr = [big, 1, 1, 1, 1, 1, 1, 1]
+    members = [1, 2, 3, 4]
+    spec = W.with_needles(
+        W.Spec("co_cascade", 93, 32, 8, 128, 16, hist, incr, shared_prefix_tokens=4096, shared_seqs=members),
+        needles=[(0, 0), (0, big - 1), (1, 0), (3, 0), (5, 0)])
+    group_of = [0 if s in members else -1 for s in range(len(hist))]
+    print(f"[case] co-scheduled cascade hist={hist} incr={incr} members={members}", flush=True)
+    b = W.make_batch(spec, DEV)
+    host = host_caches(b)
+    rows = sorted({0, 95, 96, 1000, big - 1} | set(range(big, big + 7)))
+    ref, ref_lse, after = oracle_step(
+        b, rows=rows, caches=tuple(x.copy() if isinstance(x, np.ndarray) else x for x in host))
+    bound = lse_bounds(b, after)[rows]
+    at = {r: i for i, r in enumerate(rows)}
+    needles = [(at[r], h) for r, h, _, _ in b.needles if r in at]
+    outs = {}
+    for force in (0, 64, -1):
+        palib.pa_debug_overlap_cus(force)
+        try:
+            out, lse, _ = cascade_step(palib, b, group_of, [4096],
+                                       tuple(x.copy() if isinstance(x, np.ndarray) else x for x in host))
+        finally:
+            palib.pa_debug_overlap_cus(-1)
+        what = f"co-scheduled cascade, CUs taken from the prefill {force}"
+        assert_parity(out[rows], ref, False, what, needles=needles)
+        assert_lse(lse[rows], ref_lse, bound, what)
+        outs[force] = out
+    dec = slice(big, big + 7)
+    for force in (64, -1):
+        assert torch.equal(outs[force][dec].view(torch.int16), outs[0][dec].view(torch.int16)), force
