@@ -610,7 +610,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, 0>(pa::AttnArgs)"
 PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, 1>(pa::AttnArgs)"
 PREFILL_FP4_KERNEL = "void pa::prefill_w48_kernel<64, 2>(pa::AttnArgs)"
-DECODE_KERNEL = "void pa::decode_dma_kernel<16, 4, 4>(pa::AttnArgs)"
+DECODE_KERNEL = "void pa::decode_dma_kernel<16, 8, 2>(pa::AttnArgs)"
 DECODE_CLAIM_KERNEL = ("void pa::decode_claim_kernel<16, 0>(pa::AttnArgs, unsigned int*, int, pa::CascadeItem const*, "
                        "pa::CascadeMember const*, int)")
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
@@ -982,7 +982,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(byts / (dk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_batch_bytes"),
-                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_kernel<16, 4, 4>",
+                         "algorithmic_bytes": int(byts), "kernel": "decode_dma_kernel<16, 8, 2>",
                          "kernel_ms": round(dk_ms, 4)},
         }
         del r

@@ -146,6 +146,7 @@ struct Plan {
   // each partial slot, the task counters
   std::vector<int32_t> step_queue, step_queue_off, step_pre_merge, step_dec_merge;
   int32_t step_xcds = 1, step_ranges = 0;
+  int32_t step_decode_cus = 0;  // one-launch step: CUs that take decode items first
   size_t n_ctr = 0;
   // co-scheduled mixed step: CUs that stream decode items beside the
   // persistent prefill launch (0: the launches run one after the other)
@@ -383,20 +384,21 @@ int64_t decode_chunk(const std::vector<Tile> &tiles, int32_t hkv, int32_t cus, i
 // streams from HBM and computes little.  A CU streams more than its 1/256
 // share of the chip's bandwidth when few CUs stream (measured with the
 // LDS-filling read alone: 59 GB/s per CU with 32 CUs, 55 with 64, 48 with
-// 128, 28 with all 256; the decode items beside the prefill: ~38 GB/s per
-// CU), so a few CUs given to the decode while the others prefill stream most
-// of it before the prefill ends.  The candidates are multiples of the XCD
-// count (an equal number per XCD, so the prefill's ranges stay balanced per
-// XCD) up to half the CUs; the time of each is predicted as the prefill on
-// the remaining CUs plus the decode bytes those few CUs could not stream
-// meanwhile, streamed afterwards by the whole chip; the shortest wins (0: no
-// co-scheduling).  Unit costs, MI355X: a 384-row tile's 64-key step of one
-// KV head takes a CU ~2.47 us; the decode streams ~38 GB/s per CU beside the
-// prefill and ~6.5 TB/s over the whole chip.  (The mixed step of 4
-// incremental prefills and 48 decodes: 12.55 ms one after the other; 11.5 ms
-// with the 56 decode CUs the model picks, 11.7-12.0 ms with 32 to 48 or 64.)
+// 128, 28 with all 256; the decode items beside the prefill: ~45 GB/s per CU
+// with 8-wave work-groups), so a few CUs given to the decode while the others
+// prefill stream most of it before the prefill ends.  The candidates are
+// multiples of the XCD count (an equal number per XCD, so the prefill's
+// ranges stay balanced per XCD) up to half the CUs; the time of each is
+// predicted as the prefill on the remaining CUs plus the decode bytes those
+// few CUs could not stream meanwhile, streamed afterwards by the whole chip;
+// the shortest wins (0: no co-scheduling).  Unit costs, MI355X: a 384-row
+// tile's 64-key step of one KV head takes a CU ~2.47 us; the decode streams
+// ~45 GB/s per CU beside the prefill and ~6.5 TB/s over the whole chip.
+// (The mixed step of 4 incremental prefills and 48 decodes: 12.6 ms one
+// after the other; 11.0 ms with the 48 decode CUs the model picks, 11.3-11.5
+// with 40 or 56; the one-launch step likewise 12.1 -> 10.9 ms.)
 constexpr double kCoPrefillStepSec = 2.47e-6;
-constexpr double kCoDecodeCuBytesPerSec = 38e9;
+constexpr double kCoDecodeCuBytesPerSec = 45e9;
 constexpr double kCoDecodeChipBytesPerSec = 6.5e12;
 std::atomic<int32_t> g_overlap_force{-1};  // pa_debug_overlap_cus: < 0 the model's choice
 
@@ -488,19 +490,20 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, prefill_target_items));
 
   const bool persistent = tile_rows == kDmaTileRows;
-  // co-scheduling: bf16 KV at head_dim 128 (the LDS-DMA prefill and decode),
-  // not the one-launch step
+  // co-scheduling: bf16 KV at head_dim 128 (the LDS-DMA prefill and decode);
+  // in the one-launch step, some work-groups take decode items first
   int64_t shared_keys = 0;
   for (const auto &v : group_tiles)
     if (!v.empty()) shared_keys += tiles[v[0]].shared;
-  const int32_t co = persistent && !step && c->dtype == PA_KV_BF16
-                         ? choose_overlap_cus(tiles, shared_keys, hkv, d, M) : -1;
+  const int32_t co = persistent && c->dtype == PA_KV_BF16 ? choose_overlap_cus(tiles, shared_keys, hkv, d, M) : -1;
   if (persistent) {
     MachineShape Mp = M;
     Mp.cus -= std::max(co, 0);
     plan_persistent(tiles, hkv, tile_rows, Mp, P, step ? kStepRangesPerCu : 1);
-    // the decode takes every CU the prefill launch does not hold
-    if (co >= 0 && !P.wg_first.empty()) P.overlap_cus = std::max(0, M.cus - ((int32_t)P.wg_first.size() - 1));
+    if (step)
+      P.step_decode_cus = std::max(co, 0);
+    else if (co >= 0 && !P.wg_first.empty())  // the decode takes every CU the prefill launch does not hold
+      P.overlap_cus = std::max(0, M.cus - ((int32_t)P.wg_first.size() - 1));
   }
   std::vector<std::vector<Item>> pre_by_head(hkv);
   std::vector<std::pair<int32_t, int32_t>> ranges;
@@ -1025,6 +1028,15 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
   put(P.off_sdm, P.step_dec_merge);  // (the counters stay zero)
   hipStream_t s = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
+  // the co-scheduling stream is made (once per device) before anything is
+  // enqueued, so a failure there leaves everything untouched
+  const bool coschedule = P.overlap_cus > 0 && !no_alloc;
+  CoStream co{};
+  if (coschedule) {
+    std::lock_guard<std::mutex> lk(g_co_mu);
+    st = co_stream(&co);
+    if (st) return st;
+  }
   if (no_alloc) {
     hipError_t e = hipMemcpyAsync(ws, host.data(), P.plan_bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "work-list copy");
@@ -1096,13 +1108,14 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     sa.n_append_tasks = (int32_t)((sa.app.nchunks + kStepAppendChunks - 1) / kStepAppendChunks);
     sa.n_decode = (int32_t)P.decode.size();
     sa.xcds = P.step_xcds;
+    sa.decode_first = P.step_xcds > 1 ? P.step_decode_cus / P.step_xcds : P.step_decode_cus;
     const int64_t tasks = (int64_t)sa.n_append_tasks + P.step_ranges + sa.n_decode;
     const int groups_n = (int)std::max<int64_t>(1, std::min<int64_t>(machine_shape().cus, tasks));
     e = timed(4, s, [&] { return launch_step(sa, groups_n, bs, s); });
     if (e != hipSuccess) return hip_fail(e, "step launch");
     return PA_OK;
   }
-  if (P.overlap_cus > 0 && !no_alloc) {
+  if (coschedule) {
     // Co-scheduled mixed step: the persistent prefill (its ranges cut for
     // the CUs it leaves to the decode) on the call's stream; beside it, on
     // the second stream, overlap_cus work-groups claim the decode launch's
@@ -1129,10 +1142,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     const CascadeMember *members = (const CascadeMember *)(ws + P.off_members);
     const int n_casc = (int)P.cascade.size();
     const int tail = std::max(1, machine_shape().cus - P.overlap_cus);
-    CoStream co;
     std::lock_guard<std::mutex> lk(g_co_mu);
-    st = co_stream(&co);
-    if (st) return st;
     if ((e = hipEventRecord(co.fork, s)) != hipSuccess) return hip_fail(e, "fork event");
     if ((e = hipStreamWaitEvent(co.s2, co.fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
     e = timed(1, s, [&] { return launch_prefill(ap, n_pre, d, bs, fmt, s); });
@@ -1157,7 +1167,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     e = timed(1, s, [&] { return launch_prefill(ap, n, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   }
-  if (P.overlap_cus > 0 && !no_alloc) {
+  if (coschedule) {
     // (the decode ran above)
   } else if (!P.cascade.empty()) {  // one launch: the cascade items, then the decode items
     a.items = (const Item *)(ws + P.off_decode);

@@ -1385,10 +1385,21 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnArgs a) {
 
 constexpr int kDecSlice = 16;                      // keys per wave step
 constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4 KB
-#ifndef PA_DEC_STAGES
-#define PA_DEC_STAGES 4
+// waves per work-group and ring stages per wave of the bf16 decode items (the
+// decode launch and the claiming decode launch): 8 x 2 and 4 x 4 stream the
+// same over the whole chip (64 sessions: 5.629 against 5.628 ms), but beside
+// a prefill 8 x 2 streams more per CU (the co-scheduled mixed step: 11.02 ms
+// with 48 decode CUs against 11.33 ms at best with 4 x 4); the cascade launch
+// runs 4-wave work-groups of kCascadeStages
+#ifndef PA_DEC_WAVES
+#define PA_DEC_WAVES 8
 #endif
+#ifndef PA_DEC_STAGES
+#define PA_DEC_STAGES 2
+#endif
+constexpr int kDecWaves = PA_DEC_WAVES;
 constexpr int kDecStages = PA_DEC_STAGES;
+constexpr int kCascadeStages = 4;
 
 template <int BS, int NW, int NST>
 __device__ __forceinline__ void decode_dma_item(const AttnArgs &a, const Item it, unsigned char *smem_raw,
@@ -1562,7 +1573,7 @@ __device__ __forceinline__ void cascade_item(const AttnArgs &a, const CascadeIte
   constexpr int NCK = D / 32;
   constexpr int ND = D / 16;
   constexpr int NW = 4;
-  constexpr int NST = kDecStages;
+  constexpr int NST = kCascadeStages;
   constexpr int SB = kDecSliceBytes;
   static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
   lds_u8 *smem = (lds_u8 *)smem_raw;
@@ -1738,12 +1749,12 @@ __device__ __forceinline__ void cascade_item(const AttnArgs &a, const CascadeIte
 template <int BS, int NRB>
 __global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, const CascadeItem *citems,
                                                                 const CascadeMember *members, int n_cascade) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kDecStages * 2 * kDecSliceBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kCascadeStages * 2 * kDecSliceBytes];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   if ((int)blockIdx.x < n_cascade)
     cascade_item<BS, NRB>(a, citems[blockIdx.x], members, smem_raw, bt_lds);
   else
-    decode_dma_item<BS, 4, kDecStages>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
+    decode_dma_item<BS, 4, kCascadeStages>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
 }
 
 // The decode launch's items (the cascade items, if any, then the decode
@@ -1757,11 +1768,14 @@ __global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, cons
 // busy ([Agentic] §5.1-5.2: persistent work-groups taking tasks from a table
 // by index).  Items are listed longest first (cascade items first).  NRB = 0:
 // no cascade items.
+// (with cascade items: the cascade launch's 4-wave work-groups; without: the
+// decode launch's shape, so that every item is computed as there)
 template <int BS, int NRB>
-__global__ __launch_bounds__(256, 1) void decode_claim_kernel(AttnArgs a, uint32_t *ctr, int n_items,
-                                                              const CascadeItem *citems,
-                                                              const CascadeMember *members, int n_cascade) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kDecStages * 2 * kDecSliceBytes];
+__global__ __launch_bounds__(64 * (NRB > 0 ? 4 : kDecWaves), 1) void decode_claim_kernel(
+    AttnArgs a, uint32_t *ctr, int n_items, const CascadeItem *citems, const CascadeMember *members, int n_cascade) {
+  constexpr int NW = NRB > 0 ? 4 : kDecWaves;
+  constexpr int NST = NRB > 0 ? kCascadeStages : kDecStages;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   __shared__ int claim_s;
   for (;;) {
@@ -1774,9 +1788,9 @@ __global__ __launch_bounds__(256, 1) void decode_claim_kernel(AttnArgs a, uint32
       if (i < n_cascade)
         cascade_item<BS, NRB>(a, citems[i], members, smem_raw, bt_lds);
       else
-        decode_dma_item<BS, 4, kDecStages>(a, a.items[i - n_cascade], smem_raw, bt_lds);
+        decode_dma_item<BS, 4, kCascadeStages>(a, a.items[i - n_cascade], smem_raw, bt_lds);
     } else {
-      decode_dma_item<BS, 4, kDecStages>(a, a.items[i], smem_raw, bt_lds);
+      decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
     }
     __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
   }
@@ -2453,6 +2467,10 @@ __global__ __launch_bounds__(256) void merge_many_kernel(MergeArgs a, int first)
 //      planner puts one KV head's ranges on one XCD for L2 reuse), then the
 //      other XCDs' queues;
 //   4. decode items (eight waves, two stages).
+// Co-scheduled (decode_first > 0): the first decode_first work-groups of
+// each XCD past the wait take decode items before prefill ranges, so the
+// decode streams from HBM on those CUs while the others' matrix cores run
+// the prefill (the planner cuts the prefill ranges for the rest).
 // A split tile's partials are merged by the work-group that writes its last
 // part: after its partial stores, one lane releases them at device scope and
 // counts the part in; the one that completes the count acquires and merges
@@ -2503,7 +2521,7 @@ __device__ __forceinline__ void step_merge(const MergeArgs &a, const Merge mt) {
 // units stream the decode part while the rest compute prefill, measured
 // slower: 12.5-12.6 ms against 12.3-12.4 ms for the mixed step.)
 __device__ __forceinline__ int step_claim(const StepArgs &s, int &phase, uint32_t xcc, bool &waited,
-                                          bool &dec_empty) {
+                                          bool &dec_empty, bool &dec_first) {
   uint32_t *c = s.ctr;
   if (phase == 0) {
     const uint32_t i = atomicAdd(&c[kCtrAppendNext], 1u);
@@ -2522,6 +2540,12 @@ __device__ __forceinline__ int step_claim(const StepArgs &s, int &phase, uint32_
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     waited = true;
+    dec_first = s.decode_first > 0 && atomicAdd(&c[kCtrRole + xcc], 1u) < (uint32_t)s.decode_first;
+  }
+  if (dec_first && !dec_empty) {
+    const uint32_t i = atomicAdd(&c[kCtrDecodeNext], 1u);
+    if (i < (uint32_t)s.n_decode) return (kTaskDecode << 28) | (int)i;
+    dec_empty = true;
   }
   while (phase <= s.xcds) {  // phase p: the prefill queue of XCD (xcc + p - 1) % xcds
     const int q = (int)((xcc + (uint32_t)phase - 1) % (uint32_t)s.xcds);
@@ -2553,7 +2577,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   xcc %= (uint32_t)s.xcds;
   int phase = 0;
-  bool waited = false, dec_empty = false;
+  bool waited = false, dec_empty = false, dec_first = false;
   // after a task's partial stores: count the part in; the last one merges
   auto part_done = [&](int merge) __attribute__((always_inline)) {
     PA_WAIT_VMCNT(0);
@@ -2569,7 +2593,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
     if (merge_s >= 0) step_merge(s.mg, s.mg.merges[merge_s]);
   };
   for (;;) {
-    if (tid == 0) task_s = step_claim(s, phase, xcc, waited, dec_empty);
+    if (tid == 0) task_s = step_claim(s, phase, xcc, waited, dec_empty, dec_first);
     __syncthreads();
     const int t = task_s;
     __syncthreads();  // (task_s is rewritten by the next claim)
@@ -2628,10 +2652,7 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 #ifndef PA_DECODE_DMA
 #define PA_DECODE_DMA 1
 #endif
-// decode: waves per work-group and ring stages per wave (bf16, E4M3)
-#ifndef PA_DEC_WAVES
-#define PA_DEC_WAVES 4
-#endif
+// E4M3 decode: waves per work-group and ring stages per wave
 #ifndef PA_DEC8_WAVES
 #define PA_DEC8_WAVES 8
 #endif
@@ -2641,7 +2662,7 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
-    hipLaunchKernelGGL((decode_dma_kernel<BS, PA_DEC_WAVES, PA_DEC_STAGES>), dim3(n), dim3(64 * PA_DEC_WAVES), 0, s, a);
+    hipLaunchKernelGGL((decode_dma_kernel<BS, kDecWaves, kDecStages>), dim3(n), dim3(64 * kDecWaves), 0, s, a);
     return hipGetLastError();
   }
   if constexpr (FP8 && D == 128 && PA_DECODE_DMA) {
@@ -2704,10 +2725,9 @@ hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_decode, c
   const int n = n_cascade + n_decode;
   if (n <= 0 || groups <= 0) return hipSuccess;
   if ((n_cascade > 0 && (rows <= 0 || rows > kCascadeRows)) || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
-  static_assert(PA_DEC_WAVES == 4, "the claiming decode launch runs 4-wave work-groups");
-#define PA_CLAIM(B, R)                                                                                        \
-  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(256), 0, s, a, ctr, n, citems, members, \
-                     n_cascade)
+#define PA_CLAIM(B, R)                                                                                \
+  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(64 * (R > 0 ? 4 : kDecWaves)), 0, s, \
+                     a, ctr, n, citems, members, n_cascade)
   if (bs == 16) {
     if (n_cascade == 0) PA_CLAIM(16, 0);
     else if (rows <= 16) PA_CLAIM(16, 1);
@@ -2726,7 +2746,6 @@ hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, co
                                  int n_cascade, int n_decode, int rows, int bs, hipStream_t s) {
   if (n_cascade + n_decode <= 0) return hipSuccess;
   if (rows <= 0 || rows > kCascadeRows || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
-  static_assert(PA_DEC_WAVES == 4, "the fused decode launch runs 4-wave work-groups");
   const dim3 grid(n_cascade + n_decode);
 #define PA_CASCADE(B, R) \
   hipLaunchKernelGGL((decode_cascade_kernel<B, R>), grid, dim3(256), 0, s, a, items, members, n_cascade)

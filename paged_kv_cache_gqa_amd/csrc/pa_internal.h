@@ -154,7 +154,8 @@ constexpr int kCtrDecodeNext = 2;   // next decode item
 constexpr int kCtrFlags = 3;        // bit 0: a bounded wait gave up (never expected)
 constexpr int kCtrPrefillNext = 4;  // [kMaxXcds] next range of each XCD's prefill queue
 constexpr int kMaxXcds = 8;
-constexpr int kCtrMerge = kCtrPrefillNext + kMaxXcds;  // [n_merges] partials written per merge record
+constexpr int kCtrRole = kCtrPrefillNext + kMaxXcds;  // [kMaxXcds] work-groups of each XCD past the append wait
+constexpr int kCtrMerge = kCtrRole + kMaxXcds;        // [n_merges] partials written per merge record
 constexpr int kStepThreads = 512;
 constexpr int kStepAppendChunks = 8 * kStepThreads;  // 16-byte append chunks per append task
 
@@ -172,6 +173,7 @@ struct StepArgs {
   int32_t n_append_tasks;
   int32_t n_decode;
   int32_t xcds;                  // queues in use (1 .. kMaxXcds)
+  int32_t decode_first;          // work-groups per XCD that take decode items before prefill ranges
 };
 
 hipError_t launch_step(const StepArgs &a, int n_groups, int bs, hipStream_t s);
