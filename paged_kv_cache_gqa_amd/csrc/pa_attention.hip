@@ -1389,8 +1389,10 @@ constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4
 // decode launch and the claiming decode launch): 8 x 2 and 4 x 4 stream the
 // same over the whole chip (64 sessions: 5.629 against 5.628 ms), but beside
 // a prefill 8 x 2 streams more per CU (the co-scheduled mixed step: 11.02 ms
-// with 48 decode CUs against 11.33 ms at best with 4 x 4); the cascade launch
-// runs 4-wave work-groups of kCascadeStages
+// with 48 decode CUs against 11.33 ms at best with 4 x 4; with prefix groups
+// 11.16 against 11.65 ms).  The cascade launch (and the claiming launch with
+// cascade items) takes the same shape, except for 64-row cascade tiles,
+// whose member rows need the registers of four waves (eight spill)
 #ifndef PA_DEC_WAVES
 #define PA_DEC_WAVES 8
 #endif
@@ -1399,7 +1401,8 @@ constexpr int kDecSliceBytes = kDecSlice * 128 * 2;  // K (or V) of one slice, 4
 #endif
 constexpr int kDecWaves = PA_DEC_WAVES;
 constexpr int kDecStages = PA_DEC_STAGES;
-constexpr int kCascadeStages = 4;
+constexpr int cascade_waves(int nrb) { return nrb >= 4 ? 4 : kDecWaves; }
+constexpr int cascade_stages(int nrb) { return nrb >= 4 ? 4 : kDecStages; }
 
 template <int BS, int NW, int NST>
 __device__ __forceinline__ void decode_dma_item(const AttnArgs &a, const Item it, unsigned char *smem_raw,
@@ -1566,14 +1569,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_kernel(AttnArgs a) {
 // prefix lies before every member's own token); keys past the range end are
 // masked.  The four waves' states are combined per row block through LDS and
 // each member's rows go to its partial slot (row g of the slot = its head g).
-template <int BS, int NRB>
+template <int BS, int NRB, int NW, int NST>
 __device__ __forceinline__ void cascade_item(const AttnArgs &a, const CascadeItem it, const CascadeMember *members,
                                              unsigned char *smem_raw, int *bt_lds) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;
   constexpr int ND = D / 16;
-  constexpr int NW = 4;
-  constexpr int NST = kCascadeStages;
   constexpr int SB = kDecSliceBytes;
   static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
   lds_u8 *smem = (lds_u8 *)smem_raw;
@@ -1747,14 +1748,15 @@ __device__ __forceinline__ void cascade_item(const AttnArgs &a, const CascadeIte
 // [0, n_cascade) run the cascade items (first: each carries several members'
 // rows), the rest the ordinary decode items, in one grid.
 template <int BS, int NRB>
-__global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, const CascadeItem *citems,
+__global__ __launch_bounds__(64 * cascade_waves(NRB), 1) void decode_cascade_kernel(AttnArgs a, const CascadeItem *citems,
                                                                 const CascadeMember *members, int n_cascade) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * kCascadeStages * 2 * kDecSliceBytes];
+  constexpr int NW = cascade_waves(NRB), NST = cascade_stages(NRB);
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   if ((int)blockIdx.x < n_cascade)
-    cascade_item<BS, NRB>(a, citems[blockIdx.x], members, smem_raw, bt_lds);
+    cascade_item<BS, NRB, NW, NST>(a, citems[blockIdx.x], members, smem_raw, bt_lds);
   else
-    decode_dma_item<BS, 4, kCascadeStages>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
+    decode_dma_item<BS, NW, NST>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
 }
 
 // The decode launch's items (the cascade items, if any, then the decode
@@ -1768,13 +1770,13 @@ __global__ __launch_bounds__(256, 1) void decode_cascade_kernel(AttnArgs a, cons
 // busy ([Agentic] §5.1-5.2: persistent work-groups taking tasks from a table
 // by index).  Items are listed longest first (cascade items first).  NRB = 0:
 // no cascade items.
-// (with cascade items: the cascade launch's 4-wave work-groups; without: the
-// decode launch's shape, so that every item is computed as there)
+// (the shape of the launch that computes the same items one work-group per
+// item -- the cascade launch with cascade items, the decode launch without --
+// so that every item is computed as there)
 template <int BS, int NRB>
-__global__ __launch_bounds__(64 * (NRB > 0 ? 4 : kDecWaves), 1) void decode_claim_kernel(
+__global__ __launch_bounds__(64 * cascade_waves(NRB), 1) void decode_claim_kernel(
     AttnArgs a, uint32_t *ctr, int n_items, const CascadeItem *citems, const CascadeMember *members, int n_cascade) {
-  constexpr int NW = NRB > 0 ? 4 : kDecWaves;
-  constexpr int NST = NRB > 0 ? kCascadeStages : kDecStages;
+  constexpr int NW = cascade_waves(NRB), NST = cascade_stages(NRB);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
   __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   __shared__ int claim_s;
@@ -1786,9 +1788,9 @@ __global__ __launch_bounds__(64 * (NRB > 0 ? 4 : kDecWaves), 1) void decode_clai
     if (i >= n_items) break;
     if constexpr (NRB > 0) {
       if (i < n_cascade)
-        cascade_item<BS, NRB>(a, citems[i], members, smem_raw, bt_lds);
+        cascade_item<BS, NRB, NW, NST>(a, citems[i], members, smem_raw, bt_lds);
       else
-        decode_dma_item<BS, 4, kCascadeStages>(a, a.items[i - n_cascade], smem_raw, bt_lds);
+        decode_dma_item<BS, NW, NST>(a, a.items[i - n_cascade], smem_raw, bt_lds);
     } else {
       decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
     }
@@ -2726,7 +2728,7 @@ hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_decode, c
   if (n <= 0 || groups <= 0) return hipSuccess;
   if ((n_cascade > 0 && (rows <= 0 || rows > kCascadeRows)) || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
 #define PA_CLAIM(B, R)                                                                                \
-  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(64 * (R > 0 ? 4 : kDecWaves)), 0, s, \
+  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(64 * cascade_waves(R)), 0, s, \
                      a, ctr, n, citems, members, n_cascade)
   if (bs == 16) {
     if (n_cascade == 0) PA_CLAIM(16, 0);
@@ -2748,7 +2750,7 @@ hipError_t launch_decode_cascade(const AttnArgs &a, const CascadeItem *items, co
   if (rows <= 0 || rows > kCascadeRows || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
   const dim3 grid(n_cascade + n_decode);
 #define PA_CASCADE(B, R) \
-  hipLaunchKernelGGL((decode_cascade_kernel<B, R>), grid, dim3(256), 0, s, a, items, members, n_cascade)
+  hipLaunchKernelGGL((decode_cascade_kernel<B, R>), grid, dim3(64 * cascade_waves(R)), 0, s, a, items, members, n_cascade)
   if (bs == 16) {
     if (rows <= 16) PA_CASCADE(16, 1);
     else if (rows <= 32) PA_CASCADE(16, 2);
