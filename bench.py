@@ -611,7 +611,7 @@ PREFILL_KERNEL = "void pa::prefill_w48_kernel<16, 0>(pa::AttnArgs)"
 PREFILL_FP8_KERNEL = "void pa::prefill_w48_kernel<64, 1>(pa::AttnArgs)"
 PREFILL_FP4_KERNEL = "void pa::prefill_w48_kernel<64, 2>(pa::AttnArgs)"
 DECODE_KERNEL = "void pa::decode_dma_kernel<16, 8, 2>(pa::AttnArgs)"
-DECODE_CLAIM_KERNEL = ("void pa::decode_claim_kernel<16, 0>(pa::AttnArgs, unsigned int*, int, pa::CascadeItem const*, "
+DECODE_CLAIM_KERNEL = ("void pa::decode_claim_kernel<16, 0, 0>(pa::AttnArgs, unsigned int*, int, pa::CascadeItem const*, "
                        "pa::CascadeMember const*, int)")
 DECODE_FP8_KERNEL = "void pa::decode_dma_fp8_kernel<64, 8, 2>(pa::AttnArgs)"
 DECODE_FP4_KERNEL = "void pa::decode_dma_fp4_kernel<64, 8, 2>(pa::AttnArgs)"
@@ -742,7 +742,7 @@ def summarize_profiles(out):
 
 
 def summarize_coscheduled(out, src):
-    """profiles/decode_claim_kernel_16_0__mixed_step_coscheduled.txt: the
+    """profiles/decode_claim_kernel_16_0_0__mixed_step_coscheduled.txt: the
     mixed step as the planner runs it, from a kernel trace of bench.py --only
     mixed: per timed step, when the prefill and the two decode launches ran
     (the first beside the prefill on a second queue, the second after it)."""
@@ -756,7 +756,7 @@ def summarize_coscheduled(out, src):
 
     pre = [r for r in rows if r["Kernel_Name"] == PREFILL_KERNEL][-10:]
     claims = [r for r in rows if r["Kernel_Name"] == DECODE_CLAIM_KERNEL]
-    fn = os.path.join(ROOT, "profiles", "decode_claim_kernel_16_0__mixed_step_coscheduled.txt")
+    fn = os.path.join(ROOT, "profiles", "decode_claim_kernel_16_0_0__mixed_step_coscheduled.txt")
     with open(fn, "w") as fh:
         fh.write(f"Kernels: {PREFILL_KERNEL} and {DECODE_CLAIM_KERNEL}\n"
                  "Workload: mixed step, co-scheduled as the planner chooses (bench.py --only mixed)\n\n"

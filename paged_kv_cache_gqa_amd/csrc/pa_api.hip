@@ -384,35 +384,53 @@ int64_t decode_chunk(const std::vector<Tile> &tiles, int32_t hkv, int32_t cus, i
 // streams from HBM and computes little.  A CU streams more than its 1/256
 // share of the chip's bandwidth when few CUs stream (measured with the
 // LDS-filling read alone: 59 GB/s per CU with 32 CUs, 55 with 64, 48 with
-// 128, 28 with all 256; the decode items beside the prefill: ~45 GB/s per CU
+// 128, 28 with all 256; the bf16 decode items beside the prefill: ~45 GB/s per CU
 // with 8-wave work-groups), so a few CUs given to the decode while the others
 // prefill stream most of it before the prefill ends.  The candidates are
 // multiples of the XCD count (an equal number per XCD, so the prefill's
 // ranges stay balanced per XCD) up to half the CUs; the time of each is
 // predicted as the prefill on the remaining CUs plus the decode bytes those
 // few CUs could not stream meanwhile, streamed afterwards by the whole chip;
-// the shortest wins (0: no co-scheduling).  Unit costs, MI355X: a 384-row
-// tile's 64-key step of one KV head takes a CU ~2.47 us; the decode streams
-// ~45 GB/s per CU beside the prefill and ~6.5 TB/s over the whole chip.
-// (The mixed step of 4 incremental prefills and 48 decodes: 12.6 ms one
-// after the other; 11.0 ms with the 48 decode CUs the model picks, 11.3-11.5
-// with 40 or 56; the one-launch step likewise 12.1 -> 10.9 ms.)
-constexpr double kCoPrefillStepSec = 2.47e-6;
-constexpr double kCoDecodeCuBytesPerSec = 45e9;
-constexpr double kCoDecodeChipBytesPerSec = 6.5e12;
+// the shortest wins (0: no co-scheduling).  Each CU given to the decode
+// also slows the prefill's other CUs a little (the decode's HBM streams and
+// the chip's power draw are shared), a fraction per CU taken.  Unit costs,
+// MI355X, per KV format (fitted to the mixed step below at n = 0 .. 56):
+// the prefill time of a 384-row tile's 64-key step of one KV head on one CU;
+// the decode's bytes per second per CU beside the prefill (the quantised
+// formats spend more ALU per byte) and over the whole chip; the prefill's
+// slow-down per CU taken.
+// (The mixed step of 4 incremental prefills and 48 decodes, bf16, block 16:
+// 12.4-12.6 ms one after the other; 11.0-11.1 ms with the 48 decode CUs the
+// model picks, 11.3-11.5 with 40 or 56; the one-launch step likewise 12.1 ->
+// 10.9 ms.  The same step with E4M3 KV, block 64, whose decode takes 1.9 ms
+// on the whole chip: 10.6-10.7 ms one after the other, 10.5-10.6 with 8 to
+// 32 CUs on one device and 10.8 with 32 on another, whose prefill slowed
+// more beside the decode; with MXFP4 KV (decode 1.1 ms): 9.1 ms one after
+// the other, 9.05 with 8 CUs, 9.2 with 16, 9.7 with 32.  The rates below
+// sit between the devices' fits, so the model runs those two steps one
+// launch after the other and co-schedules quantised steps whose decode
+// share is larger.)
+struct CoRates {
+  double prefill_step_sec, decode_cu_bytes_per_sec, decode_chip_bytes_per_sec, prefill_slow_per_cu;
+};
+constexpr CoRates kCoRatesBf16 = {2.47e-6, 45e9, 6.5e12, 0.0009};
+constexpr CoRates kCoRatesE4m3 = {2.49e-6, 30e9, 6.35e12, 0.0016};
+constexpr CoRates kCoRatesMxfp4 = {2.26e-6, 28e9, 5.8e12, 0.002};
 std::atomic<int32_t> g_overlap_force{-1};  // pa_debug_overlap_cus: < 0 the model's choice
 
 // Returns the CUs taken from the prefill's share (-1: no co-scheduling).  A
 // prefill too small to fill every CU (at least kMinGroupKeyTiles steps per
 // work-group) leaves the rest to the decode at no cost.
 // shared_keys: the keys the cascade items read once for all members of
-// their groups (members' own keys count from the end of the shared prefix).
-int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int64_t shared_keys, int32_t hkv, int32_t d,
-                           const MachineShape &M) {
-  int64_t units = 0, dec_bytes = shared_keys * hkv * d * 2 * 2;
+// their groups (members' own keys count from the end of the shared prefix);
+// key_bytes: K and V bytes of one key and KV head in the cache's format;
+// R: that format's unit costs.
+int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int64_t shared_keys, int32_t hkv, int64_t key_bytes,
+                           const CoRates &R, const MachineShape &M) {
+  int64_t units = 0, dec_bytes = shared_keys * hkv * key_bytes;
   for (const Tile &t : tiles) {
     if (t.decode)
-      dec_bytes += (int64_t)(t.keys - t.shared) * hkv * d * 2 * 2;
+      dec_bytes += (int64_t)(t.keys - t.shared) * hkv * key_bytes;
     else
       units += cdiv64(t.keys, kKeyTile) * hkv;
   }
@@ -425,9 +443,9 @@ int32_t choose_overlap_cus(const std::vector<Tile> &tiles, int64_t shared_keys, 
   double best_t = -1.0;
   for (int32_t n = 0; n <= M.cus / 2; n += M.xcds) {
     const int64_t pre = std::min<int64_t>(M.cus - n, pre_max);
-    const double tp = (double)units * kCoPrefillStepSec / (double)pre;
-    const double left = std::max(0.0, (double)dec_bytes - (double)(M.cus - pre) * kCoDecodeCuBytesPerSec * tp);
-    const double t = tp + left / kCoDecodeChipBytesPerSec;
+    const double tp = (double)units * R.prefill_step_sec / (double)pre * (1.0 + R.prefill_slow_per_cu * n);
+    const double left = std::max(0.0, (double)dec_bytes - (double)(M.cus - pre) * R.decode_cu_bytes_per_sec * tp);
+    const double t = tp + left / R.decode_chip_bytes_per_sec;
     if (best_t < 0.0 || t < best_t) best_t = t, best = n;
   }
   return best;
@@ -490,12 +508,14 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
     pchunk = std::max<int64_t>(kPrefillMinChunk, cdiv64(wp, prefill_target_items));
 
   const bool persistent = tile_rows == kDmaTileRows;
-  // co-scheduling: bf16 KV at head_dim 128 (the LDS-DMA prefill and decode);
-  // in the one-launch step, some work-groups take decode items first
+  // co-scheduling: head_dim 128 (the LDS-DMA prefill and decode kernels);
+  // in the one-launch step (bf16), some work-groups take decode items first
   int64_t shared_keys = 0;
   for (const auto &v : group_tiles)
     if (!v.empty()) shared_keys += tiles[v[0]].shared;
-  const int32_t co = persistent && c->dtype == PA_KV_BF16 ? choose_overlap_cus(tiles, shared_keys, hkv, d, M) : -1;
+  const int64_t key_bytes = c->dtype == PA_KV_MXFP4 ? 2 * (d / 2 + d / 32) : c->dtype == PA_KV_FP8_E4M3 ? 2 * d : 4 * d;
+  const CoRates &rates = c->dtype == PA_KV_MXFP4 ? kCoRatesMxfp4 : c->dtype == PA_KV_FP8_E4M3 ? kCoRatesE4m3 : kCoRatesBf16;
+  const int32_t co = persistent ? choose_overlap_cus(tiles, shared_keys, hkv, key_bytes, rates, M) : -1;
   if (persistent) {
     MachineShape Mp = M;
     Mp.cus -= std::max(co, 0);
@@ -1148,11 +1168,12 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     e = timed(1, s, [&] { return launch_prefill(ap, n_pre, d, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
     e = timed(2, co.s2, [&] {
-      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, P.overlap_cus, bs, co.s2);
+      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, P.overlap_cus, bs, fmt,
+                                 co.s2);
     });
     if (e != hipSuccess) return hip_fail(e, "decode attention launch (beside the prefill)");
     e = timed(2, s, [&] {
-      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, tail, bs, s);
+      return launch_decode_claim(ad, ctr, n_dec, citems, members, n_casc, P.cascade_rows, tail, bs, fmt, s);
     });
     if (e != hipSuccess) return hip_fail(e, "decode attention launch (after the prefill)");
     if ((e = hipEventRecord(co.join, co.s2)) != hipSuccess) return hip_fail(e, "join event");

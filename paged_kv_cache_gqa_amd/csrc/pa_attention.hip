@@ -1759,45 +1759,6 @@ __global__ __launch_bounds__(64 * cascade_waves(NRB), 1) void decode_cascade_ker
     decode_dma_item<BS, NW, NST>(a, a.items[blockIdx.x - n_cascade], smem_raw, bt_lds);
 }
 
-// The decode launch's items (the cascade items, if any, then the decode
-// items) taken from a shared list instead of one per work-group: a
-// persistent grid whose work-groups claim item indexes from a counter in the
-// workspace (zeroed by the work-list copy; one vector atomic by one lane per
-// claim) until the list is exhausted.  The forward call launches it twice
-// over the same list and counter -- on a few CUs beside a prefill launch that
-// holds the others, and after that prefill on the CUs it frees -- so a mixed
-// step's decode streams from HBM while its prefill keeps the matrix cores
-// busy ([Agentic] §5.1-5.2: persistent work-groups taking tasks from a table
-// by index).  Items are listed longest first (cascade items first).  NRB = 0:
-// no cascade items.
-// (the shape of the launch that computes the same items one work-group per
-// item -- the cascade launch with cascade items, the decode launch without --
-// so that every item is computed as there)
-template <int BS, int NRB>
-__global__ __launch_bounds__(64 * cascade_waves(NRB), 1) void decode_claim_kernel(
-    AttnArgs a, uint32_t *ctr, int n_items, const CascadeItem *citems, const CascadeMember *members, int n_cascade) {
-  constexpr int NW = cascade_waves(NRB), NST = cascade_stages(NRB);
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDecSliceBytes];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
-  __shared__ int claim_s;
-  for (;;) {
-    if (threadIdx.x == 0) claim_s = (int)atomicAdd(ctr, 1u);
-    __syncthreads();
-    const int i = claim_s;
-    __syncthreads();  // (claim_s is rewritten by the next claim)
-    if (i >= n_items) break;
-    if constexpr (NRB > 0) {
-      if (i < n_cascade)
-        cascade_item<BS, NRB, NW, NST>(a, citems[i], members, smem_raw, bt_lds);
-      else
-        decode_dma_item<BS, NW, NST>(a, a.items[i - n_cascade], smem_raw, bt_lds);
-    } else {
-      decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
-    }
-    __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
-  }
-}
-
 // =============================================================================
 // Decode for E4M3 KV, head_dim 128, streamed through LDS like the bf16 one:
 // wave w takes the 32-key slices w, w+4, ... of the item's range; a slice of
@@ -1817,19 +1778,17 @@ constexpr int kDec8Slice = 32;                        // keys per wave step
 constexpr int kDec8SliceBytes = kDec8Slice * 128;     // K (or V) codes of one slice, 4 KB
 
 template <int BS, int NW, int NST>
-__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) {
+__device__ __forceinline__ void decode_fp8_item(const AttnArgs &a, const Item it, unsigned char *smem_raw,
+                                                int *bt_lds) {
   constexpr int D = 128;
   constexpr int NCK = D / 32;
   constexpr int ND = D / 16;
   constexpr int SB = kDec8SliceBytes;
   static_assert(BS == 16 || BS == 64, "block size");
   static_assert(NW * NST * 2 * SB >= NW * 16 * (D + 2) * 4, "combine scratch");
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * SB];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  const Item it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2000,6 +1959,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) 
   decode_combine<D, NW>(a, it, smem_raw, m, l, o);
 }
 
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp8_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * 2 * kDec8SliceBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  decode_fp8_item<BS, NW, NST>(a, a.items[blockIdx.x], smem_raw, bt_lds);
+}
+
 // =============================================================================
 // Decode for MXFP4 KV, head_dim 128 ([V41] kernels section: a 4-bit KV cache,
 // about half the bytes of 8-bit): wave w takes the 64-key slices w, w+4, ...
@@ -2029,7 +1995,8 @@ constexpr int kDec4ScaleBytes = kDec4Slice * 4;      // K (or V) scale bytes of 
 constexpr int kDec4StageBytes = 2 * kDec4CodeBytes + 2 * kDec4ScaleBytes;
 
 template <int BS, int NW, int NST>
-__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) {
+__device__ __forceinline__ void decode_fp4_item(const AttnArgs &a, const Item it, unsigned char *smem_raw,
+                                                int *bt_lds, float *vsf_all) {
   constexpr int D = 128;
   constexpr int ND = D / 16;
   constexpr int SB = kDec4CodeBytes;
@@ -2040,13 +2007,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) 
   // (every request of the NST stages outstanding at once fits the 6-bit
   // vector-memory counter)
   static_assert(PER_SLICE * NST < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * STB];
-  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
-  __shared__ __attribute__((aligned(16))) float vsf_lds[NW][4 * kDec4Slice];  // a slice's V scales, fp32
   lds_u8 *smem = (lds_u8 *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  const Item it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2059,7 +2022,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) 
   const int kv_lo = it.kv_lo, kv_hi = it.kv_hi;
   typedef __attribute__((address_space(3))) float lds_f32;
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-  lds_f32 *vsf = (lds_f32 *)&vsf_lds[wave][0];
+  lds_f32 *vsf = (lds_f32 *)(vsf_all + wave * 4 * kDec4Slice);
 
   // Q in the contraction order of the score product: qf[c] = d 32 q4 + 8c ..
   bf16x8 qf[4];
@@ -2281,6 +2244,79 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) 
   }
   PA_WAIT_VMCNT(0);
   decode_combine<D, NW, true>(a, it, smem_raw, m, l, o);
+}
+
+template <int BS, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void decode_dma_fp4_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NW * NST * kDec4StageBytes];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  __shared__ __attribute__((aligned(16))) float vsf_lds[NW * 4 * kDec4Slice];  // a slice's V scales, fp32
+  decode_fp4_item<BS, NW, NST>(a, a.items[blockIdx.x], smem_raw, bt_lds, vsf_lds);
+}
+
+// E4M3 decode: waves per work-group and ring stages per wave
+#ifndef PA_DEC8_WAVES
+#define PA_DEC8_WAVES 8
+#endif
+#ifndef PA_DEC8_STAGES
+#define PA_DEC8_STAGES 2
+#endif
+// MXFP4 decode: eight waves of two stages, two per SIMD, so that one converts
+// and multiplies while the other waits (measured: 0.208 ms against 0.25 ms
+// for four waves of four stages at 1M keys)
+constexpr int kDec4Waves = 8, kDec4Stages = 2;
+
+// The decode launch's items (the cascade items, if any, then the decode
+// items) taken from a shared list instead of one per work-group: a
+// persistent grid whose work-groups claim item indexes from a counter in the
+// workspace (zeroed by the work-list copy; one vector atomic by one lane per
+// claim) until the list is exhausted.  The forward call launches it twice
+// over the same list and counter -- on a few CUs beside a prefill launch that
+// holds the others, and after that prefill on the CUs it frees -- so a mixed
+// step's decode streams from HBM while its prefill keeps the matrix cores
+// busy ([Agentic] §5.1-5.2: persistent work-groups taking tasks from a table
+// by index).  Items are listed longest first (cascade items first).  NRB = 0:
+// no cascade items (the only case for E4M3 and MXFP4 KV).  Each item is
+// computed by the same item function, in the same work-group shape, as in
+// the launch that runs it one work-group per item (the cascade launch with
+// cascade items, else the decode launch of its KV format).
+template <int FMT>
+constexpr int claim_waves(int nrb) {
+  return FMT == kKvE4m3 ? PA_DEC8_WAVES : FMT == kKvMxfp4 ? kDec4Waves : cascade_waves(nrb);
+}
+template <int BS, int NRB, int FMT>
+__global__ __launch_bounds__(64 * claim_waves<FMT>(NRB), 1) void decode_claim_kernel(
+    AttnArgs a, uint32_t *ctr, int n_items, const CascadeItem *citems, const CascadeMember *members, int n_cascade) {
+  constexpr int NW = claim_waves<FMT>(NRB);
+  constexpr int NST = FMT == kKvE4m3 ? PA_DEC8_STAGES : FMT == kKvMxfp4 ? kDec4Stages : cascade_stages(NRB);
+  constexpr int RING = FMT == kKvE4m3 ? NW * NST * 2 * kDec8SliceBytes
+                     : FMT == kKvMxfp4 ? NW * NST * kDec4StageBytes
+                                       : NW * NST * 2 * kDecSliceBytes;
+  static_assert(NRB == 0 || FMT == kKvBf16, "cascade items are bf16");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[RING];
+  __shared__ int bt_lds[kMaxDecItemKeys / BS + 2];
+  __shared__ __attribute__((aligned(16))) float vsf_lds[FMT == kKvMxfp4 ? NW * 4 * kDec4Slice : 1];
+  __shared__ int claim_s;
+  for (;;) {
+    if (threadIdx.x == 0) claim_s = (int)atomicAdd(ctr, 1u);
+    __syncthreads();
+    const int i = claim_s;
+    __syncthreads();  // (claim_s is rewritten by the next claim)
+    if (i >= n_items) break;
+    if constexpr (FMT == kKvE4m3) {
+      decode_fp8_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
+    } else if constexpr (FMT == kKvMxfp4) {
+      decode_fp4_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds, vsf_lds);
+    } else if constexpr (NRB > 0) {
+      if (i < n_cascade)
+        cascade_item<BS, NRB, NW, NST>(a, citems[i], members, smem_raw, bt_lds);
+      else
+        decode_dma_item<BS, NW, NST>(a, a.items[i - n_cascade], smem_raw, bt_lds);
+    } else {
+      decode_dma_item<BS, NW, NST>(a, a.items[i], smem_raw, bt_lds);
+    }
+    __syncthreads();  // the item's LDS (ring, block ids, combine scratch) is free again
+  }
 }
 
 // =============================================================================
@@ -2654,13 +2690,6 @@ static hipError_t launch_prefill_t(const AttnArgs &a, int n, hipStream_t s) {
 #ifndef PA_DECODE_DMA
 #define PA_DECODE_DMA 1
 #endif
-// E4M3 decode: waves per work-group and ring stages per wave
-#ifndef PA_DEC8_WAVES
-#define PA_DEC8_WAVES 8
-#endif
-#ifndef PA_DEC8_STAGES
-#define PA_DEC8_STAGES 2
-#endif
 template <int D, int BS, bool FP8>
 static hipError_t launch_decode_t(const AttnArgs &a, int n, hipStream_t s) {
   if constexpr (!FP8 && D == 128 && PA_DECODE_DMA) {
@@ -2707,13 +2736,10 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, int fmt, hipSt
   if (n <= 0) return hipSuccess;
   if (fmt == kKvMxfp4) {
     if (d != 128) return hipErrorInvalidValue;
-    // eight waves of two stages: two waves per SIMD, so that one converts
-    // and multiplies while the other waits (measured: 0.208 ms against
-    // 0.25 ms for four waves of four stages at 1M keys)
     if (bs == 16)
-      hipLaunchKernelGGL((decode_dma_fp4_kernel<16, 8, 2>), dim3(n), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((decode_dma_fp4_kernel<16, kDec4Waves, kDec4Stages>), dim3(n), dim3(64 * kDec4Waves), 0, s, a);
     else if (bs == 64)
-      hipLaunchKernelGGL((decode_dma_fp4_kernel<64, 8, 2>), dim3(n), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((decode_dma_fp4_kernel<64, kDec4Waves, kDec4Stages>), dim3(n), dim3(64 * kDec4Waves), 0, s, a);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
@@ -2722,24 +2748,31 @@ hipError_t launch_decode(const AttnArgs &a, int n, int d, int bs, int fmt, hipSt
   PA_DISPATCH(launch_decode_t, a, n, s);
 }
 hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_decode, const CascadeItem *citems,
-                               const CascadeMember *members, int n_cascade, int rows, int groups, int bs,
+                               const CascadeMember *members, int n_cascade, int rows, int groups, int bs, int fmt,
                                hipStream_t s) {
   const int n = n_cascade + n_decode;
   if (n <= 0 || groups <= 0) return hipSuccess;
-  if ((n_cascade > 0 && (rows <= 0 || rows > kCascadeRows)) || (bs != 16 && bs != 64)) return hipErrorInvalidValue;
-#define PA_CLAIM(B, R)                                                                                \
-  hipLaunchKernelGGL((decode_claim_kernel<B, R>), dim3(groups), dim3(64 * cascade_waves(R)), 0, s, \
-                     a, ctr, n, citems, members, n_cascade)
-  if (bs == 16) {
-    if (n_cascade == 0) PA_CLAIM(16, 0);
-    else if (rows <= 16) PA_CLAIM(16, 1);
-    else if (rows <= 32) PA_CLAIM(16, 2);
-    else PA_CLAIM(16, 4);
+  if ((n_cascade > 0 && (fmt != kKvBf16 || rows <= 0 || rows > kCascadeRows)) || (bs != 16 && bs != 64))
+    return hipErrorInvalidValue;
+#define PA_CLAIM(B, R, F)                                                                                     \
+  hipLaunchKernelGGL((decode_claim_kernel<B, R, F>), dim3(groups), dim3(64 * claim_waves<F>(R)), 0, s, a, ctr, \
+                     n, citems, members, n_cascade)
+  if (fmt == kKvE4m3) {
+    if (bs == 16) PA_CLAIM(16, 0, kKvE4m3);
+    else PA_CLAIM(64, 0, kKvE4m3);
+  } else if (fmt == kKvMxfp4) {
+    if (bs == 16) PA_CLAIM(16, 0, kKvMxfp4);
+    else PA_CLAIM(64, 0, kKvMxfp4);
+  } else if (bs == 16) {
+    if (n_cascade == 0) PA_CLAIM(16, 0, kKvBf16);
+    else if (rows <= 16) PA_CLAIM(16, 1, kKvBf16);
+    else if (rows <= 32) PA_CLAIM(16, 2, kKvBf16);
+    else PA_CLAIM(16, 4, kKvBf16);
   } else {
-    if (n_cascade == 0) PA_CLAIM(64, 0);
-    else if (rows <= 16) PA_CLAIM(64, 1);
-    else if (rows <= 32) PA_CLAIM(64, 2);
-    else PA_CLAIM(64, 4);
+    if (n_cascade == 0) PA_CLAIM(64, 0, kKvBf16);
+    else if (rows <= 16) PA_CLAIM(64, 1, kKvBf16);
+    else if (rows <= 32) PA_CLAIM(64, 2, kKvBf16);
+    else PA_CLAIM(64, 4, kKvBf16);
   }
 #undef PA_CLAIM
   return hipGetLastError();

@@ -179,11 +179,11 @@ struct StepArgs {
 hipError_t launch_step(const StepArgs &a, int n_groups, int bs, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
-// bf16 head_dim 128 decode launch (cascade items, if any, then decode items)
+// head_dim 128 decode launch (bf16 cascade items, if any, then decode items)
 // whose items are claimed from *ctr (zero before the first of the launches
 // that share it) by `groups` persistent work-groups
 hipError_t launch_decode_claim(const AttnArgs &a, uint32_t *ctr, int n_decode, const CascadeItem *citems,
-                               const CascadeMember *members, int n_cascade, int rows, int groups, int bs,
+                               const CascadeMember *members, int n_cascade, int rows, int groups, int bs, int fmt,
                                hipStream_t s);
 // bf16 head_dim 128 decode launch with shared-prefix cascade items first
 // (rows: the largest member count times G among them, at most kCascadeRows)

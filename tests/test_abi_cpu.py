@@ -196,7 +196,7 @@ def test_planner_balances_persistent_prefill(palib):
 
 
 def test_planner_coschedules_mixed_steps(palib):
-    """A bf16 head-dim-128 step with prefill and decode rows: the planner
+    """A head-dim-128 step with prefill and decode rows: the planner
     leaves a multiple of the XCD count of CUs (up to half) to the decode
     beside the prefill, cuts the prefill's ranges for the rest (balanced), and
     still covers the causal pattern exactly; steps with one kind of row, other
@@ -222,10 +222,28 @@ def test_planner_coschedules_mixed_steps(palib):
     assert palib.pa_workspace_size(m.hist, m.incr, 32, c) == size_auto
     # prefill only, decode only: nothing to co-schedule
     assert len(palib.pa_debug_plan_groups([45_700], [2_700], 32, c)) - 1 == cus
-    # E4M3 KV: the launches one after the other
+    # E4M3 and MXFP4 KV: fewer decode bytes and a slower decode per CU beside
+    # the prefill, so no more CUs than bf16 (none for this step's short
+    # decode); a prefill too small to hold every CU leaves the rest to the
+    # decode in every format; the forced settings hold for both
     e4 = cache(palib, num_kv_heads=8, head_dim=128, block_size=64, dtype=palib.PA_KV_FP8_E4M3,
                k_scale=FAKE, v_scale=FAKE)
-    assert len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, e4)) - 1 == cus
+    f4 = cache(palib, num_kv_heads=8, head_dim=128, block_size=64, dtype=palib.PA_KV_MXFP4,
+               k_scale=FAKE, v_scale=FAKE)
+    small = ([3000, 900, 5000, 7000, 200, 40_000], [300, 150, 1, 1, 1, 1])
+    n_small = cus - (len(palib.pa_debug_plan_groups(*small, 32, c)) - 1)
+    assert n_small > cus // 2
+    for q in (e4, f4):
+        n_q = cus - (len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, q)) - 1)
+        assert 0 <= n_q <= n_dec and n_q % xcds == 0, n_q
+        assert cus - (len(palib.pa_debug_plan_groups(*small, 32, q)) - 1) == n_small
+        try:
+            palib.pa_debug_overlap_cus(24)
+            assert len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, q)) - 1 == cus - 24
+        finally:
+            palib.pa_debug_overlap_cus(-1)
+    # head_dim 64 (the register-staged kernels): no persistent prefill, no co-scheduling
+    assert len(palib.pa_debug_plan_groups(m.hist, m.incr, 32, cache(palib, head_dim=64))) == 0
 
 
 def test_planner_covers_causal_pattern_exactly(palib):

@@ -1,5 +1,5 @@
-"""The co-scheduled mixed step: a step holding prefill and decode rows (bf16
-KV, head_dim 128) whose decode items are streamed by the CUs the persistent
+"""The co-scheduled mixed step: a step holding prefill and decode rows
+(head_dim 128; bf16, E4M3 or MXFP4 KV) whose decode items are streamed by the CUs the persistent
 prefill launch leaves free and, after it, by the CUs it frees.  Which CUs run
 an item does not change its arithmetic, so the decode rows equal those of
 the launches run one after the other bit for bit; the prefill rows follow a
@@ -41,8 +41,8 @@ def _prefill_workgroups(palib, spec, c, force):
         palib.pa_debug_overlap_cus(-1)
 
 
-@pytest.mark.parametrize("bs", [16, 64])
-def test_coscheduled_step_against_sequential_and_oracle(palib, bs):
+@pytest.mark.parametrize("bs,kv", [(16, "bf16"), (64, "bf16"), (64, "e4m3"), (16, "mxfp4")])
+def test_coscheduled_step_against_sequential_and_oracle(palib, bs, kv):
     """Two increments (one long enough to fill every CU) and six decodes (one
     split over several items), with needles: forced 0 (one launch after the
     other), 8 and 64 CUs taken from the prefill, and the planner's choice;
@@ -51,8 +51,8 @@ def test_coscheduled_step_against_sequential_and_oracle(palib, bs):
     bitwise equal to the first."""
     big = 2000
     spec = W.with_needles(
-        W.Spec(f"co_bs{bs}", 91, 32, 8, 128, bs, [20_000, 900, 5000, 7000, 200, 90_000, 4000, 12_000],
-               [big, 150, 1, 1, 1, 1, 1, 1]),
+        W.Spec(f"co_{kv}_bs{bs}", 91, 32, 8, 128, bs, [20_000, 900, 5000, 7000, 200, 90_000, 4000, 12_000],
+               [big, 150, 1, 1, 1, 1, 1, 1], kv_dtype=kv),
         needles=[(0, 0), (0, 95), (0, big - 1), (1, 149), (2, 0), (5, 0), (7, 0)])
     rows = sorted({0, 1, 95, 96, 191, 192, 500, 1000, 1500, big - 96, big - 1} | set(range(big, big + 156)))
     print(f"[case] co-scheduled {spec.name} hist={spec.hist} incr={spec.incr}", flush=True)
@@ -75,7 +75,7 @@ def test_coscheduled_step_against_sequential_and_oracle(palib, bs):
     for force in (0, 8, 64, -1, 64):
         out, lse = _forced(palib, b, c, force)
         what = f"{spec.name} CUs taken from the prefill {force}"
-        assert_parity(out[rows], ref, False, what, needles=needles)
+        assert_parity(out[rows], ref, kv == "e4m3", what, needles=needles)
         assert_lse(lse[rows], ref_lse, bound, what)
         if force in outs:
             assert torch.equal(out.view(torch.int16), outs[force].view(torch.int16)), what
@@ -84,11 +84,14 @@ def test_coscheduled_step_against_sequential_and_oracle(palib, bs):
         assert torch.equal(outs[force][dec_rows].view(torch.int16), outs[0][dec_rows].view(torch.int16)), force
 
 
-def test_small_prefill_leaves_cus_to_the_decode(palib):
+@pytest.mark.parametrize("bs,kv", [(16, "bf16"), (64, "e4m3"), (16, "mxfp4")])
+def test_small_prefill_leaves_cus_to_the_decode(palib, bs, kv):
     """A prefill too small to hold every CU: the decode items run on the CUs
-    it leaves, at the same time; all rows against the oracle, decode rows
-    bitwise equal to the launches one after the other."""
-    spec = W.Spec("co_small", 92, 32, 8, 128, 16, [3000, 900, 5000, 7000, 200, 40_000], [300, 150, 1, 1, 1, 1])
+    it leaves, at the same time (the planner's choice in every KV format);
+    all rows against the oracle, decode rows bitwise equal to the launches
+    one after the other."""
+    spec = W.Spec(f"co_small_{kv}", 92, 32, 8, 128, bs, [3000, 900, 5000, 7000, 200, 40_000],
+                  [300, 150, 1, 1, 1, 1], kv_dtype=kv)
     print(f"[case] co-scheduled {spec.name} hist={spec.hist} incr={spec.incr}", flush=True)
     b = W.make_batch(spec, DEV)
     host = host_caches(b)
@@ -99,7 +102,7 @@ def test_small_prefill_leaves_cus_to_the_decode(palib):
     ref, ref_lse, after = oracle_step(
         b, caches=tuple(x.copy() if isinstance(x, np.ndarray) else x for x in host))
     out, lse = _forced(palib, b, c, -1)
-    assert_parity(out, ref, False, spec.name)
+    assert_parity(out, ref, kv == "e4m3", spec.name)
     assert_lse(lse, ref_lse, lse_bounds(b, after), spec.name)
     out0, _ = _forced(palib, b, c, 0)
     assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
