@@ -280,14 +280,17 @@ PA_API pa_status pa_debug_gather(const pa_kv_cache *cache, const int32_t *block_
  * Arguments are those of kv_append followed by those of paged_attn_forward,
  * with num_tokens = total_q: k_new, v_new [total_q][num_kv_heads][head_dim]
  * and slot_mapping [total_q] are the new tokens of the query rows, in the
- * same order.  The results equal kv_append followed by paged_attn_forward's
- * within the attention tolerance (the decode items run with eight waves and
- * the merge sums in another order, so the bits may differ).
+ * same order.  The cache after the step equals kv_append's bit for bit
+ * (E4M3: codes from the caller's scales; MXFP4: codes and the scale bytes the
+ * append computes); the outputs equal paged_attn_forward's within the
+ * attention tolerance (the merge sums in another order, so the bits may
+ * differ).
  *   workspace       NULL: *workspace_bytes is set to the bytes this step
  *                   needs (nothing else happens); otherwise at least that
  *                   many bytes, 256-byte aligned, contents need no
  *                   initialisation.
- * Supported: bf16 KV with head_dim 128 (PA_ERR_UNSUPPORTED otherwise).
+ * Supported: head_dim 128, bf16, E4M3 or MXFP4 KV (PA_ERR_UNSUPPORTED for
+ * head_dim 64).
  */
 PA_API pa_status paged_attn_step(const pa_kv_cache *cache, const void *k_new, const void *v_new,
                                  const int64_t *slot_mapping, const void *q, const int32_t *block_tables,

@@ -994,8 +994,8 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
       if (groups->group_of[s] < -1 || groups->group_of[s] >= groups->num_groups)
         return fail(PA_ERR_BAD_SHAPE, "sequence %d: group %d out of range", s, groups->group_of[s]);
   }
-  if (step && (cache->dtype != PA_KV_BF16 || cache->head_dim != 128))
-    return fail(PA_ERR_UNSUPPORTED, "the one-launch step takes bf16 KV with head_dim 128");
+  if (step && cache->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "the one-launch step takes head_dim 128 (got %d)", cache->head_dim);
   const int32_t hkv = cache->num_kv_heads, group = num_q_heads / hkv, d = cache->head_dim;
   Plan P;
   const int32_t tile_rows = prefill_tile_rows(cache);
@@ -1111,6 +1111,8 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     sa.app.slots = step->slots;
     sa.app.k_cache = cache->k_cache;
     sa.app.v_cache = cache->v_cache;
+    sa.app.ks = cache->k_scale;
+    sa.app.vs = cache->v_scale;
     sa.app.hkv = hkv;
     sa.app.bs = bs;
     sa.app.lbs = bs == 16 ? 4 : 6;
@@ -1131,7 +1133,7 @@ pa_status forward(const void *q, const pa_kv_cache *cache, const int32_t *block_
     sa.decode_first = P.step_xcds > 1 ? P.step_decode_cus / P.step_xcds : P.step_decode_cus;
     const int64_t tasks = (int64_t)sa.n_append_tasks + P.step_ranges + sa.n_decode;
     const int groups_n = (int)std::max<int64_t>(1, std::min<int64_t>(machine_shape().cus, tasks));
-    e = timed(4, s, [&] { return launch_step(sa, groups_n, bs, s); });
+    e = timed(4, s, [&] { return launch_step(sa, groups_n, bs, fmt, s); });
     if (e != hipSuccess) return hip_fail(e, "step launch");
     return PA_OK;
   }

@@ -176,7 +176,7 @@ struct StepArgs {
   int32_t decode_first;          // work-groups per XCD that take decode items before prefill ranges
 };
 
-hipError_t launch_step(const StepArgs &a, int n_groups, int bs, hipStream_t s);
+hipError_t launch_step(const StepArgs &a, int n_groups, int bs, int fmt, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 hipError_t launch_decode(const AttnArgs &a, int n_items, int d, int bs, int fmt, hipStream_t s);
 // head_dim 128 decode launch (bf16 cascade items, if any, then decode items)

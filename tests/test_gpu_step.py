@@ -2,8 +2,8 @@
 attention in one persistent kernel with device-side task claiming and merges
 by the last writer) against the oracle, at sizes the oracle finishes in
 seconds: prefill ranges, decode items, split tiles merged in-kernel, both
-block sizes, several GQA groups, needles, LSE; the cache after the step
-bit for bit; repeated steps on one workspace; the wait flag; and, at full
+block sizes, several GQA groups, bf16, E4M3 and MXFP4 KV, needles, LSE; the
+cache after the step bit for bit; repeated steps on one workspace; the wait flag; and, at full
 size, the mixed step against paged_attn_forward (itself checked against the
 oracle at full size)."""
 import numpy as np
@@ -12,7 +12,7 @@ import torch
 
 import workloads as W
 from tests.gpu_helpers import assert_lse, assert_parity, forward, gpu_caches
-from tests.helpers import bits16, host_caches, lse_bounds, oracle_step
+from tests.helpers import bits16, bytes8, host_caches, lse_bounds, oracle_step
 from tests.test_gpu_parity import _needled
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,24 @@ CASES = {
     "bs64_split": _spec([60_000, 4100], [400, 1], bs=64),
     "g8": _spec([1500, 10, 640, 333], [2, 1, 2, 150], hkv=4),
     "g1": _spec([1200, 50], [300, 1], hq=8, hkv=8),
+    # E4M3 and MXFP4 KV: the append quantises (MXFP4: its scale bytes too),
+    # the items widen the codes
+    "e4m3_mixed": _spec([5000, 900, 12_000, 0, 77, 3000], [600, 1, 1, 300, 1, 2], bs=64, kv_dtype="e4m3"),
+    "e4m3_bs16_split": _spec([60_000, 4100, 333], [1, 1, 150], kv_dtype="e4m3"),
+    "mxfp4_mixed": _spec([5000, 900, 12_000, 0, 77, 3000], [600, 1, 1, 300, 1, 2], kv_dtype="mxfp4"),
+    "mxfp4_bs64_split": _spec([60_000, 4100, 40], [400, 1, 1], bs=64, kv_dtype="mxfp4"),
 }
+
+
+def assert_cache_after(caches, after, kv):
+    """The device cache after the step's append equals the oracle's, bit for
+    bit (codes, and MXFP4's scale bytes)."""
+    if kv == "bf16":
+        assert np.array_equal(bits16(caches[0]), after[0]) and np.array_equal(bits16(caches[1]), after[1])
+        return
+    assert np.array_equal(bytes8(caches[0]), after[0]) and np.array_equal(bytes8(caches[1]), after[1])
+    if kv == "mxfp4":
+        assert np.array_equal(bytes8(caches[2]), after[2]) and np.array_equal(bytes8(caches[3]), after[3])
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -67,8 +84,8 @@ def test_step_parity(palib, name):
     out, lse, c, _ = run_step_once(palib, b, caches)
     ref, ref_lse, after = oracle_step(b, caches=tuple(x.copy() if isinstance(x, np.ndarray) else x for x in host))
     # the cache after the step's append, bit for bit
-    assert np.array_equal(bits16(caches[0]), after[0]) and np.array_equal(bits16(caches[1]), after[1])
-    assert_parity(out, ref, False, f"step {name}", needles=[(r, h) for r, h, _, _ in b.needles])
+    assert_cache_after(caches, after, spec.kv_dtype)
+    assert_parity(out, ref, spec.kv_dtype == "e4m3", f"step {name}", needles=[(r, h) for r, h, _, _ in b.needles])
     assert_lse(lse, ref_lse, lse_bounds(b, after), f"step {name}")
 
 
@@ -93,7 +110,7 @@ def test_step_repeats_bitwise_on_one_workspace(palib):
 
 
 def test_step_unsupported_formats(palib):
-    spec = _spec([100], [1], kv_dtype="e4m3")
+    spec = W.Spec("step_d64", 51, 32, 8, 64, 16, [100], [1])
     b = W.make_batch(spec, DEV)
     host = host_caches(b)
     c = palib.make_cache(*gpu_caches(b, host))
@@ -120,3 +137,27 @@ def test_mixed_step_full_size_against_forward(palib):
     assert torch.equal(c1[1].view(torch.int16), c2[1].view(torch.int16))
     ref = out2.double().cpu().numpy()
     assert_parity(out1, ref, False, "mixed step: one launch against forward")
+
+
+@pytest.mark.parametrize("kv", ["e4m3", "mxfp4"])
+def test_long_decode_step_against_forward(palib, kv):
+    """A decode step over a 1,048,575-token history (E4M3 or MXFP4 KV,
+    block 64) through paged_attn_step against kv_append + paged_attn_forward
+    on the same inputs: the row within the bars (needled heads within the
+    relative bar too), the caches (codes and scales) equal."""
+    spec = W.long_context(1_048_575, 1) if kv == "e4m3" else W.long_context_mxfp4(1_048_575, 1)
+    spec = W.with_needles(spec, needles=[(0, 0)])
+    print(f"[case] one-launch step, 1M-token {kv} decode", flush=True)
+    b = W.make_batch(spec, DEV)
+    c1 = gpu_caches(b)
+    c2 = tuple(x.clone() for x in c1)
+    out1, _, _, _ = run_step_once(palib, b, c1, want_lse=False)
+    cc = palib.make_cache(*c2)
+    palib.kv_append(cc, b.k_new, b.v_new, b.slot_mapping)
+    out2, _ = forward(palib, b, cc)
+    torch.cuda.synchronize()
+    for x, y in zip(c1, c2):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    ref = out2.double().cpu().numpy()
+    assert_parity(out1, ref, kv == "e4m3", f"one-launch {kv} decode against forward",
+                  needles=[(r, h) for r, h, _, _ in b.needles])
