@@ -172,7 +172,7 @@ PA_API pa_status kv_append(const pa_kv_cache *cache, const void *k_new, const vo
  * Neither q nor the caches are written.
  * Streams: everything is ordered after the work already on `stream`, and
  * work enqueued on `stream` afterwards is ordered after all of it.  A step
- * that holds both prefill and decode rows (bf16 KV, head_dim 128) may run
+ * that holds both prefill and decode rows (head_dim 128, any KV format) may run
  * its decode partly on a second, library-owned stream per device, forked
  * from `stream` by an event and joined back to it before the merges, so the
  * decode streams from HBM on a few CUs while the prefill occupies the others
@@ -340,7 +340,7 @@ PA_API pa_status pa_debug_plan(const int32_t *hist_lens, const int32_t *incr_len
 PA_API pa_status pa_debug_overlap_cus(int32_t n);
 
 /* Test hook for the persistent prefill launch: when the plan for these HOST
- * lengths runs the persistent 384-row kernel (head_dim 128, bf16 or E4M3 KV)
+ * lengths runs the persistent 384-row kernel (head_dim 128, any KV format)
  * with one work-group per balanced range of work, *num_groups_out receives the number
  * of work-groups n and first_out[0..n] the offsets into the prefill items
  * (as listed by pa_debug_plan) where each work-group's items begin, with

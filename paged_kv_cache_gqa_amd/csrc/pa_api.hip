@@ -201,8 +201,8 @@ void cut(int32_t keys, int32_t n, std::vector<std::pair<int32_t, int32_t>> &out)
   }
 }
 
-// Query rows per prefill tile: the LDS-DMA kernel (head_dim 128, bf16 or
-// E4M3 KV) takes 384, the register-staged kernel (head_dim 64) 128.
+// Query rows per prefill tile: the LDS-DMA kernel (head_dim 128, every KV
+// format) takes 384, the register-staged kernel (head_dim 64) 128.
 int32_t prefill_tile_rows(const pa_kv_cache *c) {
   return c->head_dim == 128 ? kDmaTileRows : kRegTileRows;
 }
@@ -509,7 +509,7 @@ void make_plan(const int32_t *hist, const int32_t *incr, int32_t num_seqs, const
 
   const bool persistent = tile_rows == kDmaTileRows;
   // co-scheduling: head_dim 128 (the LDS-DMA prefill and decode kernels);
-  // in the one-launch step (bf16), some work-groups take decode items first
+  // in the one-launch step, some work-groups take decode items first
   int64_t shared_keys = 0;
   for (const auto &v : group_tiles)
     if (!v.empty()) shared_keys += tiles[v[0]].shared;

@@ -22,14 +22,23 @@
 // merge kernel ([Agentic] §4.3.3: partial O_i with LSE merged the
 // online-softmax way; §5.2: split attention, then combine).
 //
-// Kernels, in file order:
+// Kernels, in file order (FMT: the KV format, 0 bf16, 1 E4M3, 2 MXFP4):
 //   prefill_kernel<D, BS, FP8>     register-staged, 128-row tiles (head_dim 64)
-//   prefill_w48_kernel<BS, FP8>    persistent 384-row LDS-DMA prefill (head_dim 128; bf16
-//                                  and E4M3 KV)
+//   prefill_w48_kernel<BS, FMT>    persistent 384-row LDS-DMA prefill (head_dim 128)
 //   decode_kernel<D, BS, FP8>      register-staged decode (head_dim 64)
-//   decode_dma_kernel<BS, NW, NST>, decode_dma_fp8_kernel<BS, NW, NST>
-//                                  LDS-DMA decode, bf16 and E4M3 (head_dim 128)
+//   decode_dma_kernel<BS, NW, NST> LDS-DMA decode, bf16 (head_dim 128)
+//   decode_cascade_kernel<BS, NRB, NW, NST>
+//                                  shared-prefix cascade items, then decode items
+//   decode_dma_fp8_kernel<BS, NW, NST>, decode_dma_fp4_kernel<BS, NW, NST>
+//                                  LDS-DMA decode, E4M3 and MXFP4 (head_dim 128)
+//   decode_claim_kernel<BS, NRB, FMT>
+//                                  the decode launch's items claimed by persistent
+//                                  work-groups (co-scheduled mixed steps)
 //   merge_kernel, merge_many_kernel  LSE merge of split items
+//   step_kernel<BS, FMT>           the whole step in one persistent launch
+// (the decode kernels' bodies are item functions -- decode_dma_item,
+// cascade_item, decode_fp8_item, decode_fp4_item -- that the claiming and
+// step kernels call too)
 #include "pa_append.h"
 #include "pa_device.h"
 #include "pa_internal.h"

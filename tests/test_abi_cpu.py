@@ -458,3 +458,25 @@ def test_mxfp4_cache_checks(palib):
     bf = pa.pa_workspace_size(hist, incr, 32, cache(pa))
     f4 = pa.pa_workspace_size(hist, incr, 32, cache(pa, dtype=mx, k_scale=FAKE, v_scale=FAKE))
     assert bf == f4 > 0
+
+
+def test_step_sizes_every_format_at_head_dim_128(palib):
+    """paged_attn_step's size query: bf16, E4M3 and MXFP4 caches at head_dim
+    128 are sized (the same tiles and partials); head_dim 64 is rejected."""
+    pa = palib
+    hist, incr = np.array([5000, 100], np.int32), np.array([700, 1], np.int32)
+
+    def size(c):
+        n = C.c_size_t(0)
+        st = pa.lib.paged_attn_step(C.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 512,
+                                    hist.ctypes.data_as(C.c_void_p), incr.ctypes.data_as(C.c_void_p), 2, 32,
+                                    0.088, FAKE, None, None, C.byref(n), None)
+        return st, n.value
+
+    st, bf = size(cache(pa))
+    assert st == pa.PA_OK and bf > 0
+    for dt in (pa.PA_KV_FP8_E4M3, pa.PA_KV_MXFP4):
+        st, n = size(cache(pa, dtype=dt, k_scale=FAKE, v_scale=FAKE))
+        assert st == pa.PA_OK and n == bf, (dt, st, n, pa.pa_last_error())
+    st, _ = size(cache(pa, head_dim=64))
+    assert st == pa.PA_ERR_UNSUPPORTED
