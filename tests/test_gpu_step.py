@@ -60,6 +60,10 @@ CASES = {
     "e4m3_bs16_split": _spec([60_000, 4100, 333], [1, 1, 150], kv_dtype="e4m3"),
     "mxfp4_mixed": _spec([5000, 900, 12_000, 0, 77, 3000], [600, 1, 1, 300, 1, 2], kv_dtype="mxfp4"),
     "mxfp4_bs64_split": _spec([60_000, 4100, 40], [400, 1, 1], bs=64, kv_dtype="mxfp4"),
+    "e4m3_g8": _spec([1500, 10, 640, 333], [2, 1, 2, 150], hkv=4, bs=64, kv_dtype="e4m3"),
+    "mxfp4_g1": _spec([1200, 50], [300, 1], hq=8, hkv=8, kv_dtype="mxfp4"),
+    "mxfp4_initial_and_empty": _spec([0, 700, 3000], [1000, 0, 1], bs=64, kv_dtype="mxfp4"),
+    "e4m3_initial": _spec([0, 2000], [700, 1], kv_dtype="e4m3"),
 }
 
 
