@@ -47,3 +47,5 @@ def test_noalloc_matches_workspace_entry_point(palib):
     _one(palib, small)
     e4 = W.Spec("noalloc_e4m3", 73, 32, 8, 128, 64, [9_000, 4_000], [200, 1], kv_dtype="e4m3")
     _one(palib, e4)
+    f4 = W.Spec("noalloc_mxfp4", 74, 32, 8, 128, 16, [9_000, 4_000, 20_000], [200, 1, 1], kv_dtype="mxfp4")
+    _one(palib, f4)
