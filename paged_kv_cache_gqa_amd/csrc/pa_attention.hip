@@ -2630,12 +2630,10 @@ __device__ __forceinline__ int step_claim(const StepArgs &s, int &phase, uint32_
   return -1;
 }
 
-// One loop over the claimed tasks of every kind.  (The E4M3 and MXFP4 decode
-// items run 10-15% slower here than in the decode launch: a 1M-token E4M3
-// decode step takes 0.388 ms against 0.355 for the append, decode and merge
-// launches; the cause is not established.  A structure with one loop per
-// task kind, tried against it, hung on its first test, cause not found, and
-// is not used.)
+// One loop over the claimed tasks of every kind.  (A single 1M-token decode
+// runs 9-11% slower through this kernel than through the append, decode and
+// merge launches; the cause is not established.  A structure with one loop
+// per task kind hung on its first test, cause not found, and is not used.)
 template <int BS, int FMT>
 __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
   // One LDS area for whichever item runs: the decode ring of the KV format
@@ -2657,6 +2655,18 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
   xcc %= (uint32_t)s.xcds;
   int phase = 0;
   bool waited = false, dec_empty = false, dec_first = false;
+  // Each task reads its arguments through a fresh view of the kernel
+  // argument segment (the pointer passed through an empty asm, so the
+  // compiler cannot keep the fields loaded across tasks): with one view for
+  // the whole kernel it held many fields in scalar registers throughout and
+  // spilled them into vector lanes (300-640 lane reads in the step kernels,
+  // some in the decode items' key-step loops).
+  typedef const __attribute__((address_space(4))) StepArgs KStepArgs;
+  auto fresh = [&]() __attribute__((always_inline)) {
+    KStepArgs *p = (KStepArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return (const StepArgs *)p;
+  };
   // after a task's partial stores: count the part in; the last one merges
   auto part_done = [&](int merge) __attribute__((always_inline)) {
     PA_WAIT_VMCNT(0);
@@ -2669,7 +2679,10 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
       merge_s = last ? merge : -1;
     }
     __syncthreads();
-    if (merge_s >= 0) step_merge(s.mg, s.mg.merges[merge_s]);
+    if (merge_s >= 0) {
+      const StepArgs *sp = fresh();
+      step_merge(sp->mg, sp->mg.merges[merge_s]);
+    }
   };
   for (;;) {
     if (tid == 0) task_s = step_claim(s, phase, xcc, waited, dec_empty, dec_first);
@@ -2682,9 +2695,10 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
       // (chunk bounds are multiples of 4: an MXFP4 32-element group's four
       // lanes are active together)
       const uint32_t c0 = (uint32_t)idx * kStepAppendChunks;
+      const StepArgs *sp = fresh();
 #pragma unroll 1
-      for (uint32_t gid = c0 + tid; gid < min(c0 + kStepAppendChunks, s.app.nchunks); gid += kStepThreads)
-        append_chunk<FMT>(s.app, gid);
+      for (uint32_t gid = c0 + tid; gid < min(c0 + kStepAppendChunks, sp->app.nchunks); gid += kStepThreads)
+        append_chunk<FMT>(sp->app, gid);
       PA_WAIT_VMCNT(0);
       __syncthreads();
       if (tid == 0) {
@@ -2693,21 +2707,23 @@ __global__ __launch_bounds__(kStepThreads, 1) void step_kernel(StepArgs s) {
       }
     } else if (kind == kTaskPrefill) {
       for (int i = s.wg_first[idx]; i < s.wg_first[idx + 1]; i++) {
-        const Item it = s.pre.items[i];
-        w48_item<BS, FMT>(s.pre, it, (lds_u8 *)smem_raw);
+        const StepArgs *sp = fresh();
+        const Item it = sp->pre.items[i];
+        w48_item<BS, FMT>(sp->pre, it, (lds_u8 *)smem_raw);
         if (it.part >= 0)
           part_done(s.pre_part_merge[it.part]);
         else
           __syncthreads();  // LDS of this item no longer read or written
       }
     } else {
-      const Item it = s.dec.items[idx];
+      const StepArgs *sp = fresh();
+      const Item it = sp->dec.items[idx];
       if constexpr (FMT == kKvE4m3)
-        decode_fp8_item<BS, NW, DEC_NST>(s.dec, it, smem_raw, bt_lds);
+        decode_fp8_item<BS, NW, DEC_NST>(sp->dec, it, smem_raw, bt_lds);
       else if constexpr (FMT == kKvMxfp4)
-        decode_fp4_item<BS, NW, DEC_NST>(s.dec, it, smem_raw, bt_lds, vsf_lds);
+        decode_fp4_item<BS, NW, DEC_NST>(sp->dec, it, smem_raw, bt_lds, vsf_lds);
       else
-        decode_dma_item<BS, NW, DEC_NST>(s.dec, it, smem_raw, bt_lds);
+        decode_dma_item<BS, NW, DEC_NST>(sp->dec, it, smem_raw, bt_lds);
       if (it.part >= 0) part_done(s.dec_part_merge[it.part]);
     }
   }
